@@ -1,0 +1,284 @@
+"""Pins of the oracle's walk, visit counts and accuracy reference.
+
+The walk is the per-target stackless walk of ADR-0029 (Decision) and of the
+"sycl_tree_solver.hpp" page ("What is not given up": each target sums exactly
+the nodes its own walk visits, in the same order). The accuracy reference is
+the compensated double-precision direct sum of the performance page
+("Accuracy").
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from barnes_hut_gravitational_amd import inputs
+
+from test_oracle_tree import brute_tree
+
+F = np.float32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = 0.05
+
+
+def fp32_direct_sorted(xs, eps):
+    """Direct sum over sorted sources j = 0..n-1 in order, float32, all targets at once."""
+    n = len(xs)
+    x = xs[:, :3].astype(F)
+    a = np.zeros((n, 3), F)
+    eps2 = F(eps) * F(eps)
+    for j in range(n):
+        d = x[j][None, :] - x
+        r2 = ((d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]) + eps2
+        inv = F(1.0) / np.sqrt(r2)
+        f = xs[j, 3] * ((inv * inv) * inv)
+        a += f[:, None] * d
+    return a
+
+
+def test_theta_zero_is_direct_sum():
+    pos, mass = inputs.make("plummer", 300)
+    t = oracle.build_tree(pos, mass, 8)
+    acc, pp, pc, vis = oracle.walk(t, EPS, 0.0)
+    assert np.all(pc == 0) and np.all(pp == t.n - 1) and np.all(vis == t.n_nodes)
+    assert np.array_equal(acc, fp32_direct_sorted(t.xs, EPS))
+
+
+def test_theta_zero_close_to_fp64_direct():
+    pos, mass = inputs.make("plummer", 512)
+    r = oracle.evaluate(pos, mass, EPS, 0.0, 8)
+    ref = oracle.direct_fp64(pos, mass, EPS)
+    err = np.linalg.norm(r.acc - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err.max() < 1e-5
+    assert np.sqrt(np.mean(err**2)) < 1e-6
+
+
+def test_huge_theta_accepts_root():
+    pos, mass = inputs.make("uniform", 2000)
+    t = oracle.build_tree(pos, mass, 32)
+    acc, pp, pc, vis = oracle.walk(t, EPS, 1e6)
+    d2 = ((t.xs[:, :3].astype(np.float64) - t.geom[0, :3]) ** 2).sum(1)
+    far = d2 > 1e-6
+    assert np.all(vis[far] == 1) and np.all(pc[far] == 1) and np.all(pp[far] == 0)
+
+
+def test_two_body_closed_form():
+    pos = np.array([[0.0, 0.0, 0.0], [0.3, -0.4, 1.2]], np.float32)
+    mass = np.array([0.25, 0.75], np.float32)
+    r = oracle.evaluate(pos, mass, EPS, 0.5, 32)
+    d = pos[1].astype(np.float64) - pos[0]
+    f = 1.0 / (d @ d + EPS * EPS) ** 1.5
+    exact0, exact1 = 0.75 * f * d, -0.25 * f * d
+    assert np.allclose(r.acc[0], exact0, rtol=1e-6, atol=0)
+    assert np.allclose(r.acc[1], exact1, rtol=1e-6, atol=0)
+    assert list(r.n_pp) == [1, 1] and list(r.n_pc) == [0, 0]
+
+
+@pytest.mark.parametrize("kind,n", [("plummer", 16384), ("merger", 8192), ("uniform", 8192)])
+def test_partition_invariant(kind, n):
+    """Accepted nodes and opened leaves of one walk cover every particle once;
+    visits = accepted + opened leaves + opened internal nodes; at theta 0.5 no
+    accepted node contains its target, so the target's own leaf is opened."""
+    pos, mass = inputs.make(kind, n)
+    t = oracle.build_tree(pos, mass, 32)
+    acc, pp, pc, vis = oracle.walk(t, EPS, 0.5)
+    for i in np.random.default_rng(1).choice(n, 40, replace=False):
+        nodes, action = oracle.walk_trace(t, EPS, 0.5, i)
+        used = nodes[action < 2]
+        assert int(t.count[used].sum()) == n
+        assert len(nodes) == vis[i]
+        assert np.sum(action == 0) == pc[i]
+        assert int(t.count[nodes[action == 1]].sum()) - 1 == pp[i]
+        acc_nodes = nodes[action == 0]
+        inside = (t.begin[acc_nodes] <= i) & (i < t.begin[acc_nodes] + t.count[acc_nodes])
+        assert not inside.any()
+        assert np.all(np.diff(nodes) > 0)
+
+
+# ------------------------------------------- recursive textbook walk (B.4) --
+
+def recursive_reference(pos, mass, cap, eps, theta):
+    """Tree from the prefix definition, moments and a recursive walk, all in
+    float32 scalar arithmetic; children are found by range containment."""
+    lo, side, scale = oracle.root_cube(pos, mass)
+    keys = oracle.morton_keys(pos, lo, scale)
+    perm = np.argsort(keys, kind="stable")
+    ks = keys[perm]
+    x = pos[perm].astype(F)
+    m = mass[perm].astype(F)
+    level, begin, count, _ = brute_tree(ks, cap)
+    nn = len(level)
+    children = [[] for _ in range(nn)]
+    for k in range(1, nn):
+        par = [p for p in range(nn) if level[p] == level[k] - 1 and begin[p] <= begin[k] < begin[p] + count[p]]
+        assert len(par) == 1
+        children[par[0]].append(k)
+    M = [F(0)] * nn
+    S = [None] * nn
+    com = [None] * nn
+
+    def moments(k):
+        Mk, sx, sy, sz = F(0), F(0), F(0), F(0)
+        if not children[k]:
+            for j in range(begin[k], begin[k] + count[k]):
+                Mk = F(Mk + m[j])
+                sx, sy, sz = F(sx + m[j] * x[j, 0]), F(sy + m[j] * x[j, 1]), F(sz + m[j] * x[j, 2])
+        else:
+            for c in children[k]:
+                moments(c)
+                Mk = F(Mk + M[c])
+                sx, sy, sz = F(sx + S[c][0]), F(sy + S[c][1]), F(sz + S[c][2])
+        M[k], S[k] = Mk, (sx, sy, sz)
+        com[k] = (F(sx / Mk), F(sy / Mk), F(sz / Mk))
+
+    moments(0)
+    eps2, th2 = F(eps) * F(eps), F(theta) * F(theta)
+    s2 = [F(np.ldexp(side, -int(level[k]))) * F(np.ldexp(side, -int(level[k]))) for k in range(nn)]
+
+    def term(mj, dx, dy, dz, a):
+        r2 = F(F(F(dx * dx) + F(dy * dy)) + F(dz * dz)) + eps2
+        inv = F(1) / np.sqrt(F(r2))
+        f = F(mj * F(F(inv * inv) * inv))
+        a[0], a[1], a[2] = F(a[0] + f * dx), F(a[1] + f * dy), F(a[2] + f * dz)
+
+    out = np.zeros((len(m), 3), F)
+    cnt = np.zeros((len(m), 3), np.int64)
+    for i in range(len(m)):
+        a = [F(0), F(0), F(0)]
+        c = [0, 0, 0]  # pp, pc, visits
+
+        def visit(k):
+            c[2] += 1
+            dx, dy, dz = F(com[k][0] - x[i, 0]), F(com[k][1] - x[i, 1]), F(com[k][2] - x[i, 2])
+            d2 = F(F(dx * dx) + F(dy * dy)) + F(dz * dz)
+            if s2[k] < F(th2 * d2):
+                term(M[k], dx, dy, dz, a)
+                c[1] += 1
+            elif not children[k]:
+                for j in range(begin[k], begin[k] + count[k]):
+                    term(m[j], F(x[j, 0] - x[i, 0]), F(x[j, 1] - x[i, 1]), F(x[j, 2] - x[i, 2]), a)
+                c[0] += count[k] - (1 if begin[k] <= i < begin[k] + count[k] else 0)
+            else:
+                for ch in children[k]:
+                    visit(ch)
+
+        visit(0)
+        out[i] = a
+        cnt[i] = c
+    res = np.empty_like(out)
+    res[perm] = out
+    cres = np.empty_like(cnt)
+    cres[perm] = cnt
+    return res, cres
+
+
+@pytest.mark.parametrize("kind,n,cap,theta", [("plummer", 160, 4, 0.5), ("merger", 128, 3, 0.7),
+                                              ("uniform", 150, 6, 0.3)])
+def test_recursive_walk_bitwise(kind, n, cap, theta):
+    pos, mass = inputs.make(kind, n)
+    mass = mass * np.linspace(0.5, 1.5, n).astype(F)
+    r = oracle.evaluate(pos, mass, EPS, theta, cap)
+    ref, cnt = recursive_reference(pos, mass, cap, EPS, theta)
+    assert np.array_equal(r.acc, ref)
+    assert np.array_equal(r.n_pp, cnt[:, 0]) and np.array_equal(r.n_pc, cnt[:, 1])
+    assert np.array_equal(r.visits_own, cnt[:, 2])
+
+
+# ------------------------------------------------------- fp64 direct sum --
+
+def test_direct_fp64_momentum_balance():
+    pos, mass = inputs.make("plummer", 2048)
+    mass = mass * np.linspace(0.2, 1.8, 2048).astype(F)
+    a = oracle.direct_fp64(pos, mass, EPS)
+    p = (mass.astype(np.float64)[:, None] * a)
+    assert np.all(np.abs(p.sum(0)) <= 1e-12 * np.abs(p).sum(0))
+
+
+def test_direct_fp64_matches_exact_sum():
+    """Compensated summation: within a few ulp of the exactly rounded sum of the
+    same float64 terms (math.fsum), also for the most central particle, whose
+    terms cancel heavily."""
+    n = 3000
+    pos, mass = inputs.make("plummer", n)
+    p64 = pos.astype(np.float64)
+    central = int(np.argmin(np.linalg.norm(p64, axis=1)))
+    targets = (0, 7, central)
+    a = oracle.direct_fp64(pos, mass, EPS, np.array(targets))
+    for row, i in enumerate(targets):
+        d = p64 - p64[i]
+        r2 = (d * d).sum(1) + EPS * EPS
+        f = mass.astype(np.float64) / (r2 * np.sqrt(r2))
+        for ax in range(3):
+            terms = [f[j] * d[j, ax] for j in range(n) if j != i]
+            exact = math.fsum(terms)
+            assert abs(a[row, ax] - exact) <= 4 * 2.0**-53 * abs(exact) + 1e-30, (i, ax)
+
+
+def test_opening_equality_golden():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "opening_equality.txt")) if l[0] != "#"]
+    pos = np.array([[0, 0, 0], [8, 8, 8], [4, 0, 0], [4, 0, 0], [7, 3, 3]], np.float32)
+    r = oracle.evaluate(pos, np.ones(5, np.float32), EPS, 0.5, 2)
+    assert rows[0][0] == "A"
+    assert [r.n_pp[0], r.n_pc[0], r.visits_own[0]] == [int(v) for v in rows[0][1:]]
+    e2 = EPS * EPS
+    exact = (2 * 4 / (16 + e2) ** 1.5 * np.array([1.0, 0, 0]) + np.array([7.0, 3, 3]) / (67 + e2) ** 1.5
+             + np.array([8.0, 8, 8]) / (192 + e2) ** 1.5)
+    assert np.allclose(r.acc[0], exact, rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("n,worst,rms", [(4096, 2.03e-2, 2.03e-3), (16384, 1.34e-2, 1.76e-3)])
+def test_bh_error_same_order_as_pages(n, worst, rms):
+    """Soft pin: the performance page ("Accuracy") reports the opening angle's
+    error at theta 0.5 against the compensated direct sum. The particle sets
+    differ (same seed, different generator), so the root-mean-square error is
+    held to a factor 3 and the worst error, a single particle near the centre
+    where |a| is small, to an order of magnitude."""
+    pos, mass = inputs.make("plummer", n)
+    r = oracle.evaluate(pos, mass, EPS, 0.5, 32)
+    ref = oracle.direct_fp64(pos, mass, EPS)
+    err = np.linalg.norm(r.acc - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert rms / 3 < np.sqrt(np.mean(err**2)) < rms * 3
+    assert worst / 10 < err.max() < worst * 10
+    assert worst / 3 < np.percentile(err, 99.9) < worst * 3
+
+
+# ---------------------------------------------------- group union visits --
+
+def test_union_brute_force_small():
+    pos, mass = inputs.make("plummer", 300)
+    t = oracle.build_tree(pos, mass, 4)
+    for width in (1, 8, 64):
+        u = oracle.union_visits(t, EPS, 0.5, width)
+        for g in range(len(u)):
+            nodes = set()
+            for i in range(g * width, min((g + 1) * width, t.n)):
+                nodes |= set(oracle.walk_trace(t, EPS, 0.5, i)[0].tolist())
+            assert u[g] == len(nodes)
+    _, _, _, vis = oracle.walk(t, EPS, 0.5)
+    assert np.array_equal(oracle.union_visits(t, EPS, 0.5, 1), vis)
+
+
+@pytest.mark.parametrize("kind,n", [("plummer", 16384), ("merger", 16384), ("uniform", 16384)])
+def test_min_rule_and_ballot_rule_step_through_union(kind, n):
+    pos, mass = inputs.make(kind, n)
+    t = oracle.build_tree(pos, mass, 32)
+    _, _, _, vis = oracle.walk(t, EPS, 0.5)
+    u = oracle.union_visits(t, EPS, 0.5, 64)
+    for rule in ("min", "ballot"):
+        steps, own, ok = oracle.group_walk(t, EPS, 0.5, 64, rule)
+        assert ok
+        assert np.array_equal(steps, u)
+        assert np.array_equal(own, vis)
+
+
+def test_redundancy_same_order_as_pages():
+    """Soft pin: at width 32 the performance page reports 1.19-1.25 times more
+    nodes stepped than walked; wider groups step through more."""
+    pos, mass = inputs.make("plummer", 16384)
+    t = oracle.build_tree(pos, mass, 32)
+    _, _, _, vis = oracle.walk(t, EPS, 0.5)
+    r32 = np.repeat(oracle.union_visits(t, EPS, 0.5, 32), 32).mean() / vis.mean()
+    r64 = np.repeat(oracle.union_visits(t, EPS, 0.5, 64), 64).mean() / vis.mean()
+    assert 1.1 < r32 < 1.45 and r32 < r64 < 1.8
