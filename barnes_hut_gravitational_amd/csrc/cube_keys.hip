@@ -1,0 +1,143 @@
+// Root cube and Morton keys.
+//
+// The orrery performance page ("Where one evaluation goes") puts a Morton
+// sort in front of the tree build; the root cube and key layout are the
+// readings stated in include/orr.h: corner = component-wise minimum, side =
+// largest extent, 21 bits per axis interleaved x-major.
+//
+// Both kernels are HBM-bound streaming passes (12 B of position + 4 B of mass
+// read per particle; 12 B of key + index written).
+#include "orr_internal.h"
+
+namespace orr {
+
+namespace {
+
+__device__ __forceinline__ float wave_min(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Per-block minimum and maximum of each axis plus an invalid-input flag.
+// part[b] = (min x, min y, min z, max x, max y, max z, flag bits, unused).
+__global__ __launch_bounds__(256) void k_cube_partial(const float *__restrict__ pos,
+                                                      const float *__restrict__ mass, uint32_t n,
+                                                      float *__restrict__ part) {
+    float mn0 = INFINITY, mn1 = INFINITY, mn2 = INFINITY;
+    float mx0 = -INFINITY, mx1 = -INFINITY, mx2 = -INFINITY;
+    uint32_t bad = 0;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) {
+        float x = pos[3ull * i], y = pos[3ull * i + 1], z = pos[3ull * i + 2], m = mass[i];
+        bad |= !(isfinite(x) && isfinite(y) && isfinite(z) && isfinite(m) && m >= 0.0f);
+        mn0 = fminf(mn0, x);
+        mn1 = fminf(mn1, y);
+        mn2 = fminf(mn2, z);
+        mx0 = fmaxf(mx0, x);
+        mx1 = fmaxf(mx1, y);
+        mx2 = fmaxf(mx2, z);
+    }
+    __shared__ float red[4][7];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float v[7] = {wave_min(mn0), wave_min(mn1), wave_min(mn2), wave_max(mx0), wave_max(mx1), wave_max(mx2),
+                  __uint_as_float(__ballot(bad) != 0ull ? 1u : 0u)};
+    if (lane == 0)
+        for (int k = 0; k < 7; k++) red[w][k] = v[k];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r[7];
+        for (int k = 0; k < 7; k++) r[k] = red[0][k];
+        for (int ww = 1; ww < 4; ww++) {
+            for (int k = 0; k < 3; k++) r[k] = fminf(r[k], red[ww][k]);
+            for (int k = 3; k < 6; k++) r[k] = fmaxf(r[k], red[ww][k]);
+            r[6] = __uint_as_float(__float_as_uint(r[6]) | __float_as_uint(red[ww][6]));
+        }
+        for (int k = 0; k < 7; k++) part[8 * blockIdx.x + k] = r[k];
+        part[8 * blockIdx.x + 7] = 0.0f;
+    }
+}
+
+// One block: combine the partials, write lo, side, scale and the flag.
+__global__ __launch_bounds__(64) void k_cube_final(const float *__restrict__ part, int nparts,
+                                                   DevParams *__restrict__ prm) {
+    const int lane = threadIdx.x;
+    float r[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    uint32_t bad = 0;
+    for (int b = lane; b < nparts; b += 64) {
+        for (int k = 0; k < 3; k++) r[k] = fminf(r[k], part[8 * b + k]);
+        for (int k = 3; k < 6; k++) r[k] = fmaxf(r[k], part[8 * b + k]);
+        bad |= __float_as_uint(part[8 * b + 6]);
+    }
+    for (int k = 0; k < 3; k++) r[k] = wave_min(r[k]);
+    for (int k = 3; k < 6; k++) r[k] = wave_max(r[k]);
+    bad = __ballot(bad != 0) != 0ull;
+    if (lane == 0) {
+        float lo[3], side = 0.0f;
+        for (int a = 0; a < 3; a++) {
+            lo[a] = r[a] + 0.0f;  // -0 becomes +0: a unique corner
+            float ext = r[3 + a] - lo[a];
+            if (ext > side) side = ext;
+        }
+        if (!isfinite(side) || !isfinite(lo[0]) || !isfinite(lo[1]) || !isfinite(lo[2])) {
+            bad = 1;  // keep the rest of the build well-formed
+            side = 1.0f;
+            for (int a = 0; a < 3; a++)
+                if (!isfinite(lo[a])) lo[a] = 0.0f;
+        }
+        if (side == 0.0f) side = 1.0f;
+        for (int a = 0; a < 3; a++) prm->lo[a] = lo[a];
+        prm->side = side;
+        prm->scale = 2097152.0f / side;  // correctly rounded division
+        prm->bad_input = bad;
+        prm->n_nodes = 0;
+    }
+}
+
+// Spread the low 21 bits of v so that bit b lands on bit 3b (mask-and-shift
+// bit interleaving).
+__device__ __forceinline__ uint64_t spread3(uint32_t v) {
+    uint64_t x = v & 0x1fffffu;
+    x = (x | (x << 32)) & 0x001f00000000ffffull;
+    x = (x | (x << 16)) & 0x001f0000ff0000ffull;
+    x = (x | (x << 8)) & 0x100f00f00f00f00full;
+    x = (x | (x << 4)) & 0x10c30c30c30c30c3ull;
+    x = (x | (x << 2)) & 0x1249249249249249ull;
+    return x;
+}
+
+// q = min(trunc((x - lo) * scale), 2^21 - 1); anything not >= 0 (only
+// possible for flagged input) maps to 0.
+__device__ __forceinline__ uint32_t quantise(float x, float lo, float scale) {
+    float t = (x - lo) * scale;
+    if (t >= 2097151.0f) return kQMax;
+    return t >= 0.0f ? (uint32_t)t : 0u;
+}
+
+__global__ __launch_bounds__(256) void k_morton(const float *__restrict__ pos, uint32_t n,
+                                                const DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
+                                                uint32_t *__restrict__ idx) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= n) return;
+    const float lx = prm->lo[0], ly = prm->lo[1], lz = prm->lo[2], sc = prm->scale;
+    uint32_t qx = quantise(pos[3ull * i], lx, sc);
+    uint32_t qy = quantise(pos[3ull * i + 1], ly, sc);
+    uint32_t qz = quantise(pos[3ull * i + 2], lz, sc);
+    keys[i] = (spread3(qx) << 2) | (spread3(qy) << 1) | spread3(qz);
+    idx[i] = i;
+}
+
+}  // namespace
+
+hipError_t launch_cube_and_keys(const float *pos, const float *mass, const Workspace &ws, hipStream_t s) {
+    const uint32_t n = (uint32_t)ws.n;
+    int blocks = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));
+    k_cube_partial<<<blocks, 256, 0, s>>>(pos, mass, n, ws.cube_part);
+    k_cube_final<<<1, 64, 0, s>>>(ws.cube_part, blocks, ws.prm);
+    k_morton<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(pos, n, ws.prm, ws.keys[0], ws.vals[0]);
+    return hipGetLastError();
+}
+
+}  // namespace orr

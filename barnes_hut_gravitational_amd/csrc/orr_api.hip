@@ -1,0 +1,362 @@
+// C ABI of liborr (declared in include/orr.h): argument checks, workspace
+// layout, and the stream-ordered sequence of kernels of one evaluation.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "orr.h"
+#include "orr_internal.h"
+
+namespace orr {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+orr_status fail(orr_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+orr_status fail(orr_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+orr_status hip_fail(hipError_t e, const char *where) {
+    return fail(ORR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
+    const int64_t nb = max_nodes_for(n, leaf_cap);
+    const int64_t n_tiles = ceil_div(n, kTile);
+    const int64_t scan_len = std::max<int64_t>((int64_t)kRadixBins * n_tiles, n + 1);
+    const int64_t n_part = ceil_div(scan_len, kTile);
+    char *p = static_cast<char *>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *r = p ? p + off : nullptr;
+        off = align_up(off + bytes);
+        return r;
+    };
+    Workspace w{};
+    w.prm = reinterpret_cast<DevParams *>(take(sizeof(DevParams)));
+    w.cube_part = reinterpret_cast<float *>(take(sizeof(float) * 8 * kCubeBlocks));
+    for (int k = 0; k < 2; k++) w.keys[k] = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * n));
+    for (int k = 0; k < 2; k++) w.vals[k] = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
+    w.hist = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kRadixBins * n_tiles));
+    w.scan_part = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n_part));
+    w.xs = reinterpret_cast<float4 *>(take(sizeof(float4) * n));
+    w.info = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
+    w.base = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * (n + 1)));
+    w.geom = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
+    w.topo = reinterpret_cast<uint4 *>(take(sizeof(uint4) * nb));
+    w.msum = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
+    w.parent = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
+    w.arrive = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
+    w.level = reinterpret_cast<uint8_t *>(take(sizeof(uint8_t) * nb));
+    w.n = n;
+    w.leaf_cap = leaf_cap;
+    w.max_nodes = nb;
+    w.n_tiles = n_tiles;
+    if (ws) *ws = w;
+    return off;
+}
+
+}  // namespace orr
+
+using namespace orr;
+
+struct orr_tree {
+    Workspace ws;
+    hipStream_t stream;
+};
+
+namespace {
+
+bool valid_sizes(int64_t n, int32_t leaf_cap) {
+    return n >= 1 && n <= ORR_MAX_N && leaf_cap >= 1 && leaf_cap <= ORR_MAX_LEAF_CAP;
+}
+
+orr_status check_sizes(int64_t n, int32_t leaf_cap) {
+    if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
+    if (leaf_cap < 1 || leaf_cap > ORR_MAX_LEAF_CAP)
+        return fail(ORR_ERR_RANGE, "leaf_cap = %d is outside [1, %d]", leaf_cap, ORR_MAX_LEAF_CAP);
+    return ORR_OK;
+}
+
+orr_status check_walk_args(float eps, float theta, int traversal) {
+    if (!(std::isfinite(eps) && eps > 0.0f)) return fail(ORR_ERR_RANGE, "eps must be finite and > 0 (got %g)", eps);
+    if (!(std::isfinite(theta) && theta >= 0.0f))
+        return fail(ORR_ERR_RANGE, "theta must be finite and >= 0 (got %g)", theta);
+    if (traversal != ORR_TRAVERSAL_INDEPENDENT && traversal != ORR_TRAVERSAL_COHERENT)
+        return fail(ORR_ERR_INVALID_ARG, "traversal %d is not a orr_traversal", traversal);
+    return ORR_OK;
+}
+
+orr_status check_build_args(const float *pos, const float *mass, int64_t n, int32_t leaf_cap, void *workspace,
+                            size_t workspace_bytes) {
+    orr_status st = check_sizes(n, leaf_cap);
+    if (st != ORR_OK) return st;
+    if (!pos || !mass) return fail(ORR_ERR_INVALID_ARG, "pos and mass must not be NULL");
+    if (!workspace) return fail(ORR_ERR_INVALID_ARG, "workspace must not be NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(ORR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t need = carve_workspace(nullptr, n, leaf_cap, nullptr);
+    if (workspace_bytes < need)
+        return fail(ORR_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    return ORR_OK;
+}
+
+// Records an event on the stream if timing is on.
+struct PhaseTimer {
+    bool on = false;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[8] = {};
+    int k = 0;
+    hipError_t init(bool enable, hipStream_t stream) {
+        on = enable;
+        s = stream;
+        if (!on) return hipSuccess;
+        for (auto &e : ev) {
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    }
+    hipError_t mark() { return on ? hipEventRecord(ev[k++], s) : hipSuccess; }
+    float ms(int a, int b) {
+        float t = 0.0f;
+        (void)hipEventElapsedTime(&t, ev[a], ev[b]);
+        return t;
+    }
+    ~PhaseTimer() {
+        for (auto &e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+};
+
+orr_status build_into(const float *pos, const float *mass, const Workspace &ws, hipStream_t s, PhaseTimer &tm) {
+    hipError_t e;
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_cube_and_keys(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "root cube / keys");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_sort(ws, s)) != hipSuccess) return hip_fail(e, "radix sort");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_gather(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "gather");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_build(ws, s)) != hipSuccess) return hip_fail(e, "tree build");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_moments(ws, s)) != hipSuccess) return hip_fail(e, "moments");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return ORR_OK;
+}
+
+orr_status read_params(const orr_tree *t, DevParams *out) {
+    hipError_t e = hipMemcpyAsync(out, t->ws.prm, sizeof(DevParams), hipMemcpyDeviceToHost, t->stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    if ((e = hipStreamSynchronize(t->stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return ORR_OK;
+}
+
+}  // namespace
+
+#define ORR_GUARD_BEGIN try {
+#define ORR_GUARD_END                                                       \
+    }                                                                       \
+    catch (const std::bad_alloc &) {                                        \
+        return fail(ORR_ERR_INVALID_ARG, "host allocation failed");         \
+    }                                                                       \
+    catch (...) {                                                           \
+        return fail(ORR_ERR_INVALID_ARG, "unexpected C++ exception");      \
+    }
+
+extern "C" {
+
+int orr_abi_version(void) { return ORR_ABI_VERSION; }
+
+const char *orr_status_string(orr_status s) {
+    switch (s) {
+        case ORR_OK: return "ok";
+        case ORR_ERR_INVALID_ARG: return "invalid argument";
+        case ORR_ERR_RANGE: return "argument out of range";
+        case ORR_ERR_NONFINITE: return "non-finite or negative input";
+        case ORR_ERR_HIP: return "HIP runtime error";
+        case ORR_ERR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+const char *orr_traversal_name(orr_traversal t) {
+    switch (t) {
+        case ORR_TRAVERSAL_INDEPENDENT: return "independent";
+        case ORR_TRAVERSAL_COHERENT: return "coherent";
+    }
+    return "invalid";
+}
+
+const char *orr_last_error(void) { return g_last_error.c_str(); }
+
+size_t orr_workspace_bytes(int64_t n, int32_t leaf_cap) {
+    if (!valid_sizes(n, leaf_cap)) return 0;
+    return carve_workspace(nullptr, n, leaf_cap, nullptr);
+}
+
+orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_t leaf_cap, void *workspace,
+                          size_t workspace_bytes, void *hip_stream, orr_tree **out) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!out) return fail(ORR_ERR_INVALID_ARG, "out must not be NULL");
+    *out = nullptr;
+    orr_status st = check_build_args(pos, mass, n, leaf_cap, workspace, workspace_bytes);
+    if (st != ORR_OK) return st;
+    orr_tree *t = new orr_tree;
+    carve_workspace(workspace, n, leaf_cap, &t->ws);
+    t->stream = static_cast<hipStream_t>(hip_stream);
+    PhaseTimer tm;
+    st = build_into(pos, mass, t->ws, t->stream, tm);
+    if (st != ORR_OK) {
+        delete t;
+        return st;
+    }
+    *out = t;
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_traversal traversal, float *acc,
+                         uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    orr_status st = check_walk_args(eps, theta, (int)traversal);
+    if (st != ORR_OK) return st;
+    hipError_t e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT, eps * eps, theta * theta, acc,
+                               visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "walk");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float eps, float theta,
+                           int32_t leaf_cap, orr_traversal traversal, float *acc, uint32_t *visits_own,
+                           uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *workspace,
+                           size_t workspace_bytes, void *hip_stream, orr_timings *timings) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    orr_status st = check_build_args(pos, mass, n, leaf_cap, workspace, workspace_bytes);
+    if (st != ORR_OK) return st;
+    if ((st = check_walk_args(eps, theta, (int)traversal)) != ORR_OK) return st;
+    orr_tree t;
+    carve_workspace(workspace, n, leaf_cap, &t.ws);
+    t.stream = static_cast<hipStream_t>(hip_stream);
+    PhaseTimer tm;
+    hipError_t e = tm.init(timings != nullptr, t.stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((st = build_into(pos, mass, t.ws, t.stream, tm)) != ORR_OK) return st;
+    e = launch_walk(t.ws, traversal == ORR_TRAVERSAL_COHERENT, eps * eps, theta * theta, acc, visits_own,
+                    visits_stepped, n_pp, n_pc, t.stream);
+    if (e != hipSuccess) return hip_fail(e, "walk");
+    if (!timings) return ORR_OK;
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    DevParams prm;
+    if ((st = read_params(&t, &prm)) != ORR_OK) return st;
+    timings->cube_keys_ms = tm.ms(0, 1);
+    timings->sort_ms = tm.ms(1, 2);
+    timings->gather_ms = tm.ms(2, 3);
+    timings->build_ms = tm.ms(3, 4);
+    timings->moments_ms = tm.ms(4, 5);
+    timings->walk_ms = tm.ms(5, 6);
+    timings->total_ms = tm.ms(0, 6);
+    if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_info_get(const orr_tree *tree, orr_tree_info *out) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree || !out) return fail(ORR_ERR_INVALID_ARG, "tree and out must not be NULL");
+    hipError_t e = launch_tree_info(tree->ws, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "tree info");
+    DevParams prm;
+    orr_status st = read_params(tree, &prm);
+    if (st != ORR_OK) return st;
+    out->n = (uint32_t)tree->ws.n;
+    out->n_nodes = prm.n_nodes;
+    out->n_leaves = prm.n_leaves;
+    out->depth = prm.depth;
+    out->max_leaf_count = prm.max_leaf_count;
+    out->leaf_cap = tree->ws.leaf_cap;
+    for (int a = 0; a < 3; a++) out->lo[a] = prm.lo[a];
+    out->side = prm.side;
+    out->input_status = prm.bad_input ? ORR_ERR_NONFINITE : ORR_OK;
+    if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_check(const orr_tree *tree) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    DevParams prm;
+    orr_status st = read_params(tree, &prm);
+    if (st != ORR_OK) return st;
+    if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t *perm, uint8_t *level,
+                           uint32_t *begin, uint32_t *count, uint32_t *escape, float *geom, float *s2) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    const Workspace &ws = tree->ws;
+    hipStream_t s = tree->stream;
+    hipError_t e;
+    const size_t n = (size_t)ws.n;
+    if (keys_sorted &&
+        (e = hipMemcpyAsync(keys_sorted, ws.keys[0], n * 8, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "export keys");
+    if (perm && (e = hipMemcpyAsync(perm, ws.vals[0], n * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "export perm");
+    if (level || begin || count || escape || geom || s2) {
+        DevParams prm;
+        orr_status st = read_params(tree, &prm);
+        if (st != ORR_OK) return st;
+        const size_t nn = prm.n_nodes;
+        if (level && (e = hipMemcpyAsync(level, ws.level, nn, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+            return hip_fail(e, "export level");
+        if (geom && (e = hipMemcpyAsync(geom, ws.geom, nn * 16, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+            return hip_fail(e, "export geom");
+        // topo is (escape, begin, count, s2 bits) per node: strided copies
+        struct Field {
+            void *dst;
+            size_t off;
+        } fields[4] = {{escape, 0}, {begin, 4}, {count, 8}, {s2, 12}};
+        for (const Field &f : fields) {
+            if (!f.dst) continue;
+            e = hipMemcpy2DAsync(f.dst, 4, reinterpret_cast<const char *>(ws.topo) + f.off, 16, 4, nn,
+                                 hipMemcpyDeviceToDevice, s);
+            if (e != hipSuccess) return hip_fail(e, "export topology");
+        }
+    }
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+void orr_tree_free(orr_tree *tree) { delete tree; }
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Internal declarations of liborr: workspace layout, device-side parameter
+// block, kernel launch wrappers. Not part of the public ABI (include/orr.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+
+namespace orr {
+
+constexpr int kMaxLevel = 21;            // 21 bits per axis, 63-bit keys
+constexpr uint32_t kQMax = 2097151u;     // 2^21 - 1
+constexpr uint32_t kNoParent = 0xffffffffu;
+
+// Sort and scan tiles: 256 threads x 16 items.
+constexpr int kTileThreads = 256;
+constexpr int kTileItems = 16;
+constexpr int kTile = kTileThreads * kTileItems;
+constexpr int kRadixBits = 8;
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kRadixPasses = 8;          // 64 / 8; bit 63 is always zero
+
+constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube reduction
+
+// Device-resident scalars of one build, at the start of the workspace.
+struct DevParams {
+    float lo[3];
+    float side;
+    float scale;          // 2^21 / side
+    uint32_t bad_input;   // non-zero: non-finite position/mass, negative mass or overflowing extent
+    uint32_t n_nodes;
+    uint32_t n_leaves;    // filled by the info kernels only
+    uint32_t depth;
+    uint32_t max_leaf_count;
+    uint32_t pad[6];
+};
+static_assert(sizeof(DevParams) == 64, "DevParams layout");
+
+// Device pointers carved from the caller's workspace.
+struct Workspace {
+    DevParams *prm;
+    float *cube_part;      // [kCubeBlocks][8]
+    uint64_t *keys[2];     // [n] radix ping-pong; sorted keys end in keys[0]
+    uint32_t *vals[2];     // [n] payload: original index; perm ends in vals[0]
+    uint32_t *hist;        // [kRadixBins][n_tiles] digit-major tile counts
+    uint32_t *scan_part;   // tile partials of the device-wide scans
+    float4 *xs;            // [n] sorted (x, y, z, m)
+    uint32_t *info;        // [n] first level started | leaf depth << 8
+    uint32_t *base;        // [n + 1] nodes started per particle, scanned in place
+    float4 *geom;          // [max_nodes] (com, M)
+    uint4 *topo;           // [max_nodes] (escape, begin, count, bits of s^2)
+    float4 *msum;          // [max_nodes] (S, M), unnormalised sums for the parent
+    uint32_t *parent;      // [max_nodes]
+    uint32_t *arrive;      // [max_nodes] children finished, for the bottom-up pass
+    uint8_t *level;        // [max_nodes]
+    int64_t n;
+    int32_t leaf_cap;
+    int64_t max_nodes;
+    int64_t n_tiles;
+};
+
+inline int64_t max_nodes_for(int64_t n, int32_t leaf_cap) {
+    return n + 21 * (n / (leaf_cap + 1)) + 1;
+}
+
+// Lays the workspace out from `base` (which may be null for sizing) and
+// returns the bytes it needs.
+size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws);
+
+// ---- launch wrappers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_cube_and_keys(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
+hipError_t launch_sort(const Workspace &ws, hipStream_t s);
+hipError_t launch_gather(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
+hipError_t launch_build(const Workspace &ws, hipStream_t s);
+hipError_t launch_moments(const Workspace &ws, hipStream_t s);
+hipError_t launch_tree_info(const Workspace &ws, hipStream_t s);
+hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
+                       uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
+                       hipStream_t s);
+
+// Device-wide exclusive scan of len uint32 values, in place allowed
+// (in == out). If total is not null it receives the sum.
+hipError_t launch_exclusive_scan(const uint32_t *in, uint32_t *out, int64_t len, uint32_t *part,
+                                 uint32_t *total, hipStream_t s);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace orr

@@ -1,0 +1,204 @@
+"""ctypes binding of liborr.so (include/orr.h), with the same entry-point names.
+
+Marshalling only: every step of the evaluation runs in the HIP library.
+PyTorch supplies device memory (tensors) and the current HIP stream. There is
+no fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loaded before liborr so both share one HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liborr.so")
+
+ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_ERR_WORKSPACE = range(6)
+TRAVERSALS = {"independent": 0, "coherent": 1}
+EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
+            "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_eval_forces",
+            "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_tree_free")
+
+_lib = None
+_vp = ctypes.c_void_p
+
+
+class OrrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class Timings(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_float) for f in
+                ("cube_keys_ms", "sort_ms", "gather_ms", "build_ms", "moments_ms", "walk_ms", "total_ms")]
+
+    def as_dict(self):
+        return {f: float(getattr(self, f)) for f, _ in self._fields_}
+
+
+class TreeInfo(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_uint32), ("n_nodes", ctypes.c_uint32), ("n_leaves", ctypes.c_uint32),
+                ("depth", ctypes.c_uint32), ("max_leaf_count", ctypes.c_uint32), ("leaf_cap", ctypes.c_int32),
+                ("lo", ctypes.c_float * 3), ("side", ctypes.c_float), ("input_status", ctypes.c_int32)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load liborr.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OrrError(ORR_ERR_HIP, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, f32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        L.orr_abi_version.restype = ctypes.c_int
+        L.orr_status_string.argtypes = [ctypes.c_int]
+        L.orr_status_string.restype = ctypes.c_char_p
+        L.orr_traversal_name.argtypes = [ctypes.c_int]
+        L.orr_traversal_name.restype = ctypes.c_char_p
+        L.orr_last_error.restype = ctypes.c_char_p
+        L.orr_workspace_bytes.argtypes = [i64, i32]
+        L.orr_workspace_bytes.restype = sz
+        L.orr_build_tree.argtypes = [_vp, _vp, i64, i32, _vp, sz, _vp, ctypes.POINTER(_vp)]
+        L.orr_tree_walk.argtypes = [_vp, f32, f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
+        L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
+                                      _vp, ctypes.POINTER(Timings)]
+        L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
+        L.orr_tree_check.argtypes = [_vp]
+        L.orr_tree_export.argtypes = [_vp] * 9
+        L.orr_tree_free.argtypes = [_vp]
+        L.orr_tree_free.restype = None
+        for name in ("orr_build_tree", "orr_tree_walk", "orr_eval_forces", "orr_tree_info_get", "orr_tree_check",
+                     "orr_tree_export"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != ORR_OK:
+        raise OrrError(status, lib().orr_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().orr_abi_version()
+
+
+def workspace_bytes(n: int, leaf_cap: int = 32) -> int:
+    return int(lib().orr_workspace_bytes(n, leaf_cap))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _as_inputs(pos, mass):
+    if not (pos.is_cuda and mass.is_cuda):
+        raise OrrError(ORR_ERR_INVALID_ARG, "pos and mass must be GPU tensors")
+    if pos.dtype != torch.float32 or mass.dtype != torch.float32:
+        raise OrrError(ORR_ERR_INVALID_ARG, "pos and mass must be float32")
+    if pos.dim() != 2 or pos.shape[1] != 3 or mass.shape != (pos.shape[0],):
+        raise OrrError(ORR_ERR_INVALID_ARG, "pos must be [n, 3] and mass [n]")
+    return pos.contiguous(), mass.contiguous()
+
+
+def new_workspace(n: int, leaf_cap: int, device) -> torch.Tensor:
+    nbytes = workspace_bytes(n, leaf_cap)
+    if nbytes == 0:
+        raise OrrError(ORR_ERR_RANGE, f"no workspace for n={n}, leaf_cap={leaf_cap}")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Result:
+    acc: torch.Tensor             # [n, 3] float32, caller order
+    visits_own: torch.Tensor      # [n] int32 (uint32 bits)
+    visits_stepped: torch.Tensor
+    n_pp: torch.Tensor
+    n_pc: torch.Tensor
+    timings: dict | None
+
+
+def _outputs(n, device):
+    acc = torch.empty((n, 3), dtype=torch.float32, device=device)
+    cnt = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(4)]
+    return acc, cnt
+
+
+def orr_eval_forces(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="coherent", workspace=None,
+                    out=None, timings=False) -> Result:
+    """Build the tree and walk it (orr_eval_forces). Counters are returned as
+    int32 tensors holding the uint32 values."""
+    pos, mass = _as_inputs(pos, mass)
+    n = pos.shape[0]
+    if workspace is None:
+        workspace = new_workspace(n, leaf_cap, pos.device)
+    acc, cnt = out if out is not None else _outputs(n, pos.device)
+    tm = Timings() if timings else None
+    st = lib().orr_eval_forces(_ptr(pos), _ptr(mass), n, eps, theta, leaf_cap, TRAVERSALS[traversal],
+                               _ptr(acc), *[_ptr(c) for c in cnt], _ptr(workspace), workspace.numel(),
+                               _stream(pos.device), ctypes.byref(tm) if tm is not None else None)
+    _check(st)
+    return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
+
+
+class Tree:
+    """A built tree (orr_build_tree); the workspace tensor is kept alive with it."""
+
+    def __init__(self, pos, mass, leaf_cap=32, workspace=None):
+        pos, mass = _as_inputs(pos, mass)
+        self.n = pos.shape[0]
+        self.device = pos.device
+        self.workspace = workspace if workspace is not None else new_workspace(self.n, leaf_cap, pos.device)
+        self._inputs = (pos, mass)
+        h = _vp()
+        _check(lib().orr_build_tree(_ptr(pos), _ptr(mass), self.n, leaf_cap, _ptr(self.workspace),
+                                    self.workspace.numel(), _stream(pos.device), ctypes.byref(h)))
+        self._h = h
+
+    def walk(self, eps=0.05, theta=0.5, traversal="coherent", out=None) -> Result:
+        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        _check(lib().orr_tree_walk(self._h, eps, theta, TRAVERSALS[traversal], _ptr(acc),
+                                   *[_ptr(c) for c in cnt]))
+        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+
+    def info(self) -> dict:
+        ti = TreeInfo()
+        st = lib().orr_tree_info_get(self._h, ctypes.byref(ti))
+        if st not in (ORR_OK, ORR_ERR_NONFINITE):
+            _check(st)
+        return {"n": ti.n, "n_nodes": ti.n_nodes, "n_leaves": ti.n_leaves, "depth": ti.depth,
+                "max_leaf_count": ti.max_leaf_count, "leaf_cap": ti.leaf_cap, "lo": list(ti.lo),
+                "side": ti.side, "input_status": ti.input_status}
+
+    def check(self):
+        _check(lib().orr_tree_check(self._h))
+
+    def export(self) -> dict:
+        nn = self.info()["n_nodes"]
+        d = self.device
+        out = {"keys_sorted": torch.empty(self.n, dtype=torch.int64, device=d),
+               "perm": torch.empty(self.n, dtype=torch.int32, device=d),
+               "level": torch.empty(nn, dtype=torch.uint8, device=d),
+               "begin": torch.empty(nn, dtype=torch.int32, device=d),
+               "count": torch.empty(nn, dtype=torch.int32, device=d),
+               "escape": torch.empty(nn, dtype=torch.int32, device=d),
+               "geom": torch.empty((nn, 4), dtype=torch.float32, device=d),
+               "s2": torch.empty(nn, dtype=torch.float32, device=d)}
+        _check(lib().orr_tree_export(self._h, *[_ptr(out[k]) for k in
+                                                ("keys_sorted", "perm", "level", "begin", "count", "escape",
+                                                 "geom", "s2")]))
+        return out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.orr_tree_free(h)
+            self._h = None

@@ -1,0 +1,176 @@
+"""Benchmark of one Barnes-Hut force evaluation on one MI355X.
+
+A step is one whole evaluation through the C ABI (orr_eval_forces): root cube,
+Morton keys, radix sort, gather, tree build, moments, coherent walk and
+scatter, with the particles already resident in HBM. The workload is the
+Plummer sphere of 1,048,576 particles (softening 0.05, opening angle 0.5, leaf
+capacity 32, float32; seed 20260811, generator in
+barnes_hut_gravitational_amd/inputs.py).
+
+Prints one JSON line. value = particle-node interactions per second of the
+whole evaluation: sum over targets of (particle terms + accepted cells),
+divided by the mean step time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "ms per force eval + particle-node interactions/s, Plummer N=1M, theta 0.5"
+FLOPS_PER_INTERACTION = 20       # 3 sub, 6 for r^2 + eps^2, sqrt + div, 3 mul, 6 for a += f d
+PEAK_FP32_TFLOPS = 157.3         # MI355X FP32 vector (packed); non-packed issue is half of it
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="plummer_1m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-stride", type=int, default=4,
+                    help="oracle walks every k-th sorted target of the workload")
+    return ap.parse_args()
+
+
+def percentile(v, q):
+    v = sorted(v)
+    k = (len(v) - 1) * q
+    lo = int(k)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (k - lo)
+
+
+def cpu_baseline(pos, mass, stride):
+    """The oracle as it stands, on this host's cores: the whole tree build plus
+    the walk of every stride-th sorted target; scaled to a whole evaluation."""
+    import numpy as np
+
+    import oracle
+    from barnes_hut_gravitational_amd import inputs
+
+    t0 = time.perf_counter()
+    t = oracle.build_tree(pos, mass, inputs.LEAF_CAP)
+    t1 = time.perf_counter()
+    targets = np.arange(0, t.n, stride, dtype=np.int64)
+    _, pp, pc, _ = oracle.walk(t, inputs.EPS, inputs.THETA, targets)
+    t2 = time.perf_counter()
+    inter = float(pp.sum(dtype=np.int64) + pc.sum(dtype=np.int64)) * t.n / len(targets)
+    eval_s = (t1 - t0) + (t2 - t1) * t.n / len(targets)
+    return {"value": inter / eval_s, "unit": "interactions/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"tree build of all {t.n} particles ({t1 - t0:.2f} s, serial) + walk of every "
+                      f"{stride}th sorted target ({len(targets)} targets, {t2 - t1:.2f} s, OpenMP); "
+                      f"scaled to one whole evaluation ({eval_s * 1e3:.0f} ms)",
+            "eval_ms_estimated": eval_s * 1e3}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from barnes_hut_gravitational_amd import inputs, orr
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    orr.lib()
+    kind, n = inputs.CONFIGS[args.workload]
+    pos_np, mass_np = inputs.make(kind, n)
+    dev = torch.device("cuda:0")
+    pos = torch.from_numpy(pos_np).to(dev)
+    mass = torch.from_numpy(mass_np).to(dev)
+    ws = orr.new_workspace(n, inputs.LEAF_CAP, dev)
+    acc = torch.empty((n, 3), dtype=torch.float32, device=dev)
+    cnt = [torch.empty(n, dtype=torch.int32, device=dev) for _ in range(4)]
+    kw = dict(eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP, workspace=ws, out=(acc, cnt))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(traversal="coherent"):
+        orr.orr_eval_forces(pos, mass, traversal=traversal, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    # counts of the workload (identical every step)
+    inter = int(cnt[2].long().sum().item() + cnt[3].long().sum().item())
+    visits_own = float(cnt[0].double().mean().item())
+    visits_stepped = float(cnt[1].double().mean().item())
+
+    # timed region: K whole evaluations, events per step on the library's stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+
+    # the dominant kernel alone: K walks of the built tree, both traversals
+    tree = orr.Tree(pos, mass, inputs.LEAF_CAP, workspace=ws)
+    walk_ms = {}
+    for tr in ("coherent", "independent"):
+        tree.walk(inputs.EPS, inputs.THETA, tr, out=(acc, cnt))
+        wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        wev[0].record(stream)
+        for k in range(args.steps):
+            tree.walk(inputs.EPS, inputs.THETA, tr, out=(acc, cnt))
+            wev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        walk_ms[tr] = [wev[k].elapsed_time(wev[k + 1]) for k in range(args.steps)]
+    phases = orr.orr_eval_forces(pos, mass, traversal="coherent", timings=True, **kw).timings
+    info = tree.info()
+
+    ms = wall_ms
+    walk_mean = sum(walk_ms["coherent"]) / args.steps
+    achieved = FLOPS_PER_INTERACTION * inter / (walk_mean * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": inter / (ms * 1e-3),
+        "unit": "interactions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "kind": kind, "n": n, "eps": inputs.EPS, "theta": inputs.THETA,
+                   "leaf_cap": inputs.LEAF_CAP, "traversal": "coherent", "seed": inputs.SEED},
+        "roofline": {"bound": "alu", "kernel": "k_walk_coherent", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "flops_per_interaction": FLOPS_PER_INTERACTION, "walk_ms_mean": walk_mean},
+        "step_ms_median": percentile(step_ms, 0.5),
+        "step_ms_iqr": percentile(step_ms, 0.75) - percentile(step_ms, 0.25),
+        "walk_ms_median": {k: percentile(v, 0.5) for k, v in walk_ms.items()},
+        "coherent_speedup_walk": percentile(walk_ms["independent"], 0.5) / percentile(walk_ms["coherent"], 0.5),
+        "walk_interactions_per_s": inter / (walk_mean * 1e-3),
+        "interactions": inter,
+        "visits_own_per_particle": visits_own,
+        "visits_stepped_per_particle": visits_stepped,
+        "redundancy": visits_stepped / visits_own,
+        "phases_ms": phases,
+        "tree": {"n_nodes": info["n_nodes"], "depth": info["depth"], "n_leaves": info["n_leaves"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pos_np, mass_np, args.cpu_sample_stride)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

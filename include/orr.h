@@ -1,0 +1,192 @@
+/*
+ * orr.h - C ABI of liborr.so, the MI355X (gfx950) Barnes-Hut force evaluation.
+ *
+ * What it computes (the orrery pages):
+ *   - "sycl_tree_solver.hpp" page, "The mitigation" and "What is not given
+ *     up": a Barnes-Hut tree walk in which a 64-lane wave walks one shared
+ *     node index; a lane that accepts a cell adds the cell's monopole term and
+ *     then contributes nothing until the wave leaves that cell's subtree, so
+ *     each target sums exactly the nodes its own walk visits, in the same
+ *     order; enum TreeTraversal: the independent per-lane walk is kept as the
+ *     measured baseline.
+ *   - ADR-0029 "Mask the accepted cells rather than descending together",
+ *     Decision: the wave advances to the smallest node index any lane still
+ *     wants; Consequences: both traversals are the same function of the
+ *     input, and interaction counts equal the CPU walk's.
+ *   - performance page "docs/performance/sycl_tree.md", table "The machine and
+ *     the device": softened monopole gravity (softening 0.05), opening angle
+ *     0.5, leaf capacity 32; table "Where one evaluation goes": Morton sort,
+ *     gather, build, node staging, walk, scatter. All of these steps run on
+ *     the device here.
+ *
+ * Definitions used by every entry point (G = 1, float32 throughout):
+ *   root cube: corner lo = component-wise minimum of the positions, side L =
+ *     the largest per-axis extent (1 if that is 0); keys: 21 bits per axis,
+ *     q = min(trunc((x - lo) * (2^21 / L)), 2^21 - 1), interleaved x-major
+ *     into 63 bits; order: keys ascending, equal keys by ascending index;
+ *   tree: a node of level l is a maximal run of sorted keys sharing their top
+ *     3l bits; it splits iff it holds more than leaf_cap particles and l < 21;
+ *     children are the non-empty octants in digit order; nodes are numbered in
+ *     depth-first preorder (first child = index + 1) and escape = index +
+ *     subtree size; node side s = L * 2^-l;
+ *   moments: leaf M and S = sum m*x over its particles in sorted order,
+ *     internal M and S = sum over children in octant order, com = S / M (the
+ *     node's first particle if M = 0);
+ *   walk of target i: at node c, accept iff s^2 < theta^2 * |com - x_i|^2;
+ *     accept -> monopole term, pc += 1, go to escape; otherwise a leaf -> the
+ *     term of each of its particles in sorted order, pp += its count minus the
+ *     target itself, go to escape; otherwise -> c + 1;
+ *   term: a += m * d * (|d|^2 + eps^2)^(-3/2), d = source - target, evaluated
+ *     as r2 = ((dx*dx + dy*dy) + dz*dz) + eps^2, inv = 1/sqrt(r2),
+ *     f = m * ((inv*inv)*inv), a += f*d, each step one correctly rounded
+ *     float operation (no contraction), so results are reproducible bit for
+ *     bit and identical between the two traversals.
+ *
+ * Conventions:
+ *   - Array arguments are DEVICE pointers (HIP), contiguous, owned by the
+ *     caller; positions are [n][3] float, masses [n] float, and every output
+ *     is in the caller's particle order. Any output pointer may be NULL, in
+ *     which case that output is not written.
+ *   - The caller provides one device workspace of at least
+ *     orr_workspace_bytes(n, leaf_cap) bytes, 256-byte aligned. The library
+ *     allocates no device memory. The workspace holds the tree: it must stay
+ *     alive and untouched while a tree handle that uses it is in use.
+ *   - All device work is enqueued on the given HIP stream (NULL = the default
+ *     stream) in stream order. No call synchronises the stream unless it says
+ *     so.
+ *   - Every entry point returns a status; nothing aborts and no C++ exception
+ *     crosses the ABI. On error, orr_last_error() gives a thread-local
+ *     message; outputs are then unspecified. Argument checks happen before any
+ *     device work.
+ *   - Inputs whose positions or masses are non-finite, whose masses are
+ *     negative, or whose extent overflows float32 are detected on the device
+ *     while the tree is built; the evaluation still runs to completion on a
+ *     well-formed (but meaningless) tree, and the condition is reported as
+ *     ORR_ERR_NONFINITE by the next call that synchronises (orr_tree_info_get,
+ *     orr_tree_check, or orr_eval_forces with timings requested).
+ */
+#ifndef ORR_H
+#define ORR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORR_ABI_VERSION 1
+#define ORR_MAX_LEAF_CAP 256
+#define ORR_MAX_N 2147483647LL
+
+typedef enum {
+    ORR_OK = 0,
+    ORR_ERR_INVALID_ARG = 1, /* null pointer, bad enum, bad alignment */
+    ORR_ERR_RANGE = 2,       /* n, leaf_cap, eps or theta out of range */
+    ORR_ERR_NONFINITE = 3,   /* non-finite input found on the device */
+    ORR_ERR_HIP = 4,         /* a HIP runtime call failed */
+    ORR_ERR_WORKSPACE = 5    /* workspace smaller than orr_workspace_bytes */
+} orr_status;
+
+/* Which walk the device runs (enum TreeTraversal of the solver page). */
+typedef enum {
+    ORR_TRAVERSAL_INDEPENDENT = 0, /* one lane per target, own node index */
+    ORR_TRAVERSAL_COHERENT = 1     /* one node index per 64-lane wave, masked */
+} orr_traversal;
+
+typedef struct orr_tree orr_tree; /* host handle; device data lives in the workspace */
+
+/* Where one evaluation spent its time, in milliseconds, measured with HIP
+ * events on the stream (struct SyclTreeTimings of the solver page; phases of
+ * the performance page's "Where one evaluation goes" table). */
+typedef struct {
+    float cube_keys_ms; /* root cube and Morton keys */
+    float sort_ms;      /* radix sort of (key, index) */
+    float gather_ms;    /* particles into sorted order */
+    float build_ms;     /* topology and escape indices (node staging included) */
+    float moments_ms;   /* monopole moments */
+    float walk_ms;      /* the traversal, scatter to caller order included */
+    float total_ms;
+} orr_timings;
+
+typedef struct {
+    uint32_t n;
+    uint32_t n_nodes;
+    uint32_t n_leaves;
+    uint32_t depth;          /* deepest node level */
+    uint32_t max_leaf_count; /* may exceed leaf_cap only at level 21 */
+    int32_t leaf_cap;
+    float lo[3];
+    float side;
+    int32_t input_status;    /* ORR_OK or ORR_ERR_NONFINITE */
+} orr_tree_info;
+
+/* ABI version of the loaded library (ORR_ABI_VERSION it was built with). */
+int orr_abi_version(void);
+
+/* Static strings; never NULL. */
+const char *orr_status_string(orr_status s);
+const char *orr_traversal_name(orr_traversal t); /* "independent", "coherent", "invalid" */
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *orr_last_error(void);
+
+/* Workspace bytes needed for n particles at this leaf capacity; 0 if the
+ * arguments are out of range. Needs no GPU. The bound allows n leaves plus,
+ * on each of the 21 split levels, n / (leaf_cap + 1) internal nodes. */
+size_t orr_workspace_bytes(int64_t n, int32_t leaf_cap);
+
+/* Enqueue the tree build: root cube, keys, sort, gather, topology, escape
+ * indices and moments. pos [n][3], mass [n]. On success *out receives a host
+ * handle (free with orr_tree_free) that refers to the workspace and stream.
+ * Errors: ORR_ERR_INVALID_ARG (null pos/mass/workspace/out, workspace not
+ * 256-byte aligned), ORR_ERR_RANGE (n < 1 or n > ORR_MAX_N, leaf_cap < 1 or
+ * > ORR_MAX_LEAF_CAP), ORR_ERR_WORKSPACE, ORR_ERR_HIP. */
+orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_t leaf_cap,
+                          void *workspace, size_t workspace_bytes, void *hip_stream, orr_tree **out);
+
+/* Enqueue a walk over a built tree, on the tree's stream. eps > 0 and finite
+ * (eps = 0 would make the target's own term 0/0); theta >= 0 and finite.
+ * acc [n][3]; visits_own = nodes where the target's own walk acted (equal for
+ * both traversals); visits_stepped = nodes its wave stepped through (the
+ * union of the wave's walks for the coherent traversal, the own walk for the
+ * independent one); n_pp = particle terms (self excluded), n_pc = accepted
+ * cells. Errors: ORR_ERR_INVALID_ARG (null tree, bad traversal),
+ * ORR_ERR_RANGE (eps, theta), ORR_ERR_HIP. */
+orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_traversal traversal,
+                         float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                         uint32_t *n_pc);
+
+/* Build and walk in one call. If timings is not NULL, every phase is timed
+ * with HIP events, the stream is synchronised and the input status checked
+ * (ORR_ERR_NONFINITE possible). Errors: those of orr_build_tree and
+ * orr_tree_walk. */
+orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float eps, float theta,
+                           int32_t leaf_cap, orr_traversal traversal, float *acc, uint32_t *visits_own,
+                           uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *workspace,
+                           size_t workspace_bytes, void *hip_stream, orr_timings *timings);
+
+/* Synchronise the tree's stream and report its sizes and input status.
+ * Returns ORR_ERR_NONFINITE (with *out filled) if the input was non-finite. */
+orr_status orr_tree_info_get(const orr_tree *tree, orr_tree_info *out);
+
+/* Synchronise the stream of a previous build in this workspace and report
+ * its input status (ORR_OK or ORR_ERR_NONFINITE). */
+orr_status orr_tree_check(const orr_tree *tree);
+
+/* Enqueue device-to-device copies of the tree for inspection. Sizes: n for
+ * keys_sorted (uint64) and perm (uint32, sorted position -> caller index);
+ * n_nodes (from orr_tree_info_get) for level (uint8), begin, count, escape
+ * (uint32), geom ([n_nodes][4] float: com x, y, z, mass) and s2 (float, the
+ * squared node side). Any pointer may be NULL. */
+orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t *perm, uint8_t *level,
+                           uint32_t *begin, uint32_t *count, uint32_t *escape, float *geom, float *s2);
+
+/* Release the host handle. The workspace stays the caller's. NULL is a no-op. */
+void orr_tree_free(orr_tree *tree);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORR_H */

@@ -65,7 +65,7 @@ def lib():
         L.oracle_walk_trace.argtypes = [_f32p, _f32p, _f32p, _u32p, _u32p, _u32p, _i64, _f32, _f32, _i64,
                                         _u64p, _i64]
         L.oracle_walk_trace.restype = _i64
-        L.oracle_union_visits.argtypes = walk_head + [_i64, _u32p]
+        L.oracle_union_visits.argtypes = walk_head + [_i64, ctypes.c_void_p, _i64, _u32p]
         L.oracle_union_visits.restype = ctypes.c_int
         L.oracle_group_walk.argtypes = walk_head + [_i64, ctypes.c_int, _u32p, _u32p]
         L.oracle_group_walk.restype = ctypes.c_int
@@ -218,12 +218,16 @@ def walk_trace(t: Tree, eps, theta, target):
     return (buf[:k] >> np.uint64(2)).astype(np.int64), (buf[:k] & np.uint64(3)).astype(np.int64)
 
 
-def union_visits(t: Tree, eps, theta, width=64):
-    """Per group of `width` consecutive sorted targets: size of the union of the
-    members' visited node sets."""
-    groups = (t.n + width - 1) // width
-    out = np.empty(groups, np.uint32)
-    st = lib().oracle_union_visits(*_walk_args(t, eps, theta), width, out)
+def union_visits(t: Tree, eps, theta, width=64, groups=None):
+    """Per group of `width` consecutive sorted targets (all groups, or the
+    listed group indices): size of the union of the members' visited node sets."""
+    if groups is None:
+        m, gp = (t.n + width - 1) // width, None
+    else:
+        groups = np.ascontiguousarray(groups, np.int64)
+        m, gp = len(groups), groups.ctypes.data_as(ctypes.c_void_p)
+    out = np.empty(m, np.uint32)
+    st = lib().oracle_union_visits(*_walk_args(t, eps, theta), width, gp, m, out)
     if st:
         raise OracleError(st, "union_visits")
     return out

@@ -352,13 +352,15 @@ int64_t oracle_walk_trace(const float *xs, const float *geom, const float *s2, c
 /* the union of its lanes' walks). Groups are `width` consecutive sorted     */
 /* targets, the last one possibly partial. Plain definition: the size of the */
 /* set union of the members' own walks, computed with a bit set.             */
-/* out[g] = union size of group g.                                          */
+/* out[k] = union size of group group_ids[k] (of group k if group_ids is     */
+/* NULL, all groups).                                                        */
 /* ------------------------------------------------------------------------ */
 int oracle_union_visits(const float *xs, int64_t n, const float *geom, const float *s2,
                         const uint32_t *begin, const uint32_t *count, const uint32_t *escape,
-                        int64_t n_nodes, float eps, float theta, int64_t width, uint32_t *out) {
+                        int64_t n_nodes, float eps, float theta, int64_t width, const int64_t *group_ids,
+                        int64_t n_groups, uint32_t *out) {
     walk_ctx W = {xs, geom, s2, begin, count, escape, n_nodes, eps * eps, theta * theta};
-    int64_t groups = (n + width - 1) / width;
+    int64_t groups = group_ids ? n_groups : (n + width - 1) / width;
     int64_t words = (n_nodes + 63) / 64;
     int failed = 0;
 #pragma omp parallel
@@ -370,7 +372,8 @@ int oracle_union_visits(const float *xs, int64_t n, const float *geom, const flo
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 4)
-            for (int64_t g = 0; g < groups; g++) {
+            for (int64_t gi = 0; gi < groups; gi++) {
+                int64_t g = group_ids ? group_ids[gi] : gi;
                 memset(bits, 0, (size_t)words * sizeof(uint64_t));
                 int64_t hi = (g + 1) * width < n ? (g + 1) * width : n;
                 for (int64_t i = g * width; i < hi; i++) {
@@ -384,7 +387,7 @@ int oracle_union_visits(const float *xs, int64_t n, const float *geom, const flo
                 }
                 uint32_t total = 0;
                 for (int64_t w = 0; w < words; w++) total += (uint32_t)__builtin_popcountll(bits[w]);
-                out[g] = total;
+                out[gi] = total;
             }
         }
         free(bits);

@@ -1,0 +1,75 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and compare it with the oracle, element by element."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from barnes_hut_gravitational_amd import orr
+
+# The stated bar for float32 accelerations: max relative per-particle error.
+ACC_REL_TOL = 1e-5
+
+
+def to_dev(pos, mass):
+    return torch.from_numpy(np.ascontiguousarray(pos)).cuda(), torch.from_numpy(np.ascontiguousarray(mass)).cuda()
+
+
+def u32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def check_tree(tree: orr.Tree, ot: oracle.Tree):
+    """Keys, order, topology and node records bit-exact."""
+    info = tree.info()
+    assert info["input_status"] == 0
+    assert info["n_nodes"] == ot.n_nodes
+    assert info["depth"] == ot.depth
+    assert info["n_leaves"] == int(ot.is_leaf().sum())
+    assert info["max_leaf_count"] == int(ot.count[ot.is_leaf()].max())
+    assert np.array_equal(np.array(info["lo"], np.float32).view(np.uint32), ot.lo.view(np.uint32))
+    assert np.float32(info["side"]) == ot.side
+    ex = tree.export()
+    torch.cuda.synchronize()
+    assert np.array_equal(ex["keys_sorted"].cpu().numpy().view(np.uint64), ot.keys_sorted)
+    assert np.array_equal(u32(ex["perm"]), ot.perm)
+    assert np.array_equal(ex["level"].cpu().numpy(), ot.level)
+    assert np.array_equal(u32(ex["begin"]), ot.begin)
+    assert np.array_equal(u32(ex["count"]), ot.count)
+    assert np.array_equal(u32(ex["escape"]), ot.escape)
+    assert np.array_equal(u32(ex["s2"]), ot.s2.view(np.uint32))
+    assert np.array_equal(u32(ex["geom"]), ot.geom.view(np.uint32))
+
+
+def rel_err(acc: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    num = np.linalg.norm(acc.astype(np.float64) - ref, axis=1)
+    den = np.linalg.norm(ref.astype(np.float64), axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), np.where(num > 0, np.inf, 0.0))
+
+
+def check_walk(r: orr.Result, ref: oracle.Result, traversal: str, rows=None):
+    """Counts bit-exact, accelerations within ACC_REL_TOL. rows: caller-order
+    indices to compare (all if None); ref arrays are indexed like rows."""
+    sel = slice(None) if rows is None else rows
+    acc = r.acc.cpu().numpy()[sel]
+    assert rel_err(acc, ref.acc).max() <= ACC_REL_TOL
+    assert np.array_equal(u32(r.visits_own)[sel], ref.visits_own)
+    assert np.array_equal(u32(r.n_pp)[sel], ref.n_pp)
+    assert np.array_equal(u32(r.n_pc)[sel], ref.n_pc)
+    stepped = ref.visits_stepped if traversal == "coherent" else ref.visits_own
+    assert np.array_equal(u32(r.visits_stepped)[sel], stepped)
+
+
+def check_acc_bitwise(r: orr.Result, ref_acc: np.ndarray, rows=None):
+    sel = slice(None) if rows is None else rows
+    assert np.array_equal(r.acc.cpu().numpy()[sel].view(np.uint32), ref_acc.view(np.uint32))
+
+
+def sampled_reference(ot: oracle.Tree, eps, theta, targets_sorted: np.ndarray, groups: np.ndarray, width=64):
+    """Oracle outputs for selected sorted targets, plus union visits of selected
+    groups; returned in the caller order of those targets."""
+    acc, pp, pc, vis = oracle.walk(ot, eps, theta, targets_sorted)
+    union = oracle.union_visits(ot, eps, theta, width, groups)
+    return acc, pp, pc, vis, union

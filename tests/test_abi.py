@@ -1,0 +1,98 @@
+"""CPU-side checks of the C ABI: the built library loads, exports every entry
+point include/orr.h declares, and rejects bad arguments before any device
+work (no GPU is touched by these calls)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from barnes_hut_gravitational_amd import orr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orr.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(orr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_binding_names():
+    assert declared() == sorted(orr.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = orr.lib()
+    for name in declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", orr.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(declared()) <= syms
+
+
+def test_static_strings_and_version():
+    L = orr.lib()
+    assert orr.abi_version() == 1
+    assert L.orr_traversal_name(0) == b"independent" and L.orr_traversal_name(1) == b"coherent"
+    assert L.orr_traversal_name(7) == b"invalid"
+    assert L.orr_status_string(0) == b"ok" and L.orr_status_string(5) == b"workspace too small"
+    assert L.orr_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    assert orr.workspace_bytes(0, 32) == 0
+    assert orr.workspace_bytes(100, 0) == 0 and orr.workspace_bytes(100, 257) == 0
+    assert orr.workspace_bytes(2**31, 32) == 0
+    assert orr.workspace_bytes(2**31 - 1, 32) > 0
+    a, b = orr.workspace_bytes(1 << 20, 32), orr.workspace_bytes(1 << 20, 1)
+    assert 0 < a < b
+    assert a % 256 == 0
+    # grows with n
+    assert orr.workspace_bytes(1000, 32) < orr.workspace_bytes(2000, 32)
+
+
+def _eval(**kw):
+    L = orr.lib()
+    args = dict(pos=1, mass=1, n=100, eps=0.05, theta=0.5, cap=32, tr=1, ws=256, ws_bytes=1 << 30)
+    args.update(kw)
+    st = L.orr_eval_forces(args["pos"], args["mass"], args["n"], args["eps"], args["theta"], args["cap"],
+                           args["tr"], None, None, None, None, None, args["ws"], args["ws_bytes"], None, None)
+    return st, L.orr_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"n": 0}, orr.ORR_ERR_RANGE), ({"n": -5}, orr.ORR_ERR_RANGE), ({"n": 2**31}, orr.ORR_ERR_RANGE),
+    ({"cap": 0}, orr.ORR_ERR_RANGE), ({"cap": 300}, orr.ORR_ERR_RANGE),
+    ({"eps": 0.0}, orr.ORR_ERR_RANGE), ({"eps": -1.0}, orr.ORR_ERR_RANGE), ({"eps": float("inf")}, orr.ORR_ERR_RANGE),
+    ({"eps": float("nan")}, orr.ORR_ERR_RANGE), ({"theta": -0.1}, orr.ORR_ERR_RANGE),
+    ({"theta": float("nan")}, orr.ORR_ERR_RANGE), ({"tr": 2}, orr.ORR_ERR_INVALID_ARG),
+    ({"pos": None}, orr.ORR_ERR_INVALID_ARG), ({"mass": None}, orr.ORR_ERR_INVALID_ARG),
+    ({"ws": None}, orr.ORR_ERR_INVALID_ARG), ({"ws": 256 + 8}, orr.ORR_ERR_INVALID_ARG),
+    ({"ws_bytes": 1000}, orr.ORR_ERR_WORKSPACE)])
+def test_eval_argument_errors(kw, status):
+    st, msg = _eval(**kw)
+    assert st == status and msg
+
+
+def test_build_and_walk_argument_errors():
+    L = orr.lib()
+    h = ctypes.c_void_p()
+    assert L.orr_build_tree(1, 1, 100, 32, 256, 1 << 30, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_build_tree(1, 1, 0, 32, 256, 1 << 30, None, ctypes.byref(h)) == orr.ORR_ERR_RANGE
+    assert h.value is None
+    assert L.orr_tree_walk(None, 0.05, 0.5, 1, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_check(None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_export(None, None, None, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    L.orr_tree_free(None)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(orr.OrrError):
+        orr.orr_eval_forces(torch.zeros(4, 3), torch.ones(4))

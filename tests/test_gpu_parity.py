@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work (keys, order, topology, escape indices, node records, per-target
+interaction and visit counts) must match bit for bit; float32 accelerations
+within 1e-5 max relative per-particle error, and, by construction of the
+term's operation sequence, bit for bit. The two traversals must agree with
+each other exactly (ADR-0029, Consequences).
+"""
+
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from barnes_hut_gravitational_amd import inputs, orr
+
+from parity import check_acc_bitwise, check_tree, check_walk, rel_err, sampled_reference, to_dev, u32, ACC_REL_TOL
+
+pytestmark = pytest.mark.gpu
+EPS, THETA = inputs.EPS, inputs.THETA
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    orr.lib()
+
+
+def run_full_case(pos, mass, cap, eps, theta):
+    print(f"[case] n={len(mass)} cap={cap} eps={eps} theta={theta}", flush=True)
+    ref = oracle.evaluate(pos, mass, eps, theta, cap)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, cap)
+    check_tree(tree, ref.tree)
+    res = {}
+    for tr in ("coherent", "independent"):
+        r = tree.walk(eps, theta, tr)
+        torch.cuda.synchronize()
+        check_walk(r, ref, tr)
+        check_acc_bitwise(r, ref.acc)
+        res[tr] = r
+    a, b = res["coherent"], res["independent"]
+    assert torch.equal(a.acc.view(torch.int32), b.acc.view(torch.int32))
+    for f in ("visits_own", "n_pp", "n_pc"):
+        assert torch.equal(getattr(a, f), getattr(b, f))
+    return ref, res
+
+
+SMALL = [("plummer", n, 32, 0.5) for n in (1, 2, 3, 31, 32, 33, 63, 64, 65, 100, 257, 1000, 4097)] + [
+    ("plummer", 2000, 1, 0.5), ("plummer", 2000, 8, 0.0), ("plummer", 3000, 256, 0.5), ("merger", 5000, 16, 0.7),
+    ("uniform", 6000, 32, 0.3), ("plummer", 4096, 32, 1.0), ("merger", 2048, 3, 100.0)]
+
+
+@pytest.mark.parametrize("kind,n,cap,theta", SMALL)
+def test_small_cases(kind, n, cap, theta):
+    pos, mass = inputs.make(kind, n)
+    run_full_case(pos, mass, cap, EPS, theta)
+
+
+def test_unequal_masses_and_small_eps():
+    pos, mass = inputs.make("plummer", 3000)
+    mass = (mass * np.random.default_rng(2).uniform(0.1, 3.0, 3000)).astype(np.float32)
+    mass[::7] = 0.0
+    run_full_case(pos, mass, 32, 1e-3, 0.5)
+
+
+def test_degenerate_inputs():
+    # all particles at one point: a chain down to level 21 ending in one big leaf
+    run_full_case(np.full((100, 3), 0.25, np.float32), np.full(100, 0.01, np.float32), 32, EPS, 0.5)
+    # heavy duplicates on a coarse lattice, over-cap leaves at level 21
+    rng = np.random.default_rng(4)
+    pos = rng.integers(0, 3, (3000, 3)).astype(np.float32)
+    run_full_case(pos, np.full(3000, 1 / 3000, np.float32), 8, EPS, 0.5)
+    # collinear, and a flat (zero-extent) axis
+    t = np.linspace(-1, 1, 1500, dtype=np.float32)
+    run_full_case(np.stack([t, 2 * t, np.zeros_like(t)], 1), np.full(1500, 1 / 1500, np.float32), 32, EPS, 0.5)
+    # tiny and huge coordinate scales
+    pos, mass = inputs.make("plummer", 2000)
+    run_full_case(pos * np.float32(1e-30), mass, 32, EPS, 0.5)
+    run_full_case(pos * np.float32(1e30), mass, 32, EPS, 0.5)
+
+
+@pytest.mark.parametrize("name", ["plummer_16k", "plummer_131k", "uniform_262k"])
+def test_configs_full(name):
+    pos, mass = inputs.make_config(name)
+    ref, _ = run_full_case(pos, mass, inputs.LEAF_CAP, EPS, THETA)
+    st = ref.visits_stepped.astype(np.float64).mean() / ref.visits_own.astype(np.float64).mean()
+    print(f"[{name}] nodes={ref.tree.n_nodes} visits own {ref.visits_own.mean():.0f} "
+          f"stepped {ref.visits_stepped.mean():.0f} redundancy {st:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["plummer_1m", "merger_8m"])
+def test_configs_large_sampled(name):
+    """Full-size workloads in the launch configuration the benchmark times:
+    the whole tree bit-exact; the walk on sampled targets and waves; the two
+    traversals identical on every target."""
+    pos, mass = inputs.make_config(name)
+    n = len(mass)
+    print(f"[case] {name} n={n}", flush=True)
+    ot = oracle.build_tree(pos, mass, inputs.LEAF_CAP)
+    P, M = to_dev(pos, mass)
+    ws = orr.new_workspace(n, inputs.LEAF_CAP, P.device)
+    r = orr.orr_eval_forces(P, M, eps=EPS, theta=THETA, leaf_cap=inputs.LEAF_CAP, traversal="coherent",
+                            workspace=ws, timings=True)
+    tree = orr.Tree(P, M, inputs.LEAF_CAP, workspace=ws)
+    check_tree(tree, ot)
+    ri = tree.walk(EPS, THETA, "independent")
+    torch.cuda.synchronize()
+    assert torch.equal(r.acc.view(torch.int32), ri.acc.view(torch.int32))
+    for f in ("visits_own", "n_pp", "n_pc"):
+        assert torch.equal(getattr(r, f), getattr(ri, f))
+    rng = np.random.default_rng(7)
+    groups = np.sort(rng.choice((n + 63) // 64, 24, replace=False))
+    targets = np.unique(np.concatenate([rng.choice(n, 3000, replace=False),
+                                        (groups[:, None] * 64 + np.arange(64)).ravel()]))
+    acc, pp, pc, vis, union = sampled_reference(ot, EPS, THETA, targets, groups)
+    rows = ot.perm[targets].astype(np.int64)
+    assert rel_err(r.acc.cpu().numpy()[rows], acc).max() <= ACC_REL_TOL
+    check_acc_bitwise(r, acc, rows)
+    assert np.array_equal(u32(r.visits_own)[rows], vis)
+    assert np.array_equal(u32(r.n_pp)[rows], pp)
+    assert np.array_equal(u32(r.n_pc)[rows], pc)
+    stepped = u32(r.visits_stepped)[ot.perm[(groups[:, None] * 64 + np.arange(64)).ravel()].astype(np.int64)]
+    assert np.array_equal(stepped.reshape(-1, 64), np.repeat(union[:, None], 64, 1))
+    print(f"[{name}] timings {r.timings}", flush=True)
+
+
+def test_nonfinite_input_reported():
+    pos, mass = inputs.make("plummer", 1000)
+    for bad_pos, bad_mass in ((np.nan, None), (np.inf, None), (None, -1.0), (None, np.nan)):
+        p, m = pos.copy(), mass.copy()
+        if bad_pos is not None:
+            p[17, 1] = bad_pos
+        if bad_mass is not None:
+            m[5] = bad_mass
+        P, M = to_dev(p, m)
+        with pytest.raises(orr.OrrError) as e:
+            orr.orr_eval_forces(P, M, timings=True)
+        assert e.value.status == orr.ORR_ERR_NONFINITE
+        tree = orr.Tree(P, M, 32)
+        tree.walk()
+        with pytest.raises(orr.OrrError):
+            tree.check()
+        assert tree.info()["input_status"] == orr.ORR_ERR_NONFINITE
+    # the next good input on the same workspace is clean
+    P, M = to_dev(pos, mass)
+    orr.orr_eval_forces(P, M, timings=True)
+
+
+def test_workspace_reuse_and_side_stream():
+    """A workspace reused for a smaller input, on a non-default stream."""
+    big, small = inputs.make("plummer", 20000), inputs.make("uniform", 3000)
+    ws = orr.new_workspace(20000, 32, "cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for pos, mass in (big, small, big):
+            ref = oracle.evaluate(pos, mass, EPS, THETA, 32)
+            P, M = to_dev(pos, mass)
+            r = orr.orr_eval_forces(P, M, workspace=ws)
+            s.synchronize()
+            check_walk(r, ref, "coherent")
+
+
+def test_argument_errors_on_device_tensors():
+    P, M = to_dev(*inputs.make("plummer", 100))
+    for kw in ({"eps": 0.0}, {"eps": float("nan")}, {"theta": -1.0}, {"leaf_cap": 0}, {"leaf_cap": 257}):
+        with pytest.raises(orr.OrrError) as e:
+            orr.orr_eval_forces(P, M, **kw)
+        assert e.value.status == orr.ORR_ERR_RANGE
+    with pytest.raises(orr.OrrError) as e:
+        orr.orr_eval_forces(P, M, workspace=torch.empty(1024, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == orr.ORR_ERR_WORKSPACE
+
+
+def test_native_library_loaded_once():
+    """The in-tree liborr.so is the code that ran, over the same HIP runtime as torch."""
+    maps = open("/proc/self/maps").read()
+    assert orr.LIB_PATH in maps
+    runtimes = {m for m in re.findall(r"(/\S*libamdhip64\.so[.\d]*)", maps)}
+    assert len({os.path.realpath(p) for p in runtimes}) == 1, runtimes
