@@ -357,6 +357,20 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
     ORR_GUARD_END
 }
 
+orr_status orr_selftest_inv_sqrt(uint32_t first_bits, uint32_t last_bits, uint64_t *mismatches,
+                                 uint32_t *examples, void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!mismatches || !examples) return fail(ORR_ERR_INVALID_ARG, "mismatches and examples must not be NULL");
+    if (first_bits > last_bits) return fail(ORR_ERR_INVALID_ARG, "first_bits > last_bits");
+    hipError_t e = launch_selftest_inv_sqrt(first_bits, (uint64_t)last_bits - first_bits + 1,
+                                            reinterpret_cast<unsigned long long *>(mismatches), examples,
+                                            static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "inverse square root self-check");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
 void orr_tree_free(orr_tree *tree) { delete tree; }
 
 }  // extern "C"

@@ -80,6 +80,10 @@ hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float thet
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s);
 
+hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
+                                    uint32_t *examples, hipStream_t s);
+bool walk_uses_fast_inv(float eps2);
+
 // Device-wide exclusive scan of len uint32 values, in place allowed
 // (in == out). If total is not null it receives the sum.
 hipError_t launch_exclusive_scan(const uint32_t *in, uint32_t *out, int64_t len, uint32_t *part,

@@ -21,20 +21,62 @@
 // performance page's "Where one evaluation goes" table).
 #include "orr_internal.h"
 
+#ifndef ORR_WALK_BLOCK
+#define ORR_WALK_BLOCK 256
+#endif
+#ifndef ORR_XCD_REMAP
+#define ORR_XCD_REMAP 1
+#endif
+
 namespace orr {
 
 namespace {
 
+constexpr uint32_t kWalkBlock = ORR_WALK_BLOCK;  // threads per block (multiple of 64)
+
+// RN(1 / RN(sqrt(x))) for x in [2^-96, +inf] without the range scaling and
+// special-value handling of the general IEEE sequences, which this domain
+// never needs (x >= eps^2 >= 2^-96). sqrt: the hardware estimate is within one
+// ulp; the correctly rounded root is chosen among it and its two neighbours by
+// the signs of the exact residuals x - s'*s (fma). Reciprocal: the hardware
+// estimate refined by one Newton step y += y * (1 - s*y) in fma, which is
+// correctly rounded for every s = sqrt(x) of this domain. Equality with the
+// IEEE operations for every float of the domain is checked by
+// orr_selftest_inv_sqrt.
+__device__ __forceinline__ float inv_sqrt_rn(float x) {
+    float s = __builtin_amdgcn_sqrtf(x);
+    const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+    const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+    const float rm = fmaf(-sm, s, x);
+    const float rp = fmaf(-sp, s, x);
+    s = (rm <= 0.0f) ? sm : s;
+    s = (rp > 0.0f) ? sp : s;
+    float y = __builtin_amdgcn_rcpf(s);
+    const float e = fmaf(-s, y, 1.0f);
+    y = fmaf(e, y, y);
+    return (x == INFINITY) ? 0.0f : y;
+}
+
 // a += m * d * (|d|^2 + eps^2)^(-3/2), every step one correctly rounded float
-// operation; the library is compiled without contraction.
+// operation; the library is compiled without contraction. kFastInv selects
+// inv_sqrt_rn (bit-identical on its domain) over the general IEEE sequences.
+template <bool kFastInv>
 __device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, float eps2, float &ax, float &ay,
                                          float &az) {
     const float r2 = ((dx * dx + dy * dy) + dz * dz) + eps2;
-    const float inv = 1.0f / sqrtf(r2);
+    const float inv = kFastInv ? inv_sqrt_rn(r2) : 1.0f / sqrtf(r2);
     const float f = m * ((inv * inv) * inv);
     ax += f * dx;
     ay += f * dy;
     az += f * dz;
+}
+
+// Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous run
+// of target blocks so that its L2 holds one region of the tree.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
+    if (!ORR_XCD_REMAP) return b;
+    const uint32_t x = b & 7u, q = nblocks >> 3, r = nblocks & 7u;
+    return x * q + min(x, r) + (b >> 3);
 }
 
 struct WalkOut {
@@ -55,22 +97,25 @@ __device__ __forceinline__ void write_out(const WalkOut &o, uint32_t dst, float 
     if (o.n_pc) o.n_pc[dst] = pc;
 }
 
-__global__ __launch_bounds__(256) void k_walk_coherent(const float4 *__restrict__ xs,
+template <bool kFastInv>
+__global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
                                                        const float4 *__restrict__ geom,
                                                        const uint4 *__restrict__ topo,
                                                        const DevParams *__restrict__ prm,
                                                        const uint32_t *__restrict__ perm, uint32_t n,
                                                        uint32_t max_nodes, float eps2, float theta2, WalkOut out) {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const bool valid = i < n;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
-    uint32_t vown = 0, vstep = 0, pp = 0, pc = 0;
+    uint32_t vown = 0, pp = 0, pc = 0;
+    uint32_t steps = 0;  // wave-uniform
     uint32_t c = 0;
     while (c < n_nodes) {
         c = __builtin_amdgcn_readfirstlane(c);
+        steps += 1;
         const float4 g = geom[c];
         uint4 t = topo[c];  // (escape, begin, count, s^2 bits)
         t.x = max(t.x, c + 1);  // a well-formed tree has escape > c; never step back
@@ -80,10 +125,9 @@ __global__ __launch_bounds__(256) void k_walk_coherent(const float4 *__restrict_
         const bool accept = active && (__uint_as_float(t.w) < theta2 * d2);
         const bool open = active && !accept;
         vown += active ? 1u : 0u;
-        vstep += valid ? 1u : 0u;
         if (__ballot(accept)) {
             if (accept) {
-                add_term(g.w, dx, dy, dz, eps2, ax, ay, az);
+                add_term<kFastInv>(g.w, dx, dy, dz, eps2, ax, ay, az);
                 pc += 1;
                 next = t.x;
             }
@@ -93,7 +137,7 @@ __global__ __launch_bounds__(256) void k_walk_coherent(const float4 *__restrict_
                 const uint32_t e = t.y + t.z;
                 for (uint32_t j = t.y; j < e; j++) {
                     const float4 p = xs[j];
-                    if (open) add_term(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                    if (open) add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
                 }
                 if (open) {
                     pp += t.z - ((i - t.y) < t.z ? 1u : 0u);
@@ -106,17 +150,18 @@ __global__ __launch_bounds__(256) void k_walk_coherent(const float4 *__restrict_
             c = __ballot(open) ? c + 1 : t.x;
         }
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, vown, vstep, pp, pc);
+    if (valid) write_out(out, perm[i], ax, ay, az, vown, steps, pp, pc);
 }
 
-__global__ __launch_bounds__(256) void k_walk_independent(const float4 *__restrict__ xs,
+template <bool kFastInv>
+__global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
                                                           const float4 *__restrict__ geom,
                                                           const uint4 *__restrict__ topo,
                                                           const DevParams *__restrict__ prm,
                                                           const uint32_t *__restrict__ perm, uint32_t n,
                                                           uint32_t max_nodes, float eps2, float theta2,
                                                           WalkOut out) {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const float4 xi = xs[i];
@@ -131,14 +176,14 @@ __global__ __launch_bounds__(256) void k_walk_independent(const float4 *__restri
         const float d2 = (dx * dx + dy * dy) + dz * dz;
         vown += 1;
         if (__uint_as_float(t.w) < theta2 * d2) {
-            add_term(g.w, dx, dy, dz, eps2, ax, ay, az);
+            add_term<kFastInv>(g.w, dx, dy, dz, eps2, ax, ay, az);
             pc += 1;
             c = t.x;
         } else if (t.x == c + 1) {
             const uint32_t e = t.y + t.z;
             for (uint32_t j = t.y; j < e; j++) {
                 const float4 p = xs[j];
-                add_term(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
             }
             pp += t.z - ((i - t.y) < t.z ? 1u : 0u);
             c = t.x;
@@ -149,21 +194,57 @@ __global__ __launch_bounds__(256) void k_walk_independent(const float4 *__restri
     write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
 }
 
+// Self-check of inv_sqrt_rn against the IEEE operations over the float bit
+// patterns [first, first + count).
+__global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint64_t count,
+                                                           unsigned long long *mismatches, uint32_t *examples) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256u;
+    for (uint64_t k = (uint64_t)blockIdx.x * 256u + threadIdx.x; k < count; k += stride) {
+        const uint32_t bits = first + (uint32_t)k;
+        const float x = __uint_as_float(bits);
+        const float ref = 1.0f / sqrtf(x);
+        if (__float_as_uint(inv_sqrt_rn(x)) != __float_as_uint(ref)) {
+            const unsigned long long old = atomicAdd(mismatches, 1ull);
+            if (old < 8) examples[old] = bits;
+        }
+    }
+}
+
+__global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
+
+template <bool kFast>
+hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float theta2, const WalkOut &out,
+                         hipStream_t s) {
+    const uint32_t n = (uint32_t)ws.n;
+    const uint32_t nb = (uint32_t)ws.max_nodes;
+    const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
+    if (coherent)
+        k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n, nb,
+                                                             eps2, theta2, out);
+    else
+        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n,
+                                                                nb, eps2, theta2, out);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// The fast inverse square root applies when every r^2 >= eps^2 is >= 2^-96.
+bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
 
 hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s) {
-    const uint32_t n = (uint32_t)ws.n;
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    const uint32_t nb = (uint32_t)ws.max_nodes;
-    const unsigned blocks = (unsigned)ceil_div(ws.n, 256);
-    if (coherent)
-        k_walk_coherent<<<blocks, 256, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n, nb, eps2, theta2,
-                                               out);
-    else
-        k_walk_independent<<<blocks, 256, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n, nb, eps2,
-                                                  theta2, out);
+    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, coherent, eps2, theta2, out, s);
+    return launch_walk_t<false>(ws, coherent, eps2, theta2, out, s);
+}
+
+hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
+                                    uint32_t *examples, hipStream_t s) {
+    k_zero_u64<<<1, 1, 0, s>>>(mismatches);
+    const uint64_t blocks = std::min<uint64_t>(std::max<uint64_t>(1, ceil_div((int64_t)count, 256)), 8192);
+    k_selftest_inv_sqrt<<<(unsigned)blocks, 256, 0, s>>>(first, count, mismatches, examples);
     return hipGetLastError();
 }
 

@@ -33,8 +33,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="plummer_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-stride", type=int, default=4,
-                    help="oracle walks every k-th sorted target of the workload")
+    ap.add_argument("--cpu-trials", type=int, default=5,
+                    help="whole oracle evaluations timed for the CPU baseline (median)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -46,27 +48,43 @@ def percentile(v, q):
     return v[lo] + (v[hi] - v[lo]) * (k - lo)
 
 
-def cpu_baseline(pos, mass, stride):
-    """The oracle as it stands, on this host's cores: the whole tree build plus
-    the walk of every stride-th sorted target; scaled to a whole evaluation."""
+def walk_traffic_bytes():
+    """HBM bytes per coherent-walk launch from the committed rocprofv3 counter
+    summary, or None if the walk source has changed since it was taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    prof = os.path.join(root, "profiles", "k_walk_coherent_plummer_1m.md")
+    src = os.path.join(root, "barnes_hut_gravitational_amd", "csrc", "walk.hip")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines()[:5] if ": " in l)
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if fields.get("walk-source-sha256-16", "").strip() == digest:
+            return int(fields["traffic-bytes-per-launch"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(pos, mass, trials):
+    """The oracle as it stands, on this host's cores: whole evaluations of the
+    workload (build, walk of every target, group union visits), median."""
     import numpy as np
 
     import oracle
     from barnes_hut_gravitational_amd import inputs
 
-    t0 = time.perf_counter()
-    t = oracle.build_tree(pos, mass, inputs.LEAF_CAP)
-    t1 = time.perf_counter()
-    targets = np.arange(0, t.n, stride, dtype=np.int64)
-    _, pp, pc, _ = oracle.walk(t, inputs.EPS, inputs.THETA, targets)
-    t2 = time.perf_counter()
-    inter = float(pp.sum(dtype=np.int64) + pc.sum(dtype=np.int64)) * t.n / len(targets)
-    eval_s = (t1 - t0) + (t2 - t1) * t.n / len(targets)
-    return {"value": inter / eval_s, "unit": "interactions/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"tree build of all {t.n} particles ({t1 - t0:.2f} s, serial) + walk of every "
-                      f"{stride}th sorted target ({len(targets)} targets, {t2 - t1:.2f} s, OpenMP); "
-                      f"scaled to one whole evaluation ({eval_s * 1e3:.0f} ms)",
-            "eval_ms_estimated": eval_s * 1e3}
+    times, inter = [], 0
+    for _ in range(trials):
+        t0 = time.perf_counter()
+        r = oracle.evaluate(pos, mass, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
+        times.append(time.perf_counter() - t0)
+        inter = int(r.n_pp.sum(dtype=np.int64) + r.n_pc.sum(dtype=np.int64))
+    med = percentile(times, 0.5)
+    return {"value": inter / med, "unit": "interactions/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{trials} whole oracle evaluations of the workload (tree build serial; walk and group "
+                      f"union visits OpenMP over targets), median {med * 1e3:.0f} ms, total {sum(times):.1f} s",
+            "eval_ms": med * 1e3}
 
 
 def main():
@@ -99,6 +117,13 @@ def main():
     def step(traversal="coherent"):
         orr.orr_eval_forces(pos, mass, traversal=traversal, **kw)
 
+    if args.copy_mib:
+        # a plain copy of known size: HBM traffic counters are scaled by what they read for it
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     # counts of the workload (identical every step)
@@ -152,7 +177,8 @@ def main():
         "config": {"workload": args.workload, "kind": kind, "n": n, "eps": inputs.EPS, "theta": inputs.THETA,
                    "leaf_cap": inputs.LEAF_CAP, "traversal": "coherent", "seed": inputs.SEED},
         "roofline": {"bound": "alu", "kernel": "k_walk_coherent", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": walk_traffic_bytes() if args.workload == "plummer_1m" else None,
                      "flops_per_interaction": FLOPS_PER_INTERACTION, "walk_ms_mean": walk_mean},
         "step_ms_median": percentile(step_ms, 0.5),
         "step_ms_iqr": percentile(step_ms, 0.75) - percentile(step_ms, 0.25),
@@ -168,7 +194,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pos_np, mass_np, args.cpu_sample_stride)
+        out["cpu_baseline"] = cpu_baseline(pos_np, mass_np, args.cpu_trials)
     print(json.dumps(out), flush=True)
 
 

@@ -182,6 +182,17 @@ orr_status orr_tree_check(const orr_tree *tree);
 orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t *perm, uint8_t *level,
                            uint32_t *begin, uint32_t *count, uint32_t *escape, float *geom, float *s2);
 
+/* Self-check of the walk's inverse square root. For eps >= 2^-48 the walk
+ * evaluates RN(1/RN(sqrt(r2))) with a shorter instruction sequence valid for
+ * r2 >= 2^-96 (every r2 >= eps^2 there); this enqueues a comparison of that
+ * sequence with the IEEE square root and division for every float whose bit
+ * pattern lies in [first_bits, last_bits]. *mismatches (device, uint64)
+ * receives the count and examples (device, 8 x uint32) up to 8 failing bit
+ * patterns. Errors: ORR_ERR_INVALID_ARG (null pointer, first > last),
+ * ORR_ERR_HIP. */
+orr_status orr_selftest_inv_sqrt(uint32_t first_bits, uint32_t last_bits, uint64_t *mismatches,
+                                 uint32_t *examples, void *hip_stream);
+
 /* Release the host handle. The workspace stays the caller's. NULL is a no-op. */
 void orr_tree_free(orr_tree *tree);
 

@@ -88,6 +88,8 @@ def test_build_and_walk_argument_errors():
     assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_check(None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_export(None, None, None, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_selftest_inv_sqrt(0, 1, None, 1, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_selftest_inv_sqrt(5, 1, 1, 1, None) == orr.ORR_ERR_INVALID_ARG
     L.orr_tree_free(None)
 
 

@@ -60,6 +60,19 @@ def test_small_cases(kind, n, cap, theta):
     run_full_case(pos, mass, cap, EPS, theta)
 
 
+def test_inverse_sqrt_exhaustive():
+    """The walk's shorter inverse square root equals the IEEE square root then
+    division for every float in its domain [2^-96, +inf]."""
+    first, last = 0x0F800000, 0x7F800000  # 2^-96 .. +inf
+    k, ex = orr.orr_selftest_inv_sqrt(first, last)
+    assert k == 0, [hex(v) for v in ex]
+
+
+def test_tiny_eps_uses_ieee_path():
+    pos, mass = inputs.make("plummer", 3000)
+    run_full_case(pos, mass, 32, 1e-20, 0.5)  # eps^2 is subnormal in float32
+
+
 def test_unequal_masses_and_small_eps():
     pos, mass = inputs.make("plummer", 3000)
     mass = (mass * np.random.default_rng(2).uniform(0.1, 3.0, 3000)).astype(np.float32)
