@@ -59,8 +59,7 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     w.xs = reinterpret_cast<float4 *>(take(sizeof(float4) * n));
     w.info = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
     w.base = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * (n + 1)));
-    w.geom = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
-    w.topo = reinterpret_cast<uint4 *>(take(sizeof(uint4) * nb));
+    w.nodes = reinterpret_cast<NodeRec *>(take(sizeof(NodeRec) * nb));
     w.msum = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
     w.parent = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
     w.arrive = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
@@ -339,17 +338,18 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
         const size_t nn = prm.n_nodes;
         if (level && (e = hipMemcpyAsync(level, ws.level, nn, hipMemcpyDeviceToDevice, s)) != hipSuccess)
             return hip_fail(e, "export level");
-        if (geom && (e = hipMemcpyAsync(geom, ws.geom, nn * 16, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        // node records are (com, M | escape, begin, count, s2 bits): strided copies
+        const char *rec = reinterpret_cast<const char *>(ws.nodes);
+        if (geom && (e = hipMemcpy2DAsync(geom, 16, rec, sizeof(NodeRec), 16, nn, hipMemcpyDeviceToDevice, s)) !=
+                        hipSuccess)
             return hip_fail(e, "export geom");
-        // topo is (escape, begin, count, s2 bits) per node: strided copies
         struct Field {
             void *dst;
             size_t off;
-        } fields[4] = {{escape, 0}, {begin, 4}, {count, 8}, {s2, 12}};
+        } fields[4] = {{escape, 16}, {begin, 20}, {count, 24}, {s2, 28}};
         for (const Field &f : fields) {
             if (!f.dst) continue;
-            e = hipMemcpy2DAsync(f.dst, 4, reinterpret_cast<const char *>(ws.topo) + f.off, 16, 4, nn,
-                                 hipMemcpyDeviceToDevice, s);
+            e = hipMemcpy2DAsync(f.dst, 4, rec + f.off, sizeof(NodeRec), 4, nn, hipMemcpyDeviceToDevice, s);
             if (e != hipSuccess) return hip_fail(e, "export topology");
         }
     }

@@ -38,6 +38,14 @@ struct DevParams {
 };
 static_assert(sizeof(DevParams) == 64, "DevParams layout");
 
+// One tree node, 32 bytes: g = (com.x, com.y, com.z, M),
+// t = (escape, begin, count, bits of s^2). A wave reads it with one scalar load.
+struct alignas(32) NodeRec {
+    float4 g;
+    uint4 t;
+};
+static_assert(sizeof(NodeRec) == 32, "NodeRec layout");
+
 // Device pointers carved from the caller's workspace.
 struct Workspace {
     DevParams *prm;
@@ -49,8 +57,7 @@ struct Workspace {
     float4 *xs;            // [n] sorted (x, y, z, m)
     uint32_t *info;        // [n] first level started | leaf depth << 8
     uint32_t *base;        // [n + 1] nodes started per particle, scanned in place
-    float4 *geom;          // [max_nodes] (com, M)
-    uint4 *topo;           // [max_nodes] (escape, begin, count, bits of s^2)
+    NodeRec *nodes;        // [max_nodes]
     float4 *msum;          // [max_nodes] (S, M), unnormalised sums for the parent
     uint32_t *parent;      // [max_nodes]
     uint32_t *arrive;      // [max_nodes] children finished, for the bottom-up pass

@@ -125,7 +125,7 @@ __device__ uint32_t cell_begin(const uint64_t *__restrict__ keys, uint32_t i, in
 __global__ __launch_bounds__(256) void k_tree_emit(const uint64_t *__restrict__ keys,
                                                    const uint32_t *__restrict__ info,
                                                    const uint32_t *__restrict__ base, uint32_t n,
-                                                   const DevParams *__restrict__ prm, uint4 *__restrict__ topo,
+                                                   const DevParams *__restrict__ prm, NodeRec *__restrict__ nodes,
                                                    uint8_t *__restrict__ level, uint32_t *__restrict__ parent,
                                                    uint32_t *__restrict__ arrive) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_tree_emit(const uint64_t *__restrict__ 
         const uint32_t end = cell_end(keys, n, i, sh, ki >> sh);
         const float s = ldexpf(side, -l);  // exact
         const float s2 = s * s;
-        topo[node] = make_uint4(base[end], i, end - i, __float_as_uint(s2));
+        nodes[node].t = make_uint4(base[end], i, end - i, __float_as_uint(s2));
         level[node] = (uint8_t)l;
         arrive[node] = 0u;
         uint32_t par;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void k_tree_emit(const uint64_t *__restrict__ 
 }
 
 __device__ __forceinline__ void store_node(uint32_t k, float M, float sx, float sy, float sz, float4 first,
-                                           float4 *__restrict__ msum, float4 *__restrict__ geom) {
+                                           float4 *__restrict__ msum, NodeRec *__restrict__ nodes) {
     msum[k] = make_float4(sx, sy, sz, M);
     float4 g;
     if (M > 0.0f) {
@@ -167,19 +167,19 @@ __device__ __forceinline__ void store_node(uint32_t k, float M, float sx, float 
     } else {
         g = make_float4(first.x, first.y, first.z, M);
     }
-    geom[k] = g;
+    nodes[k].g = g;
 }
 
 // One thread per node slot; leaves start, the last child of each parent
 // finishes it. No thread waits on another.
-__global__ __launch_bounds__(256) void k_moments(const float4 *__restrict__ xs, const uint4 *__restrict__ topo,
+__global__ __launch_bounds__(256) void k_moments(const float4 *__restrict__ xs, NodeRec *nodes,
                                                  const uint32_t *__restrict__ parent,
                                                  const DevParams *__restrict__ prm, uint32_t max_nodes,
-                                                 float4 *msum, float4 *geom, uint32_t *arrive) {
+                                                 float4 *msum, uint32_t *arrive) {
     const uint32_t k = blockIdx.x * 256u + threadIdx.x;
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     if (k >= nn) return;
-    const uint4 t = topo[k];
+    const uint4 t = nodes[k].t;
     if (t.x != k + 1) return;  // internal node: finished by its last child
     float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
     for (uint32_t j = t.y; j < t.y + t.z; j++) {
@@ -189,28 +189,28 @@ __global__ __launch_bounds__(256) void k_moments(const float4 *__restrict__ xs, 
         sy += p.w * p.y;
         sz += p.w * p.z;
     }
-    store_node(k, M, sx, sy, sz, xs[t.y], msum, geom);
+    store_node(k, M, sx, sy, sz, xs[t.y], msum, nodes);
     uint32_t c = k;
     while (c != 0) {
         const uint32_t p = parent[c];
         if (p >= c) return;  // parents precede children in preorder
-        const uint4 tp = topo[p];
+        const uint4 tp = nodes[p].t;
         uint32_t nch = 0;
         const uint32_t pend = min(tp.x, nn);
-        for (uint32_t q = p + 1; q < pend; q = max(topo[q].x, q + 1)) nch++;
+        for (uint32_t q = p + 1; q < pend; q = max(nodes[q].t.x, q + 1)) nch++;
         // release this node's sums, then count it; the last arrival acquires
         // every sibling's sums
         const uint32_t old = __hip_atomic_fetch_add(&arrive[p], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (old != nch - 1) return;
         M = sx = sy = sz = 0.0f;
-        for (uint32_t q = p + 1; q < pend; q = max(topo[q].x, q + 1)) {
+        for (uint32_t q = p + 1; q < pend; q = max(nodes[q].t.x, q + 1)) {
             const float4 cs = msum[q];
             M += cs.w;
             sx += cs.x;
             sy += cs.y;
             sz += cs.z;
         }
-        store_node(p, M, sx, sy, sz, xs[tp.y], msum, geom);
+        store_node(p, M, sx, sy, sz, xs[tp.y], msum, nodes);
         c = p;
     }
 }
@@ -222,13 +222,13 @@ __global__ void k_info_zero(DevParams *prm) {
     prm->max_leaf_count = 0;
 }
 
-__global__ __launch_bounds__(256) void k_info(const uint4 *__restrict__ topo, const uint8_t *__restrict__ level,
+__global__ __launch_bounds__(256) void k_info(const NodeRec *__restrict__ nodes, const uint8_t *__restrict__ level,
                                               uint32_t max_nodes, DevParams *prm) {
     const uint32_t k = blockIdx.x * 256u + threadIdx.x;
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     uint32_t leaf = 0, dep = 0, cnt = 0;
     if (k < nn) {
-        const uint4 t = topo[k];
+        const uint4 t = nodes[k].t;
         dep = level[k];
         if (t.x == k + 1) {
             leaf = 1;
@@ -256,21 +256,20 @@ hipError_t launch_build(const Workspace &ws, hipStream_t s) {
     k_tree_count<<<blocks, 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info, ws.base);
     hipError_t e = launch_exclusive_scan(ws.base, ws.base, ws.n + 1, ws.scan_part, &ws.prm->n_nodes, s);
     if (e != hipSuccess) return e;
-    k_tree_emit<<<blocks, 256, 0, s>>>(ws.keys[0], ws.info, ws.base, n, ws.prm, ws.topo, ws.level, ws.parent,
+    k_tree_emit<<<blocks, 256, 0, s>>>(ws.keys[0], ws.info, ws.base, n, ws.prm, ws.nodes, ws.level, ws.parent,
                                        ws.arrive);
     return hipGetLastError();
 }
 
 hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
-    k_moments<<<(unsigned)ceil_div(ws.max_nodes, 256), 256, 0, s>>>(ws.xs, ws.topo, ws.parent, ws.prm,
-                                                                      (uint32_t)ws.max_nodes, ws.msum, ws.geom,
-                                                                      ws.arrive);
+    k_moments<<<(unsigned)ceil_div(ws.max_nodes, 256), 256, 0, s>>>(ws.xs, ws.nodes, ws.parent, ws.prm,
+                                                                      (uint32_t)ws.max_nodes, ws.msum, ws.arrive);
     return hipGetLastError();
 }
 
 hipError_t launch_tree_info(const Workspace &ws, hipStream_t s) {
     k_info_zero<<<1, 1, 0, s>>>(ws.prm);
-    k_info<<<(unsigned)ceil_div(ws.max_nodes, 256), 256, 0, s>>>(ws.topo, ws.level, (uint32_t)ws.max_nodes, ws.prm);
+    k_info<<<(unsigned)ceil_div(ws.max_nodes, 256), 256, 0, s>>>(ws.nodes, ws.level, (uint32_t)ws.max_nodes, ws.prm);
     return hipGetLastError();
 }
 

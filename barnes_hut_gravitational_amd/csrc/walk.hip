@@ -34,16 +34,19 @@ namespace {
 
 constexpr uint32_t kWalkBlock = ORR_WALK_BLOCK;  // threads per block (multiple of 64)
 
-// RN(1 / RN(sqrt(x))) for x in [2^-96, +inf] without the range scaling and
+// RN(1 / RN(sqrt(x))) for x in [2^-96, FLT_MAX] without the range scaling and
 // special-value handling of the general IEEE sequences, which this domain
 // never needs (x >= eps^2 >= 2^-96). sqrt: the hardware estimate is within one
 // ulp; the correctly rounded root is chosen among it and its two neighbours by
 // the signs of the exact residuals x - s'*s (fma). Reciprocal: the hardware
 // estimate refined by one Newton step y += y * (1 - s*y) in fma, which is
-// correctly rounded for every s = sqrt(x) of this domain. Equality with the
-// IEEE operations for every float of the domain is checked by
-// orr_selftest_inv_sqrt.
+// correctly rounded for every s = sqrt(x) of this domain. x = +inf (only from
+// coordinate differences beyond float range) is clamped to FLT_MAX: its
+// inverse cube then underflows to 0, as 1/inf cubed does. Equality of the cube
+// with the IEEE operations' cube for every float in [2^-96, +inf] is checked
+// by orr_selftest_inv_sqrt.
 __device__ __forceinline__ float inv_sqrt_rn(float x) {
+    x = fminf(x, 3.40282347e38f);
     float s = __builtin_amdgcn_sqrtf(x);
     const float sm = __uint_as_float(__float_as_uint(s) - 1u);
     const float sp = __uint_as_float(__float_as_uint(s) + 1u);
@@ -51,24 +54,30 @@ __device__ __forceinline__ float inv_sqrt_rn(float x) {
     const float rp = fmaf(-sp, s, x);
     s = (rm <= 0.0f) ? sm : s;
     s = (rp > 0.0f) ? sp : s;
-    float y = __builtin_amdgcn_rcpf(s);
+    const float y = __builtin_amdgcn_rcpf(s);
     const float e = fmaf(-s, y, 1.0f);
-    y = fmaf(e, y, y);
-    return (x == INFINITY) ? 0.0f : y;
+    return fmaf(e, y, y);
 }
 
-// a += m * d * (|d|^2 + eps^2)^(-3/2), every step one correctly rounded float
-// operation; the library is compiled without contraction. kFastInv selects
-// inv_sqrt_rn (bit-identical on its domain) over the general IEEE sequences.
+// a += m * d * r2^(-3/2) with r2 = |d|^2 + eps^2 given, every step one
+// correctly rounded float operation (the library is compiled without
+// contraction). kFastInv selects inv_sqrt_rn (same cube on its domain) over the
+// general IEEE square root and division.
 template <bool kFastInv>
-__device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, float eps2, float &ax, float &ay,
-                                         float &az) {
-    const float r2 = ((dx * dx + dy * dy) + dz * dz) + eps2;
+__device__ __forceinline__ void add_term_r2(float m, float dx, float dy, float dz, float r2, float &ax, float &ay,
+                                            float &az) {
     const float inv = kFastInv ? inv_sqrt_rn(r2) : 1.0f / sqrtf(r2);
     const float f = m * ((inv * inv) * inv);
     ax += f * dx;
     ay += f * dy;
     az += f * dz;
+}
+
+// The same with r2 = ((dx*dx + dy*dy) + dz*dz) + eps2.
+template <bool kFastInv>
+__device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, float eps2, float &ax, float &ay,
+                                         float &az) {
+    add_term_r2<kFastInv>(m, dx, dy, dz, ((dx * dx + dy * dy) + dz * dz) + eps2, ax, ay, az);
 }
 
 // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous run
@@ -99,68 +108,68 @@ __device__ __forceinline__ void write_out(const WalkOut &o, uint32_t dst, float 
 
 template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
-                                                       const float4 *__restrict__ geom,
-                                                       const uint4 *__restrict__ topo,
-                                                       const DevParams *__restrict__ prm,
-                                                       const uint32_t *__restrict__ perm, uint32_t n,
-                                                       uint32_t max_nodes, float eps2, float theta2, WalkOut out) {
+                                                              const NodeRec *__restrict__ nodes,
+                                                              const DevParams *__restrict__ prm,
+                                                              const uint32_t *__restrict__ perm, uint32_t n,
+                                                              uint32_t max_nodes, float eps2, float theta2,
+                                                              WalkOut out) {
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const bool valid = i < n;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
-    uint32_t vown = 0, pp = 0, pc = 0;
-    uint32_t steps = 0;  // wave-uniform
+    // visits_own = accepted nodes + opened nodes, so no per-step counter
+    uint32_t pp = 0, pc = 0, nopen = 0;
+    uint32_t steps = 0;  // wave-uniform: visits_stepped
     uint32_t c = 0;
     while (c < n_nodes) {
         c = __builtin_amdgcn_readfirstlane(c);
         steps += 1;
-        const float4 g = geom[c];
-        uint4 t = topo[c];  // (escape, begin, count, s^2 bits)
-        t.x = max(t.x, c + 1);  // a well-formed tree has escape > c; never step back
+        const NodeRec nd = nodes[c];  // one scalar load of 32 bytes
+        const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
         const bool active = next == c;
-        const float dx = g.x - xi.x, dy = g.y - xi.y, dz = g.z - xi.z;
+        const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
-        const bool accept = active && (__uint_as_float(t.w) < theta2 * d2);
-        const bool open = active && !accept;
-        vown += active ? 1u : 0u;
-        if (__ballot(accept)) {
-            if (accept) {
-                add_term<kFastInv>(g.w, dx, dy, dz, eps2, ax, ay, az);
-                pc += 1;
-                next = t.x;
-            }
+        const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
+        // Divergent branches below are skipped when no lane takes them.
+        if (active && far) {  // accept: monopole term, then wait for the escape
+            add_term_r2<kFastInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
+            pc += 1;
+            next = esc;
         }
-        if (t.x == c + 1) {  // leaf
-            if (__ballot(open)) {
-                const uint32_t e = t.y + t.z;
-                for (uint32_t j = t.y; j < e; j++) {
+        if (esc == c + 1) {  // leaf
+            if (active && !far) {
+                const uint32_t b = nd.t.y, cnt = nd.t.z;
+                for (uint32_t j = b; j < b + cnt; j++) {
                     const float4 p = xs[j];
-                    if (open) add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                    add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
                 }
-                if (open) {
-                    pp += t.z - ((i - t.y) < t.z ? 1u : 0u);
-                    next = t.x;
-                }
+                pp += cnt - ((i - b) < cnt ? 1u : 0u);
+                nopen += 1;
+                next = esc;
             }
-            c = t.x;
+            c = esc;
         } else {
-            if (open) next = c + 1;
-            c = __ballot(open) ? c + 1 : t.x;
+            if (active && !far) {  // open an internal node: descend
+                nopen += 1;
+                next = c + 1;
+            }
+            // The smallest index any lane wants: c + 1 if some lane descended
+            // (only those lanes now want c + 1), else the escape.
+            c = __builtin_amdgcn_ballot_w64(next == c + 1) ? c + 1 : esc;
         }
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, vown, steps, pp, pc);
+    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
 template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
-                                                          const float4 *__restrict__ geom,
-                                                          const uint4 *__restrict__ topo,
-                                                          const DevParams *__restrict__ prm,
-                                                          const uint32_t *__restrict__ perm, uint32_t n,
-                                                          uint32_t max_nodes, float eps2, float theta2,
-                                                          WalkOut out) {
+                                                                 const NodeRec *__restrict__ nodes,
+                                                                 const DevParams *__restrict__ prm,
+                                                                 const uint32_t *__restrict__ perm, uint32_t n,
+                                                                 uint32_t max_nodes, float eps2, float theta2,
+                                                                 WalkOut out) {
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
@@ -169,24 +178,23 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
     uint32_t vown = 0, pp = 0, pc = 0;
     uint32_t c = 0;
     while (c < n_nodes) {
-        const float4 g = geom[c];
-        uint4 t = topo[c];
-        t.x = max(t.x, c + 1);  // a well-formed tree has escape > c; never step back
-        const float dx = g.x - xi.x, dy = g.y - xi.y, dz = g.z - xi.z;
+        const NodeRec nd = nodes[c];
+        const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
+        const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
         vown += 1;
-        if (__uint_as_float(t.w) < theta2 * d2) {
-            add_term<kFastInv>(g.w, dx, dy, dz, eps2, ax, ay, az);
+        if (__uint_as_float(nd.t.w) < theta2 * d2) {
+            add_term_r2<kFastInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
             pc += 1;
-            c = t.x;
-        } else if (t.x == c + 1) {
-            const uint32_t e = t.y + t.z;
-            for (uint32_t j = t.y; j < e; j++) {
+            c = esc;
+        } else if (esc == c + 1) {
+            const uint32_t b = nd.t.y, cnt = nd.t.z;
+            for (uint32_t j = b; j < b + cnt; j++) {
                 const float4 p = xs[j];
                 add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
             }
-            pp += t.z - ((i - t.y) < t.z ? 1u : 0u);
-            c = t.x;
+            pp += cnt - ((i - b) < cnt ? 1u : 0u);
+            c = esc;
         } else {
             c = c + 1;
         }
@@ -194,16 +202,17 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
     write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
 }
 
-// Self-check of inv_sqrt_rn against the IEEE operations over the float bit
-// patterns [first, first + count).
+// Self-check over the float bit patterns [first, first + count): the cube of
+// inv_sqrt_rn (all the term uses) against the cube of the IEEE operations.
 __global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint64_t count,
                                                            unsigned long long *mismatches, uint32_t *examples) {
     const uint64_t stride = (uint64_t)gridDim.x * 256u;
     for (uint64_t k = (uint64_t)blockIdx.x * 256u + threadIdx.x; k < count; k += stride) {
         const uint32_t bits = first + (uint32_t)k;
         const float x = __uint_as_float(bits);
-        const float ref = 1.0f / sqrtf(x);
-        if (__float_as_uint(inv_sqrt_rn(x)) != __float_as_uint(ref)) {
+        const float r = 1.0f / sqrtf(x), y = inv_sqrt_rn(x);
+        const float ref = (r * r) * r, got = (y * y) * y;
+        if (__float_as_uint(got) != __float_as_uint(ref)) {
             const unsigned long long old = atomicAdd(mismatches, 1ull);
             if (old < 8) examples[old] = bits;
         }
@@ -219,11 +228,11 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
     const uint32_t nb = (uint32_t)ws.max_nodes;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
     if (coherent)
-        k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n, nb,
-                                                             eps2, theta2, out);
+        k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2,
+                                                             theta2, out);
     else
-        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.geom, ws.topo, ws.prm, ws.vals[0], n,
-                                                                nb, eps2, theta2, out);
+        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
+                                                                eps2, theta2, out);
     return hipGetLastError();
 }
 
