@@ -1,12 +1,10 @@
-// Root cube and Morton keys.
+// Root cube of the Morton keys.
 //
 // The orrery performance page ("Where one evaluation goes") puts a Morton
-// sort in front of the tree build; the root cube and key layout are the
-// readings stated in include/orr.h: corner = component-wise minimum, side =
-// largest extent, 21 bits per axis interleaved x-major.
-//
-// Both kernels are HBM-bound streaming passes (12 B of position + 4 B of mass
-// read per particle; 12 B of key + index written).
+// sort in front of the tree build; the root cube is the reading stated in
+// include/orr.h: corner = component-wise minimum, side = largest extent.
+// HBM-bound streaming reduction (12 B of position + 4 B of mass per
+// particle). The final kernel also resets the build's device counters.
 #include "orr_internal.h"
 
 namespace orr {
@@ -93,50 +91,20 @@ __global__ __launch_bounds__(64) void k_cube_final(const float *__restrict__ par
         prm->scale = 2097152.0f / side;  // correctly rounded division
         prm->bad_input = bad;
         prm->n_nodes = 0;
+        for (int p = 0; p < kRadixPasses; p++) prm->sort_ticket[p] = 0;
+        prm->scan_ticket = 0;
+        prm->n_cut = 0;
+        prm->n_top = 0;
     }
-}
-
-// Spread the low 21 bits of v so that bit b lands on bit 3b (mask-and-shift
-// bit interleaving).
-__device__ __forceinline__ uint64_t spread3(uint32_t v) {
-    uint64_t x = v & 0x1fffffu;
-    x = (x | (x << 32)) & 0x001f00000000ffffull;
-    x = (x | (x << 16)) & 0x001f0000ff0000ffull;
-    x = (x | (x << 8)) & 0x100f00f00f00f00full;
-    x = (x | (x << 4)) & 0x10c30c30c30c30c3ull;
-    x = (x | (x << 2)) & 0x1249249249249249ull;
-    return x;
-}
-
-// q = min(trunc((x - lo) * scale), 2^21 - 1); anything not >= 0 (only
-// possible for flagged input) maps to 0.
-__device__ __forceinline__ uint32_t quantise(float x, float lo, float scale) {
-    float t = (x - lo) * scale;
-    if (t >= 2097151.0f) return kQMax;
-    return t >= 0.0f ? (uint32_t)t : 0u;
-}
-
-__global__ __launch_bounds__(256) void k_morton(const float *__restrict__ pos, uint32_t n,
-                                                const DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
-                                                uint32_t *__restrict__ idx) {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-    if (i >= n) return;
-    const float lx = prm->lo[0], ly = prm->lo[1], lz = prm->lo[2], sc = prm->scale;
-    uint32_t qx = quantise(pos[3ull * i], lx, sc);
-    uint32_t qy = quantise(pos[3ull * i + 1], ly, sc);
-    uint32_t qz = quantise(pos[3ull * i + 2], lz, sc);
-    keys[i] = (spread3(qx) << 2) | (spread3(qy) << 1) | spread3(qz);
-    idx[i] = i;
 }
 
 }  // namespace
 
-hipError_t launch_cube_and_keys(const float *pos, const float *mass, const Workspace &ws, hipStream_t s) {
+hipError_t launch_cube(const float *pos, const float *mass, const Workspace &ws, hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
     int blocks = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));
     k_cube_partial<<<blocks, 256, 0, s>>>(pos, mass, n, ws.cube_part);
     k_cube_final<<<1, 64, 0, s>>>(ws.cube_part, blocks, ws.prm);
-    k_morton<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(pos, n, ws.prm, ws.keys[0], ws.vals[0]);
     return hipGetLastError();
 }
 

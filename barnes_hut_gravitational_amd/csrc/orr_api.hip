@@ -40,8 +40,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     const int64_t nb = max_nodes_for(n, leaf_cap);
     const int64_t n_tiles = ceil_div(n, kTile);
-    const int64_t scan_len = std::max<int64_t>((int64_t)kRadixBins * n_tiles, n + 1);
-    const int64_t n_part = ceil_div(scan_len, kTile);
+    const int64_t n_scan_tiles = ceil_div(n + 1, 256);
     char *p = static_cast<char *>(base);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -54,16 +53,19 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     w.cube_part = reinterpret_cast<float *>(take(sizeof(float) * 8 * kCubeBlocks));
     for (int k = 0; k < 2; k++) w.keys[k] = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * n));
     for (int k = 0; k < 2; k++) w.vals[k] = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
-    w.hist = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kRadixBins * n_tiles));
-    w.scan_part = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n_part));
+    w.hist_part = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kSortHistBlocks * kRadixPasses * kRadixBins));
+    w.digit_offs = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kRadixPasses * kRadixBins));
+    w.lb_scan_offset = (int64_t)kRadixPasses * n_tiles * kRadixBins;
+    w.n_lb_words = w.lb_scan_offset + n_scan_tiles;
+    w.lb_words = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * w.n_lb_words));
     w.xs = reinterpret_cast<float4 *>(take(sizeof(float4) * n));
     w.info = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
     w.base = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * (n + 1)));
     w.nodes = reinterpret_cast<NodeRec *>(take(sizeof(NodeRec) * nb));
     w.msum = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
-    w.parent = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
-    w.arrive = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
     w.level = reinterpret_cast<uint8_t *>(take(sizeof(uint8_t) * nb));
+    w.cut_list = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
+    w.top_list = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
     w.n = n;
     w.leaf_cap = leaf_cap;
     w.max_nodes = nb;
@@ -145,14 +147,14 @@ struct PhaseTimer {
     }
 };
 
+// Phase marks: 0 start, 1 after cube and keys, 2 after sort and gather, 3
+// after topology, 4 after moments, 5 after the walk.
 orr_status build_into(const float *pos, const float *mass, const Workspace &ws, hipStream_t s, PhaseTimer &tm) {
     hipError_t e;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_cube_and_keys(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "root cube / keys");
-    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_sort(ws, s)) != hipSuccess) return hip_fail(e, "radix sort");
-    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_gather(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "gather");
+    if ((e = launch_cube(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "root cube");
+    if ((e = launch_keys_and_sort(pos, mass, ws, s, tm.on ? tm.ev[tm.k++] : nullptr)) != hipSuccess)
+        return hip_fail(e, "keys / radix sort");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = launch_build(ws, s)) != hipSuccess) return hip_fail(e, "tree build");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -165,6 +167,7 @@ orr_status read_params(const orr_tree *t, DevParams *out) {
     hipError_t e = hipMemcpyAsync(out, t->ws.prm, sizeof(DevParams), hipMemcpyDeviceToHost, t->stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
     if ((e = hipStreamSynchronize(t->stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (out->bad_input & 2u) return fail(ORR_ERR_HIP, "a device look-back wait gave up; results are invalid");
     return ORR_OK;
 }
 
@@ -272,11 +275,11 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     if ((st = read_params(&t, &prm)) != ORR_OK) return st;
     timings->cube_keys_ms = tm.ms(0, 1);
     timings->sort_ms = tm.ms(1, 2);
-    timings->gather_ms = tm.ms(2, 3);
-    timings->build_ms = tm.ms(3, 4);
-    timings->moments_ms = tm.ms(4, 5);
-    timings->walk_ms = tm.ms(5, 6);
-    timings->total_ms = tm.ms(0, 6);
+    timings->gather_ms = 0.0f;  // fused into the last sort pass
+    timings->build_ms = tm.ms(2, 3);
+    timings->moments_ms = tm.ms(3, 4);
+    timings->walk_ms = tm.ms(4, 5);
+    timings->total_ms = tm.ms(0, 5);
     if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
     return ORR_OK;
     ORR_GUARD_END

@@ -24,19 +24,26 @@ constexpr int kRadixPasses = 8;          // 64 / 8; bit 63 is always zero
 
 constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube reduction
 
+constexpr int kSortHistBlocks = 256;     // blocks of the key + histogram pass
+
 // Device-resident scalars of one build, at the start of the workspace.
 struct DevParams {
     float lo[3];
     float side;
     float scale;          // 2^21 / side
-    uint32_t bad_input;   // non-zero: non-finite position/mass, negative mass or overflowing extent
+    uint32_t bad_input;   // bit 0: non-finite position/mass, negative mass or overflowing extent;
+                          // bit 1: a look-back wait gave up (never expected)
     uint32_t n_nodes;
     uint32_t n_leaves;    // filled by the info kernels only
     uint32_t depth;
     uint32_t max_leaf_count;
-    uint32_t pad[6];
+    uint32_t sort_ticket[kRadixPasses];  // tile tickets of the one-sweep passes
+    uint32_t scan_ticket;                // tile ticket of the node-count scan
+    uint32_t n_cut;                      // entries of the cut-node list
+    uint32_t n_top;                      // entries of the above-the-cut list
+    uint32_t pad[11];
 };
-static_assert(sizeof(DevParams) == 64, "DevParams layout");
+static_assert(sizeof(DevParams) == 128, "DevParams layout");
 
 // One tree node, 32 bytes: g = (com.x, com.y, com.z, M),
 // t = (escape, begin, count, bits of s^2). A wave reads it with one scalar load.
@@ -52,20 +59,23 @@ struct Workspace {
     float *cube_part;      // [kCubeBlocks][8]
     uint64_t *keys[2];     // [n] radix ping-pong; sorted keys end in keys[0]
     uint32_t *vals[2];     // [n] payload: original index; perm ends in vals[0]
-    uint32_t *hist;        // [kRadixBins][n_tiles] digit-major tile counts
-    uint32_t *scan_part;   // tile partials of the device-wide scans
+    uint32_t *hist_part;   // [kSortHistBlocks][kRadixPasses][kRadixBins] digit counts per block
+    uint32_t *digit_offs;  // [kRadixPasses][kRadixBins] first output slot of each digit
+    uint64_t *lb_words;    // look-back words: the sort's passes, then the node-count scan
+    int64_t n_lb_words;
+    int64_t lb_scan_offset;
     float4 *xs;            // [n] sorted (x, y, z, m)
     uint32_t *info;        // [n] first level started | leaf depth << 8
-    uint32_t *base;        // [n + 1] nodes started per particle, scanned in place
+    uint32_t *base;        // [n + 1] nodes started by earlier particles
     NodeRec *nodes;        // [max_nodes]
     float4 *msum;          // [max_nodes] (S, M), unnormalised sums for the parent
-    uint32_t *parent;      // [max_nodes]
-    uint32_t *arrive;      // [max_nodes] children finished, for the bottom-up pass
     uint8_t *level;        // [max_nodes]
+    uint32_t *cut_list;    // [max_nodes] roots of the subtrees finished by one workgroup each
+    uint32_t *top_list;    // [max_nodes] nodes above the cut
     int64_t n;
     int32_t leaf_cap;
     int64_t max_nodes;
-    int64_t n_tiles;
+    int64_t n_tiles;       // sort tiles of kTile keys
 };
 
 inline int64_t max_nodes_for(int64_t n, int32_t leaf_cap) {
@@ -77,24 +87,21 @@ inline int64_t max_nodes_for(int64_t n, int32_t leaf_cap) {
 size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws);
 
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----
-hipError_t launch_cube_and_keys(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
-hipError_t launch_sort(const Workspace &ws, hipStream_t s);
-hipError_t launch_gather(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
+hipError_t launch_cube(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
+// Keys, digit histograms, the 8 sort passes and the gather; after_keys (may be
+// null) is recorded between the key pass and the first sort pass.
+hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Workspace &ws, hipStream_t s,
+                                hipEvent_t after_keys);
 hipError_t launch_build(const Workspace &ws, hipStream_t s);
 hipError_t launch_moments(const Workspace &ws, hipStream_t s);
 hipError_t launch_tree_info(const Workspace &ws, hipStream_t s);
 hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s);
-
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
                                     uint32_t *examples, hipStream_t s);
 bool walk_uses_fast_inv(float eps2);
-
-// Device-wide exclusive scan of len uint32 values, in place allowed
-// (in == out). If total is not null it receives the sum.
-hipError_t launch_exclusive_scan(const uint32_t *in, uint32_t *out, int64_t len, uint32_t *part,
-                                 uint32_t *total, hipStream_t s);
+uint32_t morton_hist_blocks(int64_t n);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

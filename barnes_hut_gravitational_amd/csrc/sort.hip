@@ -1,4 +1,6 @@
-// Device-wide exclusive scan and the stable LSD radix sort of (key, index).
+// Morton keys with their digit histograms, and the stable one-sweep LSD radix
+// sort of (key, index) with the gather into tree order fused into its last
+// pass.
 //
 // The orrery performance page ("Where one evaluation goes", "The largest
 // row") measures the host Morton sort as the largest single cost of an
@@ -6,189 +8,232 @@
 // runs on the GPU. Equal keys keep ascending original index because every
 // pass is stable and the payload starts as the identity.
 //
-// Each of the 8 passes (8-bit digits) is: tile histogram -> device-wide scan
-// of the digit-major histogram -> stable scatter. Tiles are 256 threads x 16
-// keys; within a tile, ranks are computed in 16 rounds of 256 keys, each wave
-// finding its lanes' equal-digit peers with 8 ballots.
+// Pass structure (8 passes of 8-bit digits, bit 63 is always zero):
+//   * k_morton_hist computes every key once and the 8 digit histograms of all
+//     keys; k_digit_offsets turns them into the first output slot of each
+//     digit in each pass.
+//   * k_onesweep, one launch per pass: a tile of 4096 keys takes a ticket (its
+//     position in the output), ranks its keys stably inside each wave (lanes
+//     with the same digit found with 8 ballots), publishes its digit counts,
+//     and adds the counts of the tiles before it by decoupled look-back:
+//     walking back over predecessors' published words until one carries an
+//     inclusive prefix. Tickets are taken in the order blocks start, so every
+//     predecessor is running or done and publishes its counts without waiting
+//     on anyone; each wait is nevertheless bounded and reports an error.
 #include "orr_internal.h"
 
 namespace orr {
 
 namespace {
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
+// Look-back words: high 32 bits = state, low 32 bits = value.
+constexpr uint64_t kStAggregate = 1ull << 32;
+constexpr uint64_t kStInclusive = 2ull << 32;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ uint64_t lb_load(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void lb_store(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Block-wide exclusive scan of one value per thread (256 threads); returns
-// the exclusive prefix and writes the block total to *total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *total) {
-    __shared__ uint32_t wsum[4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t inc = wave_incl_scan(v, lane);
-    if (lane == 63) wsum[w] = inc;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-    for (int k = 0; k < 4; k++) {
-        if (k < w) off += wsum[k];
-        tot += wsum[k];
+// Exclusive prefix over earlier tiles of one value: publish `mine` as an
+// aggregate, walk back to the nearest inclusive word, publish the inclusive
+// value. Returns the exclusive prefix; sets *err on a wait that never ends.
+__device__ __forceinline__ uint32_t look_back(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine,
+                                              uint32_t *err) {
+    if (tile == 0) {
+        lb_store(words, kStInclusive | mine);
+        return 0;
     }
-    __syncthreads();
-    *total = tot;
-    return off + inc - v;
+    lb_store(words + (uint64_t)tile * stride, kStAggregate | mine);
+    uint32_t excl = 0, spins = 0;
+    int64_t t = (int64_t)tile - 1;
+    while (t >= 0) {
+        const uint64_t v = lb_load(words + (uint64_t)t * stride);
+        const uint64_t st = v & ~0xffffffffull;
+        if (st == kStInclusive) {
+            excl += (uint32_t)v;
+            break;
+        }
+        if (st == kStAggregate) {
+            excl += (uint32_t)v;
+            t--;
+            continue;
+        }
+        if (++spins > kSpinLimit) {  // a predecessor never published: give up, flagged
+            atomicOr(err, 2u);
+            break;
+        }
+    }
+    lb_store(words + (uint64_t)tile * stride, kStInclusive | (excl + mine));
+    return excl;
 }
 
-__global__ __launch_bounds__(256) void k_scan_reduce(const uint32_t *__restrict__ in, uint64_t len,
-                                                     uint32_t *__restrict__ part) {
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+// Spread the low 21 bits of v so that bit b lands on bit 3b (mask-and-shift
+// bit interleaving).
+__device__ __forceinline__ uint64_t spread3(uint32_t v) {
+    uint64_t x = v & 0x1fffffu;
+    x = (x | (x << 32)) & 0x001f00000000ffffull;
+    x = (x | (x << 16)) & 0x001f0000ff0000ffull;
+    x = (x | (x << 8)) & 0x100f00f00f00f00full;
+    x = (x | (x << 4)) & 0x10c30c30c30c30c3ull;
+    x = (x | (x << 2)) & 0x1249249249249249ull;
+    return x;
+}
+
+// q = min(trunc((x - lo) * scale), 2^21 - 1); anything not >= 0 (only
+// possible for flagged input) maps to 0.
+__device__ __forceinline__ uint32_t quantise(float x, float lo, float scale) {
+    const float t = (x - lo) * scale;
+    if (t >= 2097151.0f) return kQMax;
+    return t >= 0.0f ? (uint32_t)t : 0u;
+}
+
+// Keys and the identity payload; each block's 8 digit histograms to
+// part[block][pass][digit]; zeroes the look-back words of the build.
+__global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ pos, uint32_t n,
+                                                     const DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
+                                                     uint32_t *__restrict__ idx, uint32_t *__restrict__ part,
+                                                     uint64_t *__restrict__ lb_words, uint64_t n_lb_words) {
+    __shared__ uint32_t h[kRadixPasses * kRadixBins];
+    for (int k = threadIdx.x; k < kRadixPasses * kRadixBins; k += 256) h[k] = 0;
+    __syncthreads();
+    const float lx = prm->lo[0], ly = prm->lo[1], lz = prm->lo[2], sc = prm->scale;
+    const uint32_t stride = gridDim.x * 256u;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += stride) {
+        const uint32_t qx = quantise(pos[3ull * i], lx, sc);
+        const uint32_t qy = quantise(pos[3ull * i + 1], ly, sc);
+        const uint32_t qz = quantise(pos[3ull * i + 2], lz, sc);
+        const uint64_t key = (spread3(qx) << 2) | (spread3(qy) << 1) | spread3(qz);
+        keys[i] = key;
+        idx[i] = i;
+        for (int p = 0; p < kRadixPasses; p++)
+            atomicAdd(&h[p * kRadixBins + ((uint32_t)(key >> (p * kRadixBits)) & (kRadixBins - 1))], 1u);
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < kRadixPasses * kRadixBins; k += 256)
+        part[(uint64_t)blockIdx.x * kRadixPasses * kRadixBins + k] = h[k];
+    for (uint64_t w = (uint64_t)blockIdx.x * 256u + threadIdx.x; w < n_lb_words; w += stride) lb_words[w] = 0ull;
+}
+
+// Block p, thread d: first output slot of digit d in pass p.
+__global__ __launch_bounds__(256) void k_digit_offsets(const uint32_t *__restrict__ part, uint32_t nparts,
+                                                       uint32_t *__restrict__ offs) {
+    const int p = blockIdx.x, d = threadIdx.x;
     uint32_t s = 0;
-    for (int r = 0; r < kTileItems; r++) {
-        uint64_t e = base + (uint64_t)r * kTileThreads + threadIdx.x;
-        if (e < len) s += in[e];
-    }
-    uint32_t tot;
-    block_excl_scan(s, &tot);
-    if (threadIdx.x == 0) part[blockIdx.x] = tot;
-}
-
-// One block: exclusive scan of the tile partials in place; total -> *total.
-__global__ __launch_bounds__(256) void k_scan_partials(uint32_t *__restrict__ part, uint32_t nparts,
-                                                       uint32_t *__restrict__ total) {
-    uint32_t carry = 0;
-    for (uint32_t b0 = 0; b0 < nparts; b0 += 256) {
-        uint32_t i = b0 + threadIdx.x;
-        uint32_t v = i < nparts ? part[i] : 0u;
-        uint32_t tot;
-        uint32_t ex = block_excl_scan(v, &tot);
-        if (i < nparts) part[i] = carry + ex;
-        carry += tot;
-    }
-    if (threadIdx.x == 0 && total) *total = carry;
-}
-
-// Each thread owns 16 consecutive items of the tile.
-__global__ __launch_bounds__(256) void k_scan_down(const uint32_t *in, uint32_t *out, uint64_t len,
-                                                   const uint32_t *__restrict__ part) {
-    const uint64_t base = (uint64_t)blockIdx.x * kTile + (uint64_t)threadIdx.x * kTileItems;
-    uint32_t v[kTileItems];
-    uint32_t s = 0;
-    for (int k = 0; k < kTileItems; k++) {
-        v[k] = (base + k < len) ? in[base + k] : 0u;
-        s += v[k];
-    }
-    uint32_t tot;
-    uint32_t run = part[blockIdx.x] + block_excl_scan(s, &tot);
-    for (int k = 0; k < kTileItems; k++) {
-        if (base + k < len) out[base + k] = run;
-        run += v[k];
-    }
-}
-
-// Digit histogram of one tile, digit-major: hist[d * n_tiles + tile].
-__global__ __launch_bounds__(256) void k_radix_hist(const uint64_t *__restrict__ keys, uint32_t n, int shift,
-                                                    uint32_t *__restrict__ hist, uint32_t n_tiles) {
-    __shared__ uint32_t h[4][kRadixBins];
-    const int w = threadIdx.x >> 6;
-    for (int k = threadIdx.x; k < 4 * kRadixBins; k += 256) (&h[0][0])[k] = 0;
+    for (uint32_t b = 0; b < nparts; b++) s += part[(uint64_t)b * kRadixPasses * kRadixBins + p * kRadixBins + d];
+    __shared__ uint32_t v[kRadixBins];
+    v[d] = s;
     __syncthreads();
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
-    for (int r = 0; r < kTileItems; r++) {
-        uint64_t e = base + (uint64_t)r * kTileThreads + threadIdx.x;
-        if (e < n) atomicAdd(&h[w][(uint32_t)(keys[e] >> shift) & (kRadixBins - 1)], 1u);
+    if (d == 0) {
+        uint32_t run = 0;
+        for (int k = 0; k < kRadixBins; k++) {
+            const uint32_t c = v[k];
+            v[k] = run;
+            run += c;
+        }
     }
     __syncthreads();
-    const int d = threadIdx.x;
-    hist[(uint64_t)d * n_tiles + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+    offs[p * kRadixBins + d] = v[d];
 }
 
-// Stable scatter of one tile. offs[d * n_tiles + tile] = first output slot of
-// this tile's keys with digit d (the scanned histogram).
-__global__ __launch_bounds__(256) void k_radix_scatter(const uint64_t *__restrict__ keys_in,
-                                                       const uint32_t *__restrict__ vals_in, uint32_t n,
-                                                       int shift, const uint32_t *__restrict__ offs,
-                                                       uint32_t n_tiles, uint64_t *__restrict__ keys_out,
-                                                       uint32_t *__restrict__ vals_out) {
-    __shared__ uint32_t s_base[kRadixBins];
-    __shared__ uint32_t s_wc[4][kRadixBins];
+// One pass over a 4096-key tile. Wave w owns elements [4096 t + 1024 w,
+// + 1024), lane l of round r element 1024 w + 64 r + l, so (w, r, l) order
+// is input order.
+template <bool kGather>
+__global__ __launch_bounds__(256) void k_onesweep(const uint64_t *__restrict__ keys_in,
+                                                  const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
+                                                  const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
+                                                  DevParams *prm, uint64_t *__restrict__ keys_out,
+                                                  uint32_t *__restrict__ vals_out, const float *__restrict__ pos,
+                                                  const float *__restrict__ mass, float4 *__restrict__ xs) {
+    __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_cnt[4][kRadixBins];  // running, then total, count per wave and digit
+    __shared__ uint32_t s_base[4][kRadixBins];  // output slot of wave w's first digit-d element
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    s_base[threadIdx.x] = offs[(uint64_t)threadIdx.x * n_tiles + blockIdx.x];
-    for (int k = threadIdx.x; k < 4 * kRadixBins; k += 256) (&s_wc[0][0])[k] = 0;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int shift = pass * kRadixBits;
+    for (int k = threadIdx.x; k < 4 * kRadixBins; k += 256) (&s_cnt[0][0])[k] = 0;
+    if (threadIdx.x == 0) s_tile = atomicAdd(&prm->sort_ticket[pass], 1u);
     __syncthreads();
-    const uint64_t base = (uint64_t)blockIdx.x * kTile;
+    const uint32_t tile = s_tile;
+    const uint64_t base = (uint64_t)tile * kTile + (uint64_t)w * (kTile / 4);
+
+    uint64_t key[kTileItems];
+    uint32_t val[kTileItems], rank[kTileItems];
     for (int r = 0; r < kTileItems; r++) {
-        const uint64_t e = base + (uint64_t)r * kTileThreads + threadIdx.x;
-        const bool valid = e < n;
-        uint64_t key = valid ? keys_in[e] : 0ull;
-        uint32_t val = valid ? vals_in[e] : 0u;
-        uint32_t d = (uint32_t)(key >> shift) & (kRadixBins - 1);
-        uint64_t peers = __ballot(valid);
+        const uint64_t e = base + (uint64_t)r * 64 + lane;
+        key[r] = e < n ? keys_in[e] : 0ull;
+        val[r] = e < n ? vals_in[e] : 0u;
+    }
+    for (int r = 0; r < kTileItems; r++) {
+        const bool valid = base + (uint64_t)r * 64 + lane < n;
+        const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
+        uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
         for (int b = 0; b < kRadixBits; b++) {
-            bool bit = (d >> b) & 1u;
-            uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
+            const uint64_t m = __builtin_amdgcn_ballot_w64((d >> b) & 1u);
+            peers &= ((d >> b) & 1u) ? m : ~m;
         }
-        const uint32_t rank = __popcll(peers & lt_mask);
-        const bool leader = valid && ((peers & lt_mask) == 0ull);
-        if (leader) s_wc[w][d] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            uint32_t pos = s_base[d] + rank;
-            for (int k = 0; k < w; k++) pos += s_wc[k][d];
-            keys_out[pos] = key;
-            vals_out[pos] = val;
-        }
-        __syncthreads();
-        {
-            const int dd = threadIdx.x;
-            s_base[dd] += s_wc[0][dd] + s_wc[1][dd] + s_wc[2][dd] + s_wc[3][dd];
-            s_wc[0][dd] = s_wc[1][dd] = s_wc[2][dd] = s_wc[3][dd] = 0;
-        }
-        __syncthreads();
+        const uint32_t before = s_cnt[w][d];  // wave-private: no barrier, LDS is in order per wave
+        rank[r] = before + __popcll(peers & lt_mask);
+        if (valid && (peers & lt_mask) == 0ull) s_cnt[w][d] = before + __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
     }
-}
-
-// Particles into tree order: xs[k] = (pos[perm[k]], mass[perm[k]]).
-__global__ __launch_bounds__(256) void k_gather(const float *__restrict__ pos, const float *__restrict__ mass,
-                                                const uint32_t *__restrict__ perm, uint32_t n,
-                                                float4 *__restrict__ xs) {
-    const uint32_t k = blockIdx.x * 256u + threadIdx.x;
-    if (k >= n) return;
-    const uint64_t j = perm[k];
-    xs[k] = make_float4(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], mass[j]);
+    __syncthreads();
+    {
+        const int d = threadIdx.x;
+        uint32_t tot = 0, wb[4];
+        for (int k = 0; k < 4; k++) {
+            wb[k] = tot;
+            tot += s_cnt[k][d];
+        }
+        const uint32_t excl = look_back(lb_words + d, tile, kRadixBins, tot, &prm->bad_input);
+        const uint32_t first = digit_offs[pass * kRadixBins + d] + excl;
+        for (int k = 0; k < 4; k++) s_base[k][d] = first + wb[k];
+    }
+    __syncthreads();
+    for (int r = 0; r < kTileItems; r++) {
+        const uint64_t e = base + (uint64_t)r * 64 + lane;
+        if (e < n) {
+            const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
+            const uint32_t o = s_base[w][d] + rank[r];
+            keys_out[o] = key[r];
+            vals_out[o] = val[r];
+            if (kGather) {
+                const uint64_t j = val[r];
+                xs[o] = make_float4(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], mass[j]);
+            }
+        }
+    }
 }
 
 }  // namespace
 
-hipError_t launch_gather(const float *pos, const float *mass, const Workspace &ws, hipStream_t s) {
-    k_gather<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(pos, mass, ws.vals[0], (uint32_t)ws.n, ws.xs);
-    return hipGetLastError();
-}
+uint32_t morton_hist_blocks(int64_t n) { return (uint32_t)std::min<int64_t>(kSortHistBlocks, ceil_div(n, 256)); }
 
-hipError_t launch_exclusive_scan(const uint32_t *in, uint32_t *out, int64_t len, uint32_t *part,
-                                 uint32_t *total, hipStream_t s) {
-    const uint32_t nt = (uint32_t)ceil_div(len, kTile);
-    k_scan_reduce<<<nt, 256, 0, s>>>(in, (uint64_t)len, part);
-    k_scan_partials<<<1, 256, 0, s>>>(part, nt, total);
-    k_scan_down<<<nt, 256, 0, s>>>(in, out, (uint64_t)len, part);
-    return hipGetLastError();
-}
-
-hipError_t launch_sort(const Workspace &ws, hipStream_t s) {
+hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Workspace &ws, hipStream_t s,
+                                hipEvent_t after_keys) {
     const uint32_t n = (uint32_t)ws.n;
     const uint32_t nt = (uint32_t)ws.n_tiles;
+    const uint32_t hb = morton_hist_blocks(ws.n);
+    k_morton_hist<<<hb, 256, 0, s>>>(pos, n, ws.prm, ws.keys[0], ws.vals[0], ws.hist_part, ws.lb_words,
+                                     (uint64_t)ws.n_lb_words);
+    k_digit_offsets<<<kRadixPasses, kRadixBins, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
+    if (after_keys) {
+        hipError_t e = hipEventRecord(after_keys, s);
+        if (e != hipSuccess) return e;
+    }
     for (int pass = 0; pass < kRadixPasses; pass++) {
         const int src = pass & 1, dst = src ^ 1;
-        const int shift = pass * kRadixBits;
-        k_radix_hist<<<nt, 256, 0, s>>>(ws.keys[src], n, shift, ws.hist, nt);
-        hipError_t e = launch_exclusive_scan(ws.hist, ws.hist, (int64_t)kRadixBins * nt, ws.scan_part, nullptr, s);
-        if (e != hipSuccess) return e;
-        k_radix_scatter<<<nt, 256, 0, s>>>(ws.keys[src], ws.vals[src], n, shift, ws.hist, nt, ws.keys[dst],
-                                           ws.vals[dst]);
+        uint64_t *words = ws.lb_words + (uint64_t)pass * nt * kRadixBins;
+        if (pass + 1 < kRadixPasses)
+            k_onesweep<false><<<nt, 256, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
+                                                 ws.keys[dst], ws.vals[dst], nullptr, nullptr, nullptr);
+        else
+            k_onesweep<true><<<nt, 256, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
+                                                ws.keys[dst], ws.vals[dst], pos, mass, ws.xs);
     }
     return hipGetLastError();
 }

@@ -42,11 +42,13 @@ constexpr uint32_t kWalkBlock = ORR_WALK_BLOCK;  // threads per block (multiple 
 // estimate refined by one Newton step y += y * (1 - s*y) in fma, which is
 // correctly rounded for every s = sqrt(x) of this domain. x = +inf (only from
 // coordinate differences beyond float range) is clamped to FLT_MAX: its
-// inverse cube then underflows to 0, as 1/inf cubed does. Equality of the cube
-// with the IEEE operations' cube for every float in [2^-96, +inf] is checked
-// by orr_selftest_inv_sqrt.
+// inverse cube then underflows to 0, as 1/inf cubed does; kClamp = false
+// leaves the clamp out where no r2 can overflow. Equality of the cube with the
+// IEEE operations' cube for every float in [2^-96, +inf] is checked by
+// orr_selftest_inv_sqrt.
+template <bool kClamp = true>
 __device__ __forceinline__ float inv_sqrt_rn(float x) {
-    x = fminf(x, 3.40282347e38f);
+    if (kClamp) x = fminf(x, 3.40282347e38f);
     float s = __builtin_amdgcn_sqrtf(x);
     const float sm = __uint_as_float(__float_as_uint(s) - 1u);
     const float sp = __uint_as_float(__float_as_uint(s) + 1u);
@@ -61,12 +63,15 @@ __device__ __forceinline__ float inv_sqrt_rn(float x) {
 
 // a += m * d * r2^(-3/2) with r2 = |d|^2 + eps^2 given, every step one
 // correctly rounded float operation (the library is compiled without
-// contraction). kFastInv selects inv_sqrt_rn (same cube on its domain) over the
-// general IEEE square root and division.
-template <bool kFastInv>
+// contraction). kInv: 0 = the general IEEE square root and division;
+// 1 = inv_sqrt_rn (same cube on its domain); 2 = inv_sqrt_rn without the
+// overflow clamp.
+enum { kInvIeee = 0, kInvFast = 1, kInvFastNoClamp = 2 };
+
+template <int kInv>
 __device__ __forceinline__ void add_term_r2(float m, float dx, float dy, float dz, float r2, float &ax, float &ay,
                                             float &az) {
-    const float inv = kFastInv ? inv_sqrt_rn(r2) : 1.0f / sqrtf(r2);
+    const float inv = kInv == kInvIeee ? 1.0f / sqrtf(r2) : inv_sqrt_rn<kInv == kInvFast>(r2);
     const float f = m * ((inv * inv) * inv);
     ax += f * dx;
     ay += f * dy;
@@ -74,10 +79,10 @@ __device__ __forceinline__ void add_term_r2(float m, float dx, float dy, float d
 }
 
 // The same with r2 = ((dx*dx + dy*dy) + dz*dz) + eps2.
-template <bool kFastInv>
+template <int kInv>
 __device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, float eps2, float &ax, float &ay,
                                          float &az) {
-    add_term_r2<kFastInv>(m, dx, dy, dz, ((dx * dx + dy * dy) + dz * dz) + eps2, ax, ay, az);
+    add_term_r2<kInv>(m, dx, dy, dz, ((dx * dx + dy * dy) + dz * dz) + eps2, ax, ay, az);
 }
 
 // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous run
@@ -106,16 +111,18 @@ __device__ __forceinline__ void write_out(const WalkOut &o, uint32_t dst, float 
     if (o.n_pc) o.n_pc[dst] = pc;
 }
 
-template <bool kFastInv>
-__global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
-                                                              const NodeRec *__restrict__ nodes,
-                                                              const DevParams *__restrict__ prm,
-                                                              const uint32_t *__restrict__ perm, uint32_t n,
-                                                              uint32_t max_nodes, float eps2, float theta2,
-                                                              WalkOut out) {
-    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
+// r2 <= 3 (side (1 + 2^-20))^2 + eps2 for every pair inside the root cube,
+// coms included; below this bound no r2 can overflow float.
+__device__ __forceinline__ bool r2_cannot_overflow(const DevParams *prm, float eps2) {
+    const double s = (double)prm->side * (1.0 + 0x1p-20);
+    return 3.0 * s * s + (double)eps2 < 1e38;
+}
+
+template <int kInv>
+__device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
+                                              const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
+                                              uint32_t n_nodes, float eps2, float theta2, const WalkOut &out) {
     const bool valid = i < n;
-    const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
         const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
         // Divergent branches below are skipped when no lane takes them.
         if (active && far) {  // accept: monopole term, then wait for the escape
-            add_term_r2<kFastInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
+            add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
             pc += 1;
             next = esc;
         }
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
                 for (uint32_t j = b; j < b + cnt; j++) {
                     const float4 p = xs[j];
-                    add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                    add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
                 }
                 pp += cnt - ((i - b) < cnt ? 1u : 0u);
                 nopen += 1;
@@ -164,15 +171,26 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
 }
 
 template <bool kFastInv>
-__global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
-                                                                 const NodeRec *__restrict__ nodes,
-                                                                 const DevParams *__restrict__ prm,
-                                                                 const uint32_t *__restrict__ perm, uint32_t n,
-                                                                 uint32_t max_nodes, float eps2, float theta2,
-                                                                 WalkOut out) {
+__global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
+                                                              const NodeRec *__restrict__ nodes,
+                                                              const DevParams *__restrict__ prm,
+                                                              const uint32_t *__restrict__ perm, uint32_t n,
+                                                              uint32_t max_nodes, float eps2, float theta2,
+                                                              WalkOut out) {
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
-    if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
+    if (!kFastInv)
+        walk_coherent<kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+    else if (r2_cannot_overflow(prm, eps2))  // uniform
+        walk_coherent<kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+    else
+        walk_coherent<kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+}
+
+template <int kInv>
+__device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
+                                                 const uint32_t *__restrict__ perm, uint32_t i, uint32_t n_nodes,
+                                                 float eps2, float theta2, const WalkOut &out) {
     const float4 xi = xs[i];
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
     uint32_t vown = 0, pp = 0, pc = 0;
@@ -184,14 +202,14 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
         const float d2 = (dx * dx + dy * dy) + dz * dz;
         vown += 1;
         if (__uint_as_float(nd.t.w) < theta2 * d2) {
-            add_term_r2<kFastInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
+            add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
             pc += 1;
             c = esc;
         } else if (esc == c + 1) {
             const uint32_t b = nd.t.y, cnt = nd.t.z;
             for (uint32_t j = b; j < b + cnt; j++) {
                 const float4 p = xs[j];
-                add_term<kFastInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
             }
             pp += cnt - ((i - b) < cnt ? 1u : 0u);
             c = esc;
@@ -200,6 +218,24 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
         }
     }
     write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
+}
+
+template <bool kFastInv>
+__global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
+                                                                 const NodeRec *__restrict__ nodes,
+                                                                 const DevParams *__restrict__ prm,
+                                                                 const uint32_t *__restrict__ perm, uint32_t n,
+                                                                 uint32_t max_nodes, float eps2, float theta2,
+                                                                 WalkOut out) {
+    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
+    if (!kFastInv)
+        walk_independent<kInvIeee>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
+    else if (r2_cannot_overflow(prm, eps2))
+        walk_independent<kInvFastNoClamp>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
+    else
+        walk_independent<kInvFast>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
 }
 
 // Self-check over the float bit patterns [first, first + count): the cube of
