@@ -92,7 +92,6 @@ __global__ __launch_bounds__(64) void k_cube_final(const float *__restrict__ par
         prm->bad_input = bad;
         prm->n_nodes = 0;
         for (int p = 0; p < kRadixPasses; p++) prm->sort_ticket[p] = 0;
-        prm->scan_ticket = 0;
         prm->n_cut = 0;
         prm->n_top = 0;
     }

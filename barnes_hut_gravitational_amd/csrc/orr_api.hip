@@ -55,17 +55,19 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     for (int k = 0; k < 2; k++) w.vals[k] = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
     w.hist_part = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kSortHistBlocks * kRadixPasses * kRadixBins));
     w.digit_offs = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kRadixPasses * kRadixBins));
-    w.lb_scan_offset = (int64_t)kRadixPasses * n_tiles * kRadixBins;
-    w.n_lb_words = w.lb_scan_offset + n_scan_tiles;
+    w.n_lb_words = (int64_t)kRadixPasses * n_tiles * kRadixBins;
     w.lb_words = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * w.n_lb_words));
     w.xs = reinterpret_cast<float4 *>(take(sizeof(float4) * n));
     w.info = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
     w.base = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * (n + 1)));
+    w.tile_sum = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * (n_scan_tiles + 1)));
     w.nodes = reinterpret_cast<NodeRec *>(take(sizeof(NodeRec) * nb));
     w.msum = reinterpret_cast<float4 *>(take(sizeof(float4) * nb));
     w.level = reinterpret_cast<uint8_t *>(take(sizeof(uint8_t) * nb));
     w.cut_list = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
-    w.top_list = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * nb));
+    w.max_top = max_top_for(n);
+    w.top_list = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * w.max_top));
+    w.kids = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * 9 * w.max_top));
     w.n = n;
     w.leaf_cap = leaf_cap;
     w.max_nodes = nb;

@@ -14,9 +14,12 @@ constexpr int kMaxLevel = 21;            // 21 bits per axis, 63-bit keys
 constexpr uint32_t kQMax = 2097151u;     // 2^21 - 1
 constexpr uint32_t kNoParent = 0xffffffffu;
 
-// Sort and scan tiles: 256 threads x 16 items.
+// Sort tiles: 256 threads x kTileItems keys.
+#ifndef ORR_SORT_ITEMS
+#define ORR_SORT_ITEMS 16
+#endif
 constexpr int kTileThreads = 256;
-constexpr int kTileItems = 16;
+constexpr int kTileItems = ORR_SORT_ITEMS;
 constexpr int kTile = kTileThreads * kTileItems;
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
@@ -25,6 +28,7 @@ constexpr int kRadixPasses = 8;          // 64 / 8; bit 63 is always zero
 constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube reduction
 
 constexpr int kSortHistBlocks = 256;     // blocks of the key + histogram pass
+constexpr uint32_t kCutParticles = 4096; // subtrees of at most this many particles get one workgroup
 
 // Device-resident scalars of one build, at the start of the workspace.
 struct DevParams {
@@ -38,10 +42,9 @@ struct DevParams {
     uint32_t depth;
     uint32_t max_leaf_count;
     uint32_t sort_ticket[kRadixPasses];  // tile tickets of the one-sweep passes
-    uint32_t scan_ticket;                // tile ticket of the node-count scan
     uint32_t n_cut;                      // entries of the cut-node list
     uint32_t n_top;                      // entries of the above-the-cut list
-    uint32_t pad[11];
+    uint32_t pad[12];
 };
 static_assert(sizeof(DevParams) == 128, "DevParams layout");
 
@@ -61,17 +64,19 @@ struct Workspace {
     uint32_t *vals[2];     // [n] payload: original index; perm ends in vals[0]
     uint32_t *hist_part;   // [kSortHistBlocks][kRadixPasses][kRadixBins] digit counts per block
     uint32_t *digit_offs;  // [kRadixPasses][kRadixBins] first output slot of each digit
-    uint64_t *lb_words;    // look-back words: the sort's passes, then the node-count scan
+    uint64_t *lb_words;    // look-back words of the sort's passes
     int64_t n_lb_words;
-    int64_t lb_scan_offset;
     float4 *xs;            // [n] sorted (x, y, z, m)
     uint32_t *info;        // [n] first level started | leaf depth << 8
-    uint32_t *base;        // [n + 1] nodes started by earlier particles
+    uint32_t *base;        // [n + 1] nodes started by earlier particles of the same 256-particle tile
+    uint32_t *tile_sum;    // [tiles + 1] nodes started per 256-particle tile, then their exclusive scan
     NodeRec *nodes;        // [max_nodes]
     float4 *msum;          // [max_nodes] (S, M), unnormalised sums for the parent
     uint8_t *level;        // [max_nodes]
     uint32_t *cut_list;    // [max_nodes] roots of the subtrees finished by one workgroup each
-    uint32_t *top_list;    // [max_nodes] nodes above the cut
+    uint32_t *top_list;    // [max_top] nodes above the cut
+    uint32_t *kids;        // [9 max_top] child count and children of each node above the cut
+    int64_t max_top;
     int64_t n;
     int32_t leaf_cap;
     int64_t max_nodes;
@@ -81,6 +86,9 @@ struct Workspace {
 inline int64_t max_nodes_for(int64_t n, int32_t leaf_cap) {
     return n + 21 * (n / (leaf_cap + 1)) + 1;
 }
+
+// Nodes holding more than kCutParticles are disjoint on each of the 22 levels.
+inline int64_t max_top_for(int64_t n) { return 22 * (n / (kCutParticles + 1)) + 1; }
 
 // Lays the workspace out from `base` (which may be null for sizing) and
 // returns the bytes it needs.

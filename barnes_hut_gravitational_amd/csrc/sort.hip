@@ -12,7 +12,7 @@
 //   * k_morton_hist computes every key once and the 8 digit histograms of all
 //     keys; k_digit_offsets turns them into the first output slot of each
 //     digit in each pass.
-//   * k_onesweep, one launch per pass: a tile of 4096 keys takes a ticket (its
+//   * k_onesweep, one launch per pass: a tile of 2048 keys takes a ticket (its
 //     position in the output), ranks its keys stably inside each wave (lanes
 //     with the same digit found with 8 ballots), publishes its digit counts,
 //     and adds the counts of the tiles before it by decoupled look-back:
@@ -118,30 +118,40 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
     for (uint64_t w = (uint64_t)blockIdx.x * 256u + threadIdx.x; w < n_lb_words; w += stride) lb_words[w] = 0ull;
 }
 
-// Block p, thread d: first output slot of digit d in pass p.
-__global__ __launch_bounds__(256) void k_digit_offsets(const uint32_t *__restrict__ part, uint32_t nparts,
-                                                       uint32_t *__restrict__ offs) {
-    const int p = blockIdx.x, d = threadIdx.x;
+// Block p (1024 threads): first output slot of each digit in pass p. Thread
+// (q, d) sums the digit-d counts of every fourth histogram block from q; the
+// four partial sums are added, then scanned over digits.
+__global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restrict__ part, uint32_t nparts,
+                                                        uint32_t *__restrict__ offs) {
+    const int p = blockIdx.x, d = threadIdx.x & (kRadixBins - 1), q = threadIdx.x >> kRadixBits;
     uint32_t s = 0;
-    for (uint32_t b = 0; b < nparts; b++) s += part[(uint64_t)b * kRadixPasses * kRadixBins + p * kRadixBins + d];
-    __shared__ uint32_t v[kRadixBins];
-    v[d] = s;
+    for (uint32_t b = q; b < nparts; b += 4) s += part[(uint64_t)b * kRadixPasses * kRadixBins + p * kRadixBins + d];
+    __shared__ uint32_t sum[4][kRadixBins];
+    __shared__ uint32_t wsum[4];
+    sum[q][d] = s;
     __syncthreads();
-    if (d == 0) {
-        uint32_t run = 0;
-        for (int k = 0; k < kRadixBins; k++) {
-            const uint32_t c = v[k];
-            v[k] = run;
-            run += c;
+    const int lane = d & 63, w = d >> 6;
+    uint32_t v = 0, inc = 0;
+    if (q == 0) {
+        v = sum[0][d] + sum[1][d] + sum[2][d] + sum[3][d];
+        inc = v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += t;
         }
+        if (lane == 63) wsum[w] = inc;
     }
-    __syncthreads();
-    offs[p * kRadixBins + d] = v[d];
+    __syncthreads();  // every thread of the block reaches both barriers
+    if (q == 0) {
+        uint32_t off = 0;
+        for (int k = 0; k < w; k++) off += wsum[k];
+        offs[p * kRadixBins + d] = off + inc - v;
+    }
 }
 
-// One pass over a 4096-key tile. Wave w owns elements [4096 t + 1024 w,
-// + 1024), lane l of round r element 1024 w + 64 r + l, so (w, r, l) order
-// is input order.
+// One pass over a tile of kTile keys. Wave w owns elements [kTile t +
+// w kTile/4, + kTile/4), lane l of round r element w kTile/4 + 64 r + l, so
+// (w, r, l) order is input order.
 template <bool kGather>
 __global__ __launch_bounds__(256) void k_onesweep(const uint64_t *__restrict__ keys_in,
                                                   const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
@@ -220,7 +230,7 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
     const uint32_t hb = morton_hist_blocks(ws.n);
     k_morton_hist<<<hb, 256, 0, s>>>(pos, n, ws.prm, ws.keys[0], ws.vals[0], ws.hist_part, ws.lb_words,
                                      (uint64_t)ws.n_lb_words);
-    k_digit_offsets<<<kRadixPasses, kRadixBins, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
+    k_digit_offsets<<<kRadixPasses, 1024, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
     if (after_keys) {
         hipError_t e = hipEventRecord(after_keys, s);
         if (e != hipSuccess) return e;

@@ -17,8 +17,9 @@
 // Particle i therefore starts the nodes of levels first(i)..D(i). Depth-first
 // preorder is the order of (begin, level), so the node index of (i, l) is
 // (nodes started by particles before i) + (l - first(i)), an exclusive scan
-// (single pass, decoupled look-back). A node ending at particle e has
-// escape = the first node starting at e or later, which is the scan value at e.
+// (tile prefix + prefix inside the tile). A node ending at particle e has
+// escape = the first node starting at e or later, which is the scan value at
+// e. Each node's end is then searched in parallel, one thread per node.
 //
 // Moments bottom-up without device-wide synchronisation: the tree is cut into
 // subtrees of at most kCutParticles particles ("cut" nodes: the largest nodes
@@ -40,26 +41,24 @@ __device__ __forceinline__ int lcp_digits(uint64_t a, uint64_t b) {
     return 20 - h / 3;
 }
 
-constexpr uint64_t kStAggregate = 1ull << 32;
-constexpr uint64_t kStInclusive = 2ull << 32;
-constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr uint32_t kCutParticles = 4096;
+constexpr int kScanTile = 256;
 
-// One block of 256 particles (the block's range comes from a ticket, so that
-// the tiles before it are running or done). Writes info[i] = first(i) |
-// D(i) << 8 and base[i] = nodes started by particles before i, for
-// i in [0, n]; base[n] = n_nodes.
-__global__ __launch_bounds__(256) void k_tree_count_scan(const uint64_t *__restrict__ keys, uint32_t n,
-                                                         uint32_t cap, uint32_t *__restrict__ info,
-                                                         uint32_t *__restrict__ base, uint64_t *lb_words,
-                                                         DevParams *prm) {
+// Nodes started by particles before x: tile prefix + prefix inside the tile.
+__device__ __forceinline__ uint32_t base_at(const uint32_t *__restrict__ tile_pre, const uint32_t *__restrict__ loc,
+                                            uint32_t x) {
+    return tile_pre[x / kScanTile] + loc[x];
+}
+
+// One block of 256 particles i in [256 b, 256 b + 256), i <= n. Writes
+// info[i] = first(i) | D(i) << 8, loc[i] = nodes started by the block's
+// particles before i, and tile_sum[b] = nodes started by the block.
+__global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__ keys, uint32_t n, uint32_t cap,
+                                                    uint32_t *__restrict__ info, uint32_t *__restrict__ loc,
+                                                    uint32_t *__restrict__ tile_sum) {
     __shared__ uint64_t sk[256 + 2 * 256];
     __shared__ signed char sw[256 + 256];
-    __shared__ uint32_t s_tile, s_wsum[4], s_excl;
-    if (threadIdx.x == 0) s_tile = atomicAdd(&prm->scan_ticket, 1u);
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const int64_t B = (int64_t)tile * 256;
+    __shared__ uint32_t s_wsum[4];
+    const int64_t B = (int64_t)blockIdx.x * 256;
     const int64_t wbeg = B - (int64_t)cap;
     const int wlen = 256 + 2 * (int)cap;
     for (int t = threadIdx.x; t < wlen; t += 256) {
@@ -84,7 +83,6 @@ __global__ __launch_bounds__(256) void k_tree_count_scan(const uint64_t *__restr
         info[i] = (uint32_t)first | ((uint32_t)D << 8);
         nst = D >= first ? (uint32_t)(D - first + 1) : 0u;
     }
-    // block exclusive scan of nst, then the tile prefix by look-back
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t inc = nst;
     for (int o = 1; o < 64; o <<= 1) {
@@ -98,38 +96,36 @@ __global__ __launch_bounds__(256) void k_tree_count_scan(const uint64_t *__restr
         if (k < w) woff += s_wsum[k];
         tot += s_wsum[k];
     }
-    if (threadIdx.x == 0) {
-        uint32_t excl = 0;
-        if (tile == 0) {
-            __hip_atomic_store(lb_words, kStInclusive | tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            __hip_atomic_store(lb_words + tile, kStAggregate | tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            uint32_t spins = 0;
-            for (int64_t t = (int64_t)tile - 1; t >= 0;) {
-                const uint64_t v = __hip_atomic_load(lb_words + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t st = v & ~0xffffffffull;
-                if (st == kStInclusive) {
-                    excl += (uint32_t)v;
-                    break;
-                }
-                if (st == kStAggregate) {
-                    excl += (uint32_t)v;
-                    t--;
-                    continue;
-                }
-                if (++spins > kSpinLimit) {
-                    atomicOr(&prm->bad_input, 2u);
-                    break;
-                }
-            }
-            __hip_atomic_store(lb_words + tile, kStInclusive | (excl + tot), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    if (i <= (int64_t)n) loc[i] = woff + inc - nst;
+    if (threadIdx.x == 0) tile_sum[blockIdx.x] = tot;
+}
+
+// One block: exclusive scan of the tile sums in place; the total is n_nodes.
+__global__ __launch_bounds__(1024) void k_tile_scan(uint32_t *__restrict__ tile_sum, uint32_t n_tiles,
+                                                    DevParams *__restrict__ prm) {
+    __shared__ uint32_t s_wsum[16];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t carry = 0;
+    for (uint32_t c0 = 0; c0 < n_tiles; c0 += 1024) {
+        const uint32_t k = c0 + threadIdx.x;
+        const uint32_t v = k < n_tiles ? tile_sum[k] : 0u;
+        uint32_t inc = v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += t;
         }
-        s_excl = excl;
+        if (lane == 63) s_wsum[w] = inc;
+        __syncthreads();
+        uint32_t woff = 0, tot = 0;
+        for (int q = 0; q < 16; q++) {
+            if (q < w) woff += s_wsum[q];
+            tot += s_wsum[q];
+        }
+        if (k < n_tiles) tile_sum[k] = carry + woff + inc - v;
+        carry += tot;
+        __syncthreads();
     }
-    __syncthreads();
-    if (i <= (int64_t)n) base[i] = s_excl + woff + inc - nst;  // base[n] = n_nodes
-    if (i == (int64_t)n) prm->n_nodes = s_excl + woff + inc - nst;
+    if (threadIdx.x == 0) prm->n_nodes = carry;
 }
 
 // First j > start whose key differs from pre in its top bits (key >> sh), or
@@ -159,113 +155,121 @@ __device__ uint32_t cell_end(const uint64_t *__restrict__ keys, uint32_t n, uint
     return (uint32_t)hi;
 }
 
-// First j <= i whose key shares key[i]'s top bits (key >> sh).
-__device__ uint32_t cell_begin(const uint64_t *__restrict__ keys, uint32_t i, int sh, uint64_t pre) {
-    int64_t hi = i, lo, step = 1;
-    for (;;) {
-        const int64_t probe = hi - step;
-        if (probe < 0) {
-            lo = -1;
-            break;
-        }
-        if ((keys[probe] >> sh) != pre) {
-            lo = probe;
-            break;
-        }
-        hi = probe;
-        step <<= 1;
-    }
-    while (hi - lo > 1) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if ((keys[mid] >> sh) == pre)
-            hi = mid;
-        else
-            lo = mid;
-    }
-    return (uint32_t)hi;
-}
-
-// One thread per particle: write every node the particle starts, deepest
-// first so that each cell end is searched from the end of the cell inside it;
-// list the cut nodes (count <= kCutParticles, parent larger or none) and the
-// nodes above the cut.
-__global__ __launch_bounds__(256) void k_tree_emit(const uint64_t *__restrict__ keys,
-                                                   const uint32_t *__restrict__ info,
-                                                   const uint32_t *__restrict__ base, uint32_t n,
-                                                   DevParams *__restrict__ prm, NodeRec *__restrict__ nodes,
-                                                   uint8_t *__restrict__ level, uint32_t *__restrict__ cut_list,
-                                                   uint32_t *__restrict__ top_list) {
+// One thread per particle: the level and first particle of every node it
+// starts.
+__global__ __launch_bounds__(256) void k_tree_stub(const uint32_t *__restrict__ info,
+                                                   const uint32_t *__restrict__ tile_pre,
+                                                   const uint32_t *__restrict__ loc, uint32_t n,
+                                                   NodeRec *__restrict__ nodes, uint8_t *__restrict__ level) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n) return;
     const uint32_t inf = info[i];
     const int first = (int)(inf & 0xffu), D = (int)(inf >> 8);
-    if (D < first) return;
-    const uint64_t ki = keys[i];
-    const float side = prm->side;
-    const uint32_t node0 = base[i];
-    uint32_t end = i + 1, child_count = 0;
-    for (int l = D; l >= first; l--) {
-        const int sh = 3 * (kMaxLevel - l);  // 63 at the root: every key maps to 0
-        end = cell_end(keys, n, end - 1, sh, ki >> sh);
-        const uint32_t node = node0 + (uint32_t)(l - first);
-        const uint32_t count = end - i;
-        const float s = ldexpf(side, -l);  // exact
-        const float s2 = s * s;
-        nodes[node].t = make_uint4(base[end], i, count, __float_as_uint(s2));
+    uint32_t node = base_at(tile_pre, loc, i);
+    for (int l = first; l <= D; l++, node++) {
+        nodes[node].t.y = i;
         level[node] = (uint8_t)l;
-        // the child started here (level l + 1) is a cut node iff it is small and this node is not
-        if (l < D && child_count <= kCutParticles && count > kCutParticles)
-            cut_list[atomicAdd(&prm->n_cut, 1u)] = node + 1;
-        if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = node;
-        child_count = count;
-    }
-    // the node of level first: its parent starts before i (or it is the root)
-    if (child_count <= kCutParticles) {
-        bool cut = first == 0;
-        if (first > 0) {
-            const int shp = 3 * (kMaxLevel - (first - 1));
-            const uint64_t prep = ki >> shp;
-            const uint32_t pb = cell_begin(keys, i, shp, prep);
-            const uint32_t pe = cell_end(keys, n, end - 1, shp, prep);
-            cut = pe - pb > kCutParticles;
-        }
-        if (cut) cut_list[atomicAdd(&prm->n_cut, 1u)] = node0;
     }
 }
 
-__device__ __forceinline__ void finish_node(uint32_t k, const uint4 &t, const float4 *__restrict__ xs,
-                                            NodeRec *nodes, float4 *msum) {
-    float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
-    if (t.x == k + 1) {  // leaf: its particles in sorted order
-        for (uint32_t j = t.y; j < t.y + t.z; j++) {
-            const float4 p = xs[j];
-            M += p.w;
-            sx += p.w * p.x;
-            sy += p.w * p.y;
-            sz += p.w * p.z;
-        }
-    } else {  // internal: its children in octant order
-        for (uint32_t q = k + 1; q < t.x; q = max(nodes[q].t.x, q + 1)) {
-            const float4 cs = msum[q];
-            M += cs.w;
-            sx += cs.x;
-            sy += cs.y;
-            sz += cs.z;
-        }
-    }
+// Sums of one node, stored for the parent (S, M) and for the walk (com, M).
+__device__ __forceinline__ void store_sums(uint32_t k, float M, float sx, float sy, float sz, uint32_t first,
+                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum) {
     msum[k] = make_float4(sx, sy, sz, M);
     float4 g;
     if (M > 0.0f) {
         g = make_float4(sx / M, sy / M, sz / M, M);  // correctly rounded divisions
     } else {
-        const float4 p = xs[t.y];
+        const float4 p = xs[first];
         g = make_float4(p.x, p.y, p.z, M);
     }
     nodes[k].g = g;
 }
 
-// One workgroup per cut subtree (grid-stride over the cut list): the nodes of
-// [r, escape(r)) level by level, deepest first.
+// Leaf: its particles in sorted order.
+__device__ __forceinline__ void finish_leaf(uint32_t k, uint32_t first, uint32_t count, const float4 *__restrict__ xs,
+                                            NodeRec *nodes, float4 *msum) {
+    float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
+    for (uint32_t j = first; j < first + count; j++) {
+        const float4 p = xs[j];
+        M += p.w;
+        sx += p.w * p.x;
+        sy += p.w * p.y;
+        sz += p.w * p.z;
+    }
+    store_sums(k, M, sx, sy, sz, first, xs, nodes, msum);
+}
+
+// One thread per node: its cell end (searched from its first particle), count,
+// escape index and s^2; nodes larger than the cut go to the top list; leaves
+// also get their moments.
+__global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ keys, uint32_t n,
+                                                   const uint32_t *__restrict__ tile_pre,
+                                                   const uint32_t *__restrict__ loc, DevParams *__restrict__ prm,
+                                                   uint32_t max_nodes, NodeRec *nodes,
+                                                   const uint8_t *__restrict__ level, uint32_t *__restrict__ top_list,
+                                                   const float4 *__restrict__ xs, float4 *msum) {
+    const uint32_t k = blockIdx.x * 256u + threadIdx.x;
+    if (k >= min(prm->n_nodes, max_nodes)) return;
+    const int l = level[k];
+    const uint32_t i = nodes[k].t.y;
+    const int sh = 3 * (kMaxLevel - l);
+    const uint32_t end = l == 0 ? n : cell_end(keys, n, i, sh, keys[i] >> sh);
+    const uint32_t count = end - i;
+    const float s = ldexpf(prm->side, -l);  // exact
+    const float s2 = s * s;
+    const uint32_t esc = base_at(tile_pre, loc, end);
+    nodes[k].t = make_uint4(esc, i, count, __float_as_uint(s2));
+    if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = k;
+    if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum);
+}
+
+// Cut nodes (count <= kCutParticles, parent larger or none): the root if no
+// node is larger than the cut, else the small children of the nodes above
+// the cut. Each of those records its children: kids[9e] = how many,
+// kids[9e + 1 ..] = their indices in octant order.
+__global__ __launch_bounds__(256) void k_tree_cut(const NodeRec *__restrict__ nodes, DevParams *__restrict__ prm,
+                                                  uint32_t max_nodes, const uint32_t *__restrict__ top_list,
+                                                  uint32_t *__restrict__ kids, uint32_t *__restrict__ cut_list) {
+    const uint32_t nn = min(prm->n_nodes, max_nodes);
+    const uint32_t n_top = prm->n_top;
+    if (n_top == 0) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            cut_list[0] = 0;
+            prm->n_cut = 1;
+        }
+        return;
+    }
+    for (uint32_t e = blockIdx.x * 256u + threadIdx.x; e < n_top; e += gridDim.x * 256u) {
+        const uint32_t k = top_list[e];
+        const uint32_t end = min(nodes[k].t.x, nn);
+        uint32_t nk = 0;
+        for (uint32_t q = k + 1; q < end && nk < 8;) {
+            const uint4 tq = nodes[q].t;
+            kids[9 * e + 1 + nk++] = q;
+            if (tq.z <= kCutParticles) cut_list[atomicAdd(&prm->n_cut, 1u)] = q;
+            q = max(tq.x, q + 1);
+        }
+        kids[9 * e] = nk;
+    }
+}
+
+// Internal node: its children in octant order, by the escape chain.
+__device__ __forceinline__ void finish_internal(uint32_t k, const uint4 &t, const float4 *__restrict__ xs,
+                                                NodeRec *nodes, float4 *msum) {
+    float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
+    for (uint32_t q = k + 1; q < t.x; q = max(nodes[q].t.x, q + 1)) {
+        const float4 cs = msum[q];
+        M += cs.w;
+        sx += cs.x;
+        sy += cs.y;
+        sz += cs.z;
+    }
+    store_sums(k, M, sx, sy, sz, t.y, xs, nodes, msum);
+}
+
+// One workgroup per cut subtree (grid-stride over the cut list): the internal
+// nodes of [r, escape(r)) level by level, deepest first (leaves are done).
 __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ xs, NodeRec *nodes,
                                                      const uint8_t *__restrict__ level,
                                                      const uint32_t *__restrict__ cut_list,
@@ -286,17 +290,22 @@ __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ 
         __syncthreads();
         const int lmax = s_lmax;
         for (int l = lmax; l >= lmin; l--) {
-            for (uint32_t k = r + threadIdx.x; k < end; k += 256)
-                if (level[k] == l) finish_node(k, nodes[k].t, xs, nodes, msum);
+            for (uint32_t k = r + threadIdx.x; k < end; k += 256) {
+                if (level[k] != l) continue;
+                const uint4 t = nodes[k].t;
+                if (t.x != k + 1) finish_internal(k, t, xs, nodes, msum);
+            }
             __syncthreads();
         }
     }
 }
 
-// One workgroup: the nodes above the cut, level by level, deepest first.
+// One workgroup: the internal nodes above the cut, level by level, deepest
+// first, their children read from the recorded lists.
 __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__ xs, NodeRec *nodes,
                                                       const uint8_t *__restrict__ level,
                                                       const uint32_t *__restrict__ top_list,
+                                                      const uint32_t *__restrict__ kids,
                                                       const DevParams *__restrict__ prm, float4 *msum) {
     __shared__ int s_lmin, s_lmax;
     const uint32_t n_top = prm->n_top;
@@ -314,7 +323,19 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
     for (int l = s_lmax; l >= s_lmin; l--) {
         for (uint32_t e = threadIdx.x; e < n_top; e += 1024) {
             const uint32_t k = top_list[e];
-            if (level[k] == l) finish_node(k, nodes[k].t, xs, nodes, msum);
+            const uint32_t nk = kids[9 * e];
+            if (level[k] != l || nk == 0) continue;  // other level, or a leaf (done)
+            float4 cs[8];
+            for (uint32_t j = 0; j < 8; j++)
+                if (j < nk) cs[j] = msum[kids[9 * e + 1 + j]];
+            float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
+            for (uint32_t j = 0; j < nk; j++) {
+                M += cs[j].w;
+                sx += cs[j].x;
+                sy += cs[j].y;
+                sz += cs[j].z;
+            }
+            store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
         }
         __syncthreads();
     }
@@ -357,11 +378,14 @@ __global__ __launch_bounds__(256) void k_info(const NodeRec *__restrict__ nodes,
 
 hipError_t launch_build(const Workspace &ws, hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
-    k_tree_count_scan<<<(unsigned)ceil_div(ws.n + 1, 256), 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info,
-                                                                       ws.base, ws.lb_words + ws.lb_scan_offset,
-                                                                       ws.prm);
-    k_tree_emit<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.keys[0], ws.info, ws.base, n, ws.prm, ws.nodes,
-                                                              ws.level, ws.cut_list, ws.top_list);
+    const uint32_t scan_tiles = (uint32_t)ceil_div(ws.n + 1, kScanTile);
+    const unsigned node_blocks = (unsigned)ceil_div(ws.max_nodes, 256);
+    k_tree_count<<<scan_tiles, 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info, ws.base, ws.tile_sum);
+    k_tile_scan<<<1, 1024, 0, s>>>(ws.tile_sum, scan_tiles, ws.prm);
+    k_tree_stub<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.tile_sum, ws.base, n, ws.nodes, ws.level);
+    k_tree_ends<<<node_blocks, 256, 0, s>>>(ws.keys[0], n, ws.tile_sum, ws.base, ws.prm, (uint32_t)ws.max_nodes,
+                                            ws.nodes, ws.level, ws.top_list, ws.xs, ws.msum);
+    k_tree_cut<<<64, 256, 0, s>>>(ws.nodes, ws.prm, (uint32_t)ws.max_nodes, ws.top_list, ws.kids, ws.cut_list);
     return hipGetLastError();
 }
 
@@ -369,7 +393,7 @@ hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 2));
     k_moments_cut<<<blocks, 256, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.cut_list, ws.prm, (uint32_t)ws.max_nodes,
                                          ws.msum);
-    k_moments_top<<<1, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.prm, ws.msum);
+    k_moments_top<<<1, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum);
     return hipGetLastError();
 }
 
