@@ -27,6 +27,9 @@
 #ifndef ORR_XCD_REMAP
 #define ORR_XCD_REMAP 1
 #endif
+#ifndef ORR_PACK_KMAX
+#define ORR_PACK_KMAX 8  // pack leaf rows when at most this many lanes open the leaf
+#endif
 
 namespace orr {
 
@@ -85,6 +88,72 @@ __device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, 
     add_term_r2<kInv>(m, dx, dy, dz, ((dx * dx + dy * dy) + dz * dz) + eps2, ax, ay, az);
 }
 
+// The term's product f * d alone (same operations as add_term_r2 before its
+// three additions), for terms whose accumulation happens in another lane.
+template <int kInv>
+__device__ __forceinline__ float4 term_product(float m, float dx, float dy, float dz, float eps2) {
+    const float r2 = ((dx * dx + dy * dy) + dz * dz) + eps2;
+    const float inv = kInv == kInvIeee ? 1.0f / sqrtf(r2) : inv_sqrt_rn<kInv == kInvFast>(r2);
+    const float f = m * ((inv * inv) * inv);
+    return make_float4(f * dx, f * dy, f * dz, 0.0f);
+}
+
+// Orders the wave's LDS accesses around a hand-over between lanes (LDS
+// requests of one wave are served in order; this keeps the compiler's order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Particles per row when k lanes open a leaf of cnt particles: the wave is
+// split into g slots of 64/g lanes (g = 1, 2, 4, 8), each slot one particle,
+// each lane of a slot one opening lane.
+__device__ __forceinline__ uint32_t pack_width(uint32_t k, uint32_t cnt) {
+    uint32_t g = k > ORR_PACK_KMAX ? 1u : k <= 8 ? 8u : k <= 16 ? 4u : k <= 32 ? 2u : 1u;
+    while (g > 1 && (g >> 1) >= cnt) g >>= 1;  // no wider than the leaf
+    return g;
+}
+
+// A leaf opened by the lanes of m_open, packed g > 1 particles per row: lane
+// (slot q, position r) computes the term of the row's particle q for the
+// r-th opening lane; each opening lane then adds its products in particle
+// order, so its sum is the one its own walk makes. Per wave LDS: tgt = the
+// opening lanes' positions, src = up to 64 of the leaf's particles, prod =
+// one row of products.
+template <int kInv>
+__device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint32_t g,
+                                            uint64_t m_open, bool opening, const float4 &xi, float eps2, float &ax,
+                                            float &ay, float &az, float4 *tgt, float4 *src, float4 *prod) {
+    const uint32_t lane = __lane_id();
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_open >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m_open, 0u));
+    const uint32_t k = (uint32_t)__popcll(m_open);
+    const uint32_t lw = 6u - (31u - __clz(g));  // log2(64 / g)
+    const uint32_t q = lane >> lw, r = lane & ((1u << lw) - 1u);
+    if (opening) tgt[rank] = xi;
+    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
+        const uint32_t cc = min(cnt - c0, 64u);
+        if (lane < cc) src[lane] = xs[b + c0 + lane];
+        wave_lds_sync();
+        for (uint32_t j0 = 0; j0 < cc; j0 += g) {
+            if (r < k && j0 + q < cc) {
+                const float4 p = src[j0 + q], t = tgt[r];
+                prod[lane] = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
+            }
+            wave_lds_sync();
+            if (opening) {
+                for (uint32_t qq = 0; qq < g && j0 + qq < cc; qq++) {
+                    const float4 v = prod[(qq << lw) + rank];
+                    ax += v.x;
+                    ay += v.y;
+                    az += v.z;
+                }
+            }
+            wave_lds_sync();
+        }
+    }
+}
+
 // Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous run
 // of target blocks so that its L2 holds one region of the tree.
 __device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
@@ -118,14 +187,21 @@ __device__ __forceinline__ bool r2_cannot_overflow(const DevParams *prm, float e
     return 3.0 * s * s + (double)eps2 < 1e38;
 }
 
+// Wave-private LDS of the packed leaf evaluation.
+struct WalkLds {
+    float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64];
+};
+
 template <int kInv>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
-                                              uint32_t n_nodes, float eps2, float theta2, const WalkOut &out) {
+                                              uint32_t n_nodes, float eps2, float theta2, const WalkOut &out,
+                                              WalkLds &lds) {
     const bool valid = i < n;
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
+    const uint32_t wv = threadIdx.x >> 6;
     // visits_own = accepted nodes + opened nodes, so no per-step counter
     uint32_t pp = 0, pc = 0, nopen = 0;
     uint32_t steps = 0;  // wave-uniform: visits_stepped
@@ -146,15 +222,27 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
             next = esc;
         }
         if (esc == c + 1) {  // leaf
-            if (active && !far) {
+            const bool opening = active && !far;
+            const uint64_t m_open = __builtin_amdgcn_ballot_w64(opening);
+            if (m_open) {
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
-                for (uint32_t j = b; j < b + cnt; j++) {
-                    const float4 p = xs[j];
-                    add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                const uint32_t g = pack_width((uint32_t)__popcll(m_open), cnt);
+                if (g == 1) {
+                    if (opening) {
+                        for (uint32_t j = b; j < b + cnt; j++) {
+                            const float4 p = xs[j];
+                            add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                        }
+                    }
+                } else {
+                    leaf_packed<kInv>(xs, b, cnt, g, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv],
+                                      lds.prod[wv]);
                 }
-                pp += cnt - ((i - b) < cnt ? 1u : 0u);
-                nopen += 1;
-                next = esc;
+                if (opening) {
+                    pp += cnt - ((i - b) < cnt ? 1u : 0u);
+                    nopen += 1;
+                    next = esc;
+                }
             }
             c = esc;
         } else {
@@ -177,14 +265,15 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
                                                               const uint32_t *__restrict__ perm, uint32_t n,
                                                               uint32_t max_nodes, float eps2, float theta2,
                                                               WalkOut out) {
+    __shared__ WalkLds lds;
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
-        walk_coherent<kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_coherent<kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else if (r2_cannot_overflow(prm, eps2))  // uniform
-        walk_coherent<kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_coherent<kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else
-        walk_coherent<kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_coherent<kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
 }
 
 template <int kInv>
