@@ -24,9 +24,6 @@
 #ifndef ORR_WALK_BLOCK
 #define ORR_WALK_BLOCK 256
 #endif
-#ifndef ORR_XCD_REMAP
-#define ORR_XCD_REMAP 1
-#endif
 #ifndef ORR_PACK_KMAX
 #define ORR_PACK_KMAX 8  // pack leaf rows when at most this many lanes open the leaf
 #endif
@@ -114,6 +111,36 @@ __device__ __forceinline__ uint32_t pack_width(uint32_t k, uint32_t cnt) {
     return g;
 }
 
+// A leaf opened by many lanes: its particles are staged in the wave's LDS
+// (one coalesced load, one particle per lane) and every opening lane adds
+// them in particle order, one broadcast LDS read per particle.
+template <int kInv>
+__device__ __forceinline__ void leaf_masked(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, bool opening,
+                                            const float4 &xi, float eps2, float &ax, float &ay, float &az,
+                                            float4 *src) {
+    const uint32_t lane = __lane_id();
+    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
+        const uint32_t cc = min(cnt - c0, 64u);
+        if (lane < cc) src[lane] = xs[b + c0 + lane];
+        wave_lds_sync();
+        if (opening) {
+            uint32_t j = 0;
+            for (; j + 4u <= cc; j += 4u) {  // four reads in flight
+                const float4 p0 = src[j], p1 = src[j + 1], p2 = src[j + 2], p3 = src[j + 3];
+                add_term<kInv>(p0.w, p0.x - xi.x, p0.y - xi.y, p0.z - xi.z, eps2, ax, ay, az);
+                add_term<kInv>(p1.w, p1.x - xi.x, p1.y - xi.y, p1.z - xi.z, eps2, ax, ay, az);
+                add_term<kInv>(p2.w, p2.x - xi.x, p2.y - xi.y, p2.z - xi.z, eps2, ax, ay, az);
+                add_term<kInv>(p3.w, p3.x - xi.x, p3.y - xi.y, p3.z - xi.z, eps2, ax, ay, az);
+            }
+            for (; j < cc; j++) {
+                const float4 p = src[j];
+                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+            }
+        }
+        wave_lds_sync();
+    }
+}
+
 // A leaf opened by the lanes of m_open, packed g > 1 particles per row: lane
 // (slot q, position r) computes the term of the row's particle q for the
 // r-th opening lane; each opening lane then adds its products in particle
@@ -154,12 +181,13 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
     }
 }
 
-// Blocks are handed to the 8 XCDs round-robin; give each XCD a contiguous run
-// of target blocks so that its L2 holds one region of the tree.
-__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
-    if (!ORR_XCD_REMAP) return b;
-    const uint32_t x = b & 7u, q = nblocks >> 3, r = nblocks & 7u;
-    return x * q + min(x, r) + (b >> 3);
+// Sorted targets of this lane's wave: wave slot s of the grid runs target
+// wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
+// schedule get no targets.
+__device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict__ order, uint32_t n_waves) {
+    const uint32_t slot = blockIdx.x * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t w = slot < n_waves ? min(order[slot], n_waves) : n_waves;
+    return w * 64u + (threadIdx.x & 63u);
 }
 
 struct WalkOut {
@@ -228,12 +256,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
                 const uint32_t g = pack_width((uint32_t)__popcll(m_open), cnt);
                 if (g == 1) {
-                    if (opening) {
-                        for (uint32_t j = b; j < b + cnt; j++) {
-                            const float4 p = xs[j];
-                            add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
-                        }
-                    }
+                    leaf_masked<kInv>(xs, b, cnt, opening, xi, eps2, ax, ay, az, lds.src[wv]);
                 } else {
                     leaf_packed<kInv>(xs, b, cnt, g, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv],
                                       lds.prod[wv]);
@@ -258,15 +281,67 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
+// Walk schedule. How long a wave runs grows with the particle density
+// around its targets, and the depth of a target's leaf measures that density.
+// Target waves start in order of decreasing summed leaf depth, so the longest
+// ones start first and the last to start are short: longest-first list
+// scheduling, which keeps the grid's tail short when a wave runs for a large
+// part of the whole launch. The schedule decides only when a wave runs, never
+// what it computes.
+constexpr int kWaveOrderThreads = kWaveCostBins / 2;
+
+__global__ __launch_bounds__(256) void k_wave_cost(const uint32_t *__restrict__ info, uint32_t n,
+                                                   uint32_t *__restrict__ cost) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    uint32_t d = i < n ? (info[i] >> 8) & 0xffu : 0u;  // leaf depth of sorted target i
+    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+    if ((threadIdx.x & 63u) == 0u && i < n) cost[i >> 6] = d;
+}
+
+// One block: counting sort of the waves by decreasing cost. Waves of equal
+// cost may come out in any order.
+__global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t *__restrict__ cost,
+                                                                  uint32_t n_waves, uint32_t *__restrict__ order) {
+    __shared__ uint32_t bins[kWaveCostBins];
+    __shared__ uint32_t wsum[kWaveOrderThreads / 64];
+    const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
+    for (uint32_t b = t; b < (uint32_t)kWaveCostBins; b += kWaveOrderThreads) bins[b] = 0u;
+    __syncthreads();
+    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads)
+        atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
+    __syncthreads();
+    // Exclusive scan in decreasing cost; thread t owns bins b0 = top - 2t and b0 - 1.
+    const uint32_t b0 = (uint32_t)kWaveCostBins - 1u - 2u * t, b1 = b0 - 1u;
+    const uint32_t c0 = bins[b0], c1 = bins[b1];
+    uint32_t x = c0 + c1;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= (uint32_t)o) x += y;
+    }
+    if (lane == 63u) wsum[wv] = x;
+    __syncthreads();
+    uint32_t before = 0u;
+    for (uint32_t k = 0; k < wv; k++) before += wsum[k];
+    const uint32_t excl = before + x - (c0 + c1);
+    bins[b0] = excl;
+    bins[b1] = excl + c0;
+    __syncthreads();
+    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads) {
+        const uint32_t pos = atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
+        order[pos] = w;
+    }
+}
+
 template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
                                                               const uint32_t *__restrict__ perm, uint32_t n,
                                                               uint32_t max_nodes, float eps2, float theta2,
-                                                              WalkOut out) {
+                                                              const uint32_t *__restrict__ order,
+                                                              uint32_t n_waves, WalkOut out) {
     __shared__ WalkLds lds;
-    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
+    const uint32_t i = scheduled_target(order, n_waves);
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
         walk_coherent<kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
@@ -315,8 +390,9 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
                                                                  const DevParams *__restrict__ prm,
                                                                  const uint32_t *__restrict__ perm, uint32_t n,
                                                                  uint32_t max_nodes, float eps2, float theta2,
-                                                                 WalkOut out) {
-    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
+                                                                 const uint32_t *__restrict__ order,
+                                                                 uint32_t n_waves, WalkOut out) {
+    const uint32_t i = scheduled_target(order, n_waves);
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
@@ -351,13 +427,16 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
                          hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
     const uint32_t nb = (uint32_t)ws.max_nodes;
+    const uint32_t nw = (uint32_t)ws.n_waves;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
+    k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, n, ws.wave_cost);
+    k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
     if (coherent)
         k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2,
-                                                             theta2, out);
+                                                             theta2, ws.wave_order, nw, out);
     else
         k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
-                                                                eps2, theta2, out);
+                                                                eps2, theta2, ws.wave_order, nw, out);
     return hipGetLastError();
 }
 
