@@ -29,7 +29,7 @@ constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube redu
 
 constexpr int kSortHistBlocks = 256;     // blocks of the key + histogram pass
 constexpr uint32_t kCutParticles = 4096; // subtrees of at most this many particles get one workgroup
-constexpr int kWaveCostBins = 2048;      // wave cost = sum of 64 leaf depths <= 64 * 21 = 1344
+constexpr int kWaveCostBins = 2048;      // bins of the walk schedule's wave cost
 
 // Device-resident scalars of one build, at the start of the workspace.
 struct DevParams {
@@ -77,7 +77,7 @@ struct Workspace {
     uint32_t *cut_list;    // [max_nodes] roots of the subtrees finished by one workgroup each
     uint32_t *top_list;    // [max_top] nodes above the cut
     uint32_t *kids;        // [9 max_top] child count and children of each node above the cut
-    uint32_t *wave_cost;   // [n_waves] sum of the leaf depths of a wave's 64 sorted targets
+    uint32_t *wave_cost;   // [n_waves] estimated run time of a wave of 64 sorted targets
     uint32_t *wave_order;  // [n_waves] walk schedule: target waves by decreasing cost
     int64_t n_waves;       // ceil(n / 64)
     int64_t max_top;

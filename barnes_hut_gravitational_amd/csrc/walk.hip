@@ -282,20 +282,36 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
 }
 
 // Walk schedule. How long a wave runs grows with the particle density
-// around its targets, and the depth of a target's leaf measures that density.
-// Target waves start in order of decreasing summed leaf depth, so the longest
-// ones start first and the last to start are short: longest-first list
-// scheduling, which keeps the grid's tail short when a wave runs for a large
-// part of the whole launch. The schedule decides only when a wave runs, never
-// what it computes.
+// around its targets, which the depth of a target's leaf measures, and with
+// how spread out its 64 targets are: the wave steps through the union of
+// their walks, which grows when the targets span a large cell. The cost of a
+// wave is its summed leaf depth plus 32 times the levels between its deepest
+// leaf and the smallest cell holding all its targets (from the common prefix
+// of its first and last sorted key). Target waves start in order of
+// decreasing cost, so the longest ones start first and the last to start are
+// short: longest-first list scheduling, which keeps the grid's tail short
+// when a wave runs for a large part of the whole launch. The schedule decides
+// only when a wave runs, never what it computes.
 constexpr int kWaveOrderThreads = kWaveCostBins / 2;
+static_assert(64 * kMaxLevel + 32 * kMaxLevel < kWaveCostBins, "wave cost range");
 
-__global__ __launch_bounds__(256) void k_wave_cost(const uint32_t *__restrict__ info, uint32_t n,
+__global__ __launch_bounds__(256) void k_wave_cost(const uint32_t *__restrict__ info,
+                                                   const uint64_t *__restrict__ keys, uint32_t n,
                                                    uint32_t *__restrict__ cost) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-    uint32_t d = i < n ? (info[i] >> 8) & 0xffu : 0u;  // leaf depth of sorted target i
-    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
-    if ((threadIdx.x & 63u) == 0u && i < n) cost[i >> 6] = d;
+    const uint32_t d = i < n ? (info[i] >> 8) & 0xffu : 0u;  // leaf depth of sorted target i
+    uint32_t sum = d, deepest = d;
+    for (int o = 32; o > 0; o >>= 1) {
+        sum += __shfl_xor(sum, o, 64);
+        deepest = max(deepest, __shfl_xor(deepest, o, 64));
+    }
+    if ((threadIdx.x & 63u) == 0u && i < n) {
+        const uint64_t x = keys[i] ^ keys[min(i + 63u, n - 1u)];
+        // Level of the smallest cell holding the wave's targets: whole levels
+        // of the common key prefix below bit 63 (always zero).
+        const uint32_t enclosing = (x == 0ull ? 63u : (uint32_t)__clzll(x) - 1u) / 3u;
+        cost[i >> 6] = sum + 32u * (deepest > enclosing ? deepest - enclosing : 0u);  // <= 64*21 + 32*21 < 2048
+    }
 }
 
 // One block: counting sort of the waves by decreasing cost. Waves of equal
@@ -429,7 +445,7 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
     const uint32_t nb = (uint32_t)ws.max_nodes;
     const uint32_t nw = (uint32_t)ws.n_waves;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
-    k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, n, ws.wave_cost);
+    k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
     k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
     if (coherent)
         k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2,
