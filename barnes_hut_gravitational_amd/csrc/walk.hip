@@ -181,6 +181,14 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
     }
 }
 
+// Blocks are handed to the 8 XCDs round-robin; the independent walk gives
+// each XCD a contiguous run of target blocks, so that its L2 holds one region
+// of the tree for the per-lane node loads.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
+    const uint32_t x = b & 7u, q = nblocks >> 3, r = nblocks & 7u;
+    return x * q + min(x, r) + (b >> 3);
+}
+
 // Sorted targets of this lane's wave: wave slot s of the grid runs target
 // wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
 // schedule get no targets.
@@ -406,9 +414,8 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
                                                                  const DevParams *__restrict__ prm,
                                                                  const uint32_t *__restrict__ perm, uint32_t n,
                                                                  uint32_t max_nodes, float eps2, float theta2,
-                                                                 const uint32_t *__restrict__ order,
-                                                                 uint32_t n_waves, WalkOut out) {
-    const uint32_t i = scheduled_target(order, n_waves);
+                                                                 WalkOut out) {
+    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
@@ -445,14 +452,15 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
     const uint32_t nb = (uint32_t)ws.max_nodes;
     const uint32_t nw = (uint32_t)ws.n_waves;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
-    k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
-    k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
-    if (coherent)
+    if (coherent) {
+        k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
+        k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
         k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2,
                                                              theta2, ws.wave_order, nw, out);
-    else
+    } else {
         k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
-                                                                eps2, theta2, ws.wave_order, nw, out);
+                                                                eps2, theta2, out);
+    }
     return hipGetLastError();
 }
 
