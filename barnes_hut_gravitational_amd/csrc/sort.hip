@@ -12,14 +12,15 @@
 //   * k_morton_hist computes every key once and the 8 digit histograms of all
 //     keys; k_digit_offsets turns them into the first output slot of each
 //     digit in each pass.
-//   * k_onesweep, one launch per pass: a tile of 2048 keys takes a ticket (its
-//     position in the output), ranks its keys stably inside each wave (lanes
-//     with the same digit found with 8 ballots), publishes its digit counts,
-//     and adds the counts of the tiles before it by decoupled look-back:
-//     walking back over predecessors' published words until one carries an
-//     inclusive prefix. Tickets are taken in the order blocks start, so every
-//     predecessor is running or done and publishes its counts without waiting
-//     on anyone; each wait is nevertheless bounded and reports an error.
+//   * k_onesweep, one launch per pass: a tile of 4096 keys (256 threads x 16)
+//     takes a ticket (its position in the output), ranks its keys stably
+//     inside each wave (lanes with the same digit found with 8 ballots),
+//     publishes its digit counts, and adds the counts of the tiles before it
+//     by decoupled look-back: walking back over predecessors' published words
+//     until one carries an inclusive prefix. Tickets are taken in the order
+//     blocks start, so every predecessor is running or done and publishes its
+//     counts without waiting on anyone; each wait is nevertheless bounded and
+//     reports an error.
 #include "orr_internal.h"
 
 namespace orr {

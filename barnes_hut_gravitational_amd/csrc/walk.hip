@@ -7,8 +7,10 @@
 // is c + 1 if an acting lane opened an internal node and escape[c] otherwise
 // (a lane waiting at c skipped an ancestor of c, so its next is at least
 // escape[c]); that is one ballot per node. Node records are wave-uniform and
-// come through scalar loads; leaf particles are wave-uniform too, so a leaf
-// is streamed once for all its opening lanes.
+// come through scalar loads. An opened leaf is read once for all its opening
+// lanes: its particles are staged in the wave's LDS with one coalesced load;
+// when few lanes open it, their terms are also packed across the wave's
+// lanes. Target waves start in the order of a cost estimate (longest first).
 //
 // Independent walk (enum TreeTraversal, kIndependent): one lane per target,
 // each following its own node index with per-lane vector loads; the measured
