@@ -71,6 +71,8 @@ def lib():
         L.oracle_group_walk.restype = ctypes.c_int
         L.oracle_direct_fp64.argtypes = [_f32p, _f32p, _i64, ctypes.c_double, _i64p, _i64, _f64p]
         L.oracle_direct_fp64.restype = None
+        L.oracle_direct_fp32.argtypes = [_f32p, _f32p, _i64, _f32, _i64p, _i64, _f32p]
+        L.oracle_direct_fp32.restype = None
         _lib = L
     return _lib
 
@@ -242,6 +244,17 @@ def group_walk(t: Tree, eps, theta, width=64, rule="min"):
     own = np.empty(t.n, np.uint32)
     bad = lib().oracle_group_walk(*_walk_args(t, eps, theta), width, 0 if rule == "min" else 1, steps, own)
     return steps, own, bad == 0
+
+
+def direct_fp32(pos, mass, eps, targets=None):
+    """Float32 direct sum in index order with the walk's term, for caller-order
+    targets (all if None); the target's own term (+0) is included."""
+    pos, mass = _f32c(pos), _f32c(mass)
+    n = len(mass)
+    targets = np.arange(n, dtype=np.int64) if targets is None else np.ascontiguousarray(targets, np.int64)
+    acc = np.empty((len(targets), 3), np.float32)
+    lib().oracle_direct_fp32(pos.reshape(-1), mass, n, _f32(eps), targets, len(targets), acc.reshape(-1))
+    return acc
 
 
 def direct_fp64(pos, mass, eps, targets=None):

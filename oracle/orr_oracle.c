@@ -464,6 +464,29 @@ int oracle_group_walk(const float *xs, int64_t n, const float *geom, const float
 /* summed directly over all pairs in double precision, with Neumaier         */
 /* compensation, for the listed targets (caller order). j = i is skipped.    */
 /* ------------------------------------------------------------------------ */
+/* Float32 direct sum, the all-pairs reference (the direct solver of the     */
+/* orrery pages, "Against the two solvers it has to beat"): for each listed  */
+/* caller-order target i, a_i = sum over every particle j in index order of  */
+/* the same softened term as the walk's (add_term), the target's own term    */
+/* (an exact +0) included. One target per OpenMP iteration.                  */
+/* ------------------------------------------------------------------------ */
+void oracle_direct_fp32(const float *pos, const float *mass, int64_t n, float eps, const int64_t *targets,
+                        int64_t n_targets, float *acc) {
+    const float eps2 = eps * eps;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < n_targets; t++) {
+        const int64_t i = targets[t];
+        const float xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+        float a[3] = {0.0f, 0.0f, 0.0f};
+        for (int64_t j = 0; j < n; j++)
+            add_term(mass[j], pos[3 * j] - xi, pos[3 * j + 1] - yi, pos[3 * j + 2] - zi, eps2, a);
+        acc[3 * t + 0] = a[0];
+        acc[3 * t + 1] = a[1];
+        acc[3 * t + 2] = a[2];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 typedef struct {
     double s, c;
 } neumaier;
