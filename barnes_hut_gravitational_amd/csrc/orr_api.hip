@@ -365,6 +365,19 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
     ORR_GUARD_END
 }
 
+orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, float eps, float *acc,
+                             void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!pos || !mass || !acc) return fail(ORR_ERR_INVALID_ARG, "pos, mass and acc must not be NULL");
+    if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
+    if (!(std::isfinite(eps) && eps > 0.0f)) return fail(ORR_ERR_RANGE, "eps must be finite and > 0 (got %g)", eps);
+    hipError_t e = launch_direct(pos, mass, n, eps * eps, acc, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "direct sum");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
 orr_status orr_selftest_inv_sqrt(uint32_t first_bits, uint32_t last_bits, uint64_t *mismatches,
                                  uint32_t *examples, void *hip_stream) {
     ORR_GUARD_BEGIN

@@ -113,6 +113,7 @@ hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float thet
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
                                     uint32_t *examples, hipStream_t s);
 bool walk_uses_fast_inv(float eps2);
+hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, float *acc, hipStream_t s);
 uint32_t morton_hist_blocks(int64_t n);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

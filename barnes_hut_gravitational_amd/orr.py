@@ -20,7 +20,8 @@ ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_
 TRAVERSALS = {"independent": 0, "coherent": 1}
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_eval_forces",
-            "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_selftest_inv_sqrt", "orr_tree_free")
+            "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
+            "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -69,11 +70,12 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
         L.orr_tree_check.argtypes = [_vp]
         L.orr_tree_export.argtypes = [_vp] * 9
+        L.orr_direct_forces.argtypes = [_vp, _vp, i64, f32, _vp, _vp]
         L.orr_selftest_inv_sqrt.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp]
         L.orr_tree_free.argtypes = [_vp]
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_eval_forces", "orr_tree_info_get", "orr_tree_check",
-                     "orr_tree_export", "orr_selftest_inv_sqrt"):
+                     "orr_tree_export", "orr_direct_forces", "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,6 +150,16 @@ def orr_eval_forces(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="c
                                _stream(pos.device), ctypes.byref(tm) if tm is not None else None)
     _check(st)
     return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
+
+
+def orr_direct_forces(pos, mass, *, eps=0.05, out=None) -> torch.Tensor:
+    """All-pairs float32 direct sum with the walk's term (orr_direct_forces);
+    returns acc [n, 3] in caller order."""
+    pos, mass = _as_inputs(pos, mass)
+    n = pos.shape[0]
+    acc = out if out is not None else torch.empty((n, 3), dtype=torch.float32, device=pos.device)
+    _check(lib().orr_direct_forces(_ptr(pos), _ptr(mass), n, eps, _ptr(acc), _stream(pos.device)))
+    return acc
 
 
 def orr_selftest_inv_sqrt(first_bits: int, last_bits: int, device="cuda"):

@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-trials", type=int, default=5,
                     help="whole oracle evaluations timed for the CPU baseline (median)")
+    ap.add_argument("--no-direct", action="store_true",
+                    help="skip the all-pairs direct-sum leg (Plummer 131,072)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -55,15 +57,44 @@ def walk_traffic_bytes():
 
     root = os.path.dirname(os.path.abspath(__file__))
     prof = os.path.join(root, "profiles", "k_walk_coherent_plummer_1m.md")
-    src = os.path.join(root, "barnes_hut_gravitational_amd", "csrc", "walk.hip")
+    csrc = os.path.join(root, "barnes_hut_gravitational_amd", "csrc")
     try:
         fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines()[:5] if ": " in l)
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for name in ("walk.hip", "term.h"):  # the walk kernel and the term it inlines
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        digest = h.hexdigest()[:16]
         if fields.get("walk-source-sha256-16", "").strip() == digest:
             return int(fields["traffic-bytes-per-launch"])
     except (OSError, KeyError, ValueError):
         pass
     return None
+
+
+def direct_leg(dev, stream, trials=5):
+    """The all-pairs direct sum (orr_direct_forces) with the walk's term on the
+    Plummer sphere of 131,072 particles: every lane does useful work on every
+    term, so this is the issue-bound rate of the exact term itself."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs, orr
+
+    pos_np, mass_np = inputs.make_config("plummer_131k")
+    P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
+    acc = torch.empty((len(mass_np), 3), dtype=torch.float32, device=dev)
+    orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+    ev[0].record(stream)
+    for k in range(trials):
+        orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    t = percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5)
+    n = len(mass_np)
+    inter = n * (n - 1)
+    achieved = FLOPS_PER_INTERACTION * inter / (t * 1e-3) / 1e12
+    return {"workload": "plummer_131k", "kernel": "k_direct", "ms_median": t, "interactions": inter,
+            "interactions_per_s": inter / (t * 1e-3), "achieved": achieved, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS}
 
 
 def cpu_baseline(pos, mass, trials):
@@ -157,6 +188,7 @@ def main():
         walk_ms[tr] = [wev[k].elapsed_time(wev[k + 1]) for k in range(args.steps)]
     phases = orr.orr_eval_forces(pos, mass, traversal="coherent", timings=True, **kw).timings
     info = tree.info()
+    direct = None if args.no_direct else direct_leg(dev, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -191,6 +223,7 @@ def main():
         "redundancy": visits_stepped / visits_own,
         "phases_ms": phases,
         "tree": {"n_nodes": info["n_nodes"], "depth": info["depth"], "n_leaves": info["n_leaves"]},
+        "direct": direct,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -182,6 +182,18 @@ orr_status orr_tree_check(const orr_tree *tree);
 orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t *perm, uint8_t *level,
                            uint32_t *begin, uint32_t *count, uint32_t *escape, float *geom, float *s2);
 
+/* All-pairs float32 direct sum, the reference the tree is measured against
+ * (the direct solver of the orrery performance page, "Against the two solvers
+ * it has to beat"): for every particle i, acc[i] = sum over j = 0..n-1 in
+ * index order of the walk's softened term m_j d (|d|^2 + eps^2)^(-3/2),
+ * d = x_j - x_i, each step one correctly rounded float32 operation (the
+ * particle's own term is +0). O(n^2) work. pos [n][3], mass [n], acc [n][3]:
+ * device pointers, caller-owned; enqueued on hip_stream; no workspace.
+ * Errors: ORR_ERR_INVALID_ARG (null pointer), ORR_ERR_RANGE (n < 1 or
+ * n > ORR_MAX_N, eps not finite and > 0), ORR_ERR_HIP. */
+orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, float eps, float *acc,
+                             void *hip_stream);
+
 /* Self-check of the walk's inverse square root. For eps >= 2^-48 the walk
  * evaluates RN(1/RN(sqrt(r2))) with a shorter instruction sequence valid for
  * r2 >= 2^-96 (every r2 >= eps^2 there); this enqueues a comparison of that

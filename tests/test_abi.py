@@ -93,6 +93,18 @@ def test_build_and_walk_argument_errors():
     L.orr_tree_free(None)
 
 
+@pytest.mark.parametrize("args,status", [
+    ((None, 1, 100, 0.05, 1), orr.ORR_ERR_INVALID_ARG), ((1, None, 100, 0.05, 1), orr.ORR_ERR_INVALID_ARG),
+    ((1, 1, 100, 0.05, None), orr.ORR_ERR_INVALID_ARG), ((1, 1, 0, 0.05, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 2**31, 0.05, 1), orr.ORR_ERR_RANGE), ((1, 1, 100, 0.0, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 100, float("nan"), 1), orr.ORR_ERR_RANGE), ((1, 1, 100, float("inf"), 1), orr.ORR_ERR_RANGE)])
+def test_direct_argument_errors(args, status):
+    L = orr.lib()
+    pos, mass, n, eps, acc = args
+    assert L.orr_direct_forces(pos, mass, n, eps, acc, None) == status
+    assert L.orr_last_error().decode()
+
+
 def test_binding_rejects_host_tensors():
     import torch
 
