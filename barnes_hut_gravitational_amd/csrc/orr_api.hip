@@ -255,6 +255,23 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
     ORR_GUARD_END
 }
 
+orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, int32_t group_width,
+                                 float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                 uint32_t *n_pc) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    orr_status st = check_walk_args(eps, theta, ORR_TRAVERSAL_COHERENT);
+    if (st != ORR_OK) return st;
+    if (group_width < 1 || group_width > 64 || (group_width & (group_width - 1)) != 0)
+        return fail(ORR_ERR_RANGE, "group_width %d is not a power of two in [1, 64]", group_width);
+    hipError_t e = launch_walk_grouped(tree->ws, group_width, eps * eps, theta * theta, acc, visits_own,
+                                       visits_stepped, n_pp, n_pc, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped walk");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
 orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float eps, float theta,
                            int32_t leaf_cap, orr_traversal traversal, float *acc, uint32_t *visits_own,
                            uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *workspace,

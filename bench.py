@@ -37,6 +37,8 @@ def parse():
                     help="whole oracle evaluations timed for the CPU baseline (median)")
     ap.add_argument("--no-direct", action="store_true",
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
+    ap.add_argument("--no-width-sweep", action="store_true",
+                    help="skip the group-width sweep of the walk (orr_tree_walk_grouped)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -95,6 +97,28 @@ def direct_leg(dev, stream, trials=5):
     return {"workload": "plummer_131k", "kernel": "k_direct", "ms_median": t, "interactions": inter,
             "interactions_per_s": inter / (t * 1e-3), "achieved": achieved, "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_TFLOPS}
+
+
+def width_sweep(tree, acc, cnt, stream, trials=4):
+    """Walk time and stepped visits per target for groups of W targets sharing
+    a node index (orr_tree_walk_grouped, vector loads), W = 1 .. 64, on the
+    benchmark's tree: the sub-group width question of the orrery pages."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs
+
+    out = {}
+    for w in (1, 2, 4, 8, 16, 32, 64):
+        tree.walk_grouped(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        ev[0].record(stream)
+        for k in range(trials):
+            tree.walk_grouped(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        stepped = cnt[1].to(torch.int64).sum().item() / cnt[1].numel()
+        out[str(w)] = {"walk_ms_median": percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5),
+                       "visits_stepped_per_particle": stepped}
+    return out
 
 
 def cpu_baseline(pos, mass, trials):
@@ -189,6 +213,7 @@ def main():
     phases = orr.orr_eval_forces(pos, mass, traversal="coherent", timings=True, **kw).timings
     info = tree.info()
     direct = None if args.no_direct else direct_leg(dev, stream)
+    widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -224,6 +249,7 @@ def main():
         "phases_ms": phases,
         "tree": {"n_nodes": info["n_nodes"], "depth": info["depth"], "n_leaves": info["n_leaves"]},
         "direct": direct,
+        "width_sweep": widths,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

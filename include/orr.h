@@ -157,6 +157,19 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
                          float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                          uint32_t *n_pc);
 
+/* The walk with groups of group_width consecutive sorted targets (1, 2, 4,
+ * ..., 64) sharing one node index: the sub-group coherence of the solver page
+ * at any width (the performance page's "The sub-group width" compares 16 and
+ * 32). A group steps through the union of its members' walks; node records
+ * and leaf particles come through per-lane loads. group_width = 1 is the
+ * independent walk. acc, visits_own, n_pp and n_pc are those of
+ * orr_tree_walk (identical for every width); visits_stepped = size of the
+ * union over the target's group. Errors: those of orr_tree_walk, and
+ * ORR_ERR_RANGE for a group_width that is not a power of two in [1, 64]. */
+orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, int32_t group_width,
+                                 float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                 uint32_t *n_pc);
+
 /* Build and walk in one call. If timings is not NULL, every phase is timed
  * with HIP events, the stream is synchronised and the input status checked
  * (ORR_ERR_NONFINITE possible). Errors: those of orr_build_tree and

@@ -85,6 +85,7 @@ def test_build_and_walk_argument_errors():
     assert L.orr_build_tree(1, 1, 0, 32, 256, 1 << 30, None, ctypes.byref(h)) == orr.ORR_ERR_RANGE
     assert h.value is None
     assert L.orr_tree_walk(None, 0.05, 0.5, 1, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_walk_grouped(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_check(None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_export(None, None, None, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG

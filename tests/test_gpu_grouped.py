@@ -1,0 +1,83 @@
+"""GPU parity of the grouped walk (orr_tree_walk_grouped): groups of W
+consecutive sorted targets share a node index, W = 1, 2, ..., 64 (the
+sub-group width of the orrery pages). Each target still sums exactly its own
+walk, so accelerations and own counts must equal the oracle's bit for bit at
+every width, and visits_stepped must equal the size of the union of the
+group's walks, computed by the oracle for the same grouping."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from barnes_hut_gravitational_amd import inputs, orr
+
+from parity import to_dev, u32
+
+pytestmark = pytest.mark.gpu
+EPS, THETA = inputs.EPS, inputs.THETA
+WIDTHS = (1, 2, 4, 8, 16, 32, 64)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    orr.lib()
+
+
+def union_caller_order(ot, width, eps, theta):
+    u = oracle.union_visits(ot, eps, theta, width)
+    out = np.empty(ot.n, np.uint32)
+    out[ot.perm] = np.repeat(u, width)[:ot.n]
+    return out
+
+
+def check_grouped(pos, mass, cap, widths, theta=THETA):
+    ref = oracle.evaluate(pos, mass, EPS, theta, cap)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, cap)
+    for w in widths:
+        print(f"[case] grouped n={len(mass)} cap={cap} width={w}", flush=True)
+        r = tree.walk_grouped(EPS, theta, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.acc.cpu().numpy().view(np.uint32), ref.acc.view(np.uint32))
+        assert np.array_equal(u32(r.visits_own), ref.visits_own)
+        assert np.array_equal(u32(r.n_pp), ref.n_pp)
+        assert np.array_equal(u32(r.n_pc), ref.n_pc)
+        assert np.array_equal(u32(r.visits_stepped), union_caller_order(ref.tree, w, EPS, theta))
+    return tree
+
+
+@pytest.mark.parametrize("kind,n,cap", [("plummer", 3000, 16), ("merger", 2000, 32), ("uniform", 4097, 32),
+                                        ("plummer", 33, 8), ("plummer", 1, 32)])
+def test_grouped_small_every_width(kind, n, cap):
+    pos, mass = inputs.make(kind, n)
+    check_grouped(pos, mass, cap, WIDTHS)
+
+
+def test_grouped_plummer_131k():
+    pos, mass = inputs.make_config("plummer_131k")
+    check_grouped(pos, mass, inputs.LEAF_CAP, (8, 32))
+
+
+def test_grouped_width_one_is_independent_and_64_is_coherent():
+    pos, mass = inputs.make("plummer", 5000)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, 32)
+    g1, g64 = tree.walk_grouped(EPS, THETA, 1), tree.walk_grouped(EPS, THETA, 64)
+    ind, coh = tree.walk(EPS, THETA, "independent"), tree.walk(EPS, THETA, "coherent")
+    torch.cuda.synchronize()
+    assert torch.equal(g1.visits_stepped, ind.visits_stepped)
+    assert torch.equal(g64.visits_stepped, coh.visits_stepped)
+    for a in (g1, g64, ind):
+        assert torch.equal(a.acc.view(torch.int32), coh.acc.view(torch.int32))
+
+
+def test_grouped_rejects_bad_widths():
+    pos, mass = inputs.make("plummer", 100)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, 32)
+    for w in (0, 3, 48, 128, -4):
+        with pytest.raises(orr.OrrError) as e:
+            tree.walk_grouped(EPS, THETA, w)
+        assert e.value.status == orr.ORR_ERR_RANGE
