@@ -72,6 +72,9 @@ def lib():
         L.oracle_direct_fp64.argtypes = [_f32p, _f32p, _i64, ctypes.c_double, _i64p, _i64, _f64p]
         L.oracle_direct_fp64.restype = None
         L.oracle_direct_fp32.argtypes = [_f32p, _f32p, _i64, _f32, _i64p, _i64, _f32p]
+        L.oracle_walk_descend.argtypes = [_f32p, _i64, _f32p, _f32p, _u32p, _u32p, _u32p, _i64, _f32, _f32, _i64,
+                                          _f32p, _u32p, _u32p, _u32p, _u32p]
+        L.oracle_walk_descend.restype = ctypes.c_int
         L.oracle_direct_fp32.restype = None
         _lib = L
     return _lib
@@ -209,6 +212,21 @@ def walk(t: Tree, eps, theta, targets=None):
     vis = np.empty(m, np.uint32)
     lib().oracle_walk(*_walk_args(t, eps, theta), tp, m, acc.reshape(-1), pp, pc, vis)
     return acc, pp, pc, vis
+
+
+def walk_descend(t: Tree, eps, theta, width):
+    """The descend-together group walk (ADR-0029, Alternatives considered):
+    groups of `width` consecutive sorted targets open a node when any member
+    would. Returns sorted-order (acc [n,3] f32, pp, pc, visits, covered)."""
+    n = t.n
+    acc = np.empty((n, 3), np.float32)
+    pp, pc, vis, cov = (np.empty(n, np.uint32) for _ in range(4))
+    st = lib().oracle_walk_descend(t.xs.reshape(-1), n, t.geom.reshape(-1), t.s2, t.begin, t.count, t.escape,
+                                   t.n_nodes, _f32(eps), _f32(theta), int(width), acc.reshape(-1), pp, pc, vis,
+                                   cov)
+    if st != 0:
+        raise OracleError(st, "walk_descend")
+    return acc, pp, pc, vis, cov
 
 
 def walk_trace(t: Tree, eps, theta, target):

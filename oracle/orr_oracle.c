@@ -460,9 +460,86 @@ int oracle_group_walk(const float *xs, int64_t n, const float *geom, const float
 }
 
 /* ------------------------------------------------------------------------ */
-/* Accuracy reference ([PERF] "Accuracy"): the same softened force law       */
-/* summed directly over all pairs in double precision, with Neumaier         */
-/* compensation, for the listed targets (caller order). j = i is skipped.    */
+/* The alternative [ADR29] rejects ("Alternatives considered": descend       */
+/* wherever any lane must, and let the accepting lanes descend too), which   */
+/* is the published warp-coherent traversal. Groups of `width` consecutive   */
+/* sorted targets share one node c. Every member applies the opening test at */
+/* c. If at least one member would open c, the whole group opens it: at a    */
+/* leaf every member adds the leaf's particles in sorted order, and at an    */
+/* internal node the group moves to c + 1 without terms. If no member would  */
+/* open c, every member adds c's monopole term and the group moves to        */
+/* escape[c]. Terms use add_term, in visit order. Per sorted target:         */
+/* acc, pp (particle terms, self excluded), pc (accepted cells), visits      */
+/* (nodes the group stepped through; the target acts at each), covered       */
+/* (particles accounted for: counts of its accepted cells plus the counts of */
+/* its opened leaves, which is n when every particle is summed once).        */
+/* ------------------------------------------------------------------------ */
+int oracle_walk_descend(const float *xs, int64_t n, const float *geom, const float *s2, const uint32_t *begin,
+                        const uint32_t *count, const uint32_t *escape, int64_t n_nodes, float eps, float theta,
+                        int64_t width, float *acc, uint32_t *pp, uint32_t *pc, uint32_t *visits,
+                        uint32_t *covered) {
+    const float eps2 = eps * eps, theta2 = theta * theta;
+    const int64_t groups = (n + width - 1) / width;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float *d = (float *)malloc((size_t)width * 4 * sizeof(float));
+        if (!d) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t g = 0; g < groups; g++) {
+                const int64_t lo = g * width, hi = (g + 1) * width < n ? (g + 1) * width : n;
+                for (int64_t i = lo; i < hi; i++) {
+                    acc[3 * i] = acc[3 * i + 1] = acc[3 * i + 2] = 0.0f;
+                    pp[i] = pc[i] = visits[i] = covered[i] = 0;
+                }
+                int64_t c = 0;
+                while (c < n_nodes) {
+                    const float *gm = geom + 4 * c;
+                    int any_open = 0;
+                    for (int64_t i = lo; i < hi; i++) {
+                        const float *xi = xs + 4 * (size_t)i;
+                        float *di = d + 4 * (i - lo);
+                        di[0] = gm[0] - xi[0];
+                        di[1] = gm[1] - xi[1];
+                        di[2] = gm[2] - xi[2];
+                        di[3] = (di[0] * di[0] + di[1] * di[1]) + di[2] * di[2];
+                        if (!(s2[c] < theta2 * di[3])) any_open = 1;
+                        visits[i] += 1;
+                    }
+                    if (any_open) {
+                        if (escape[c] == (uint32_t)(c + 1)) {
+                            const uint32_t b = begin[c], e = begin[c] + count[c];
+                            for (int64_t i = lo; i < hi; i++) {
+                                const float *xi = xs + 4 * (size_t)i;
+                                for (uint32_t j = b; j < e; j++) {
+                                    const float *p = xs + 4 * (size_t)j;
+                                    add_term(p[3], p[0] - xi[0], p[1] - xi[1], p[2] - xi[2], eps2, acc + 3 * i);
+                                }
+                                pp[i] += count[c] - ((i >= b && i < e) ? 1u : 0u);
+                                covered[i] += count[c];
+                            }
+                        }
+                        c = c + 1;
+                    } else {
+                        for (int64_t i = lo; i < hi; i++) {
+                            const float *di = d + 4 * (i - lo);
+                            add_term(gm[3], di[0], di[1], di[2], eps2, acc + 3 * i);
+                            pc[i] += 1;
+                            covered[i] += count[c];
+                        }
+                        c = (int64_t)escape[c];
+                    }
+                }
+            }
+        }
+        free(d);
+    }
+    return failed ? ORACLE_NOMEM : ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Float32 direct sum, the all-pairs reference (the direct solver of the     */
 /* orrery pages, "Against the two solvers it has to beat"): for each listed  */
@@ -486,6 +563,10 @@ void oracle_direct_fp32(const float *pos, const float *mass, int64_t n, float ep
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Accuracy reference ([PERF] "Accuracy"): the same softened force law       */
+/* summed directly over all pairs in double precision, with Neumaier         */
+/* compensation, for the listed targets (caller order). j = i is skipped.    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     double s, c;
