@@ -255,9 +255,9 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
     ORR_GUARD_END
 }
 
-orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, int32_t group_width,
-                                 float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
-                                 uint32_t *n_pc) {
+static orr_status walk_grouped_entry(const orr_tree *tree, float eps, float theta, int32_t group_width,
+                                     bool descend, float *acc, uint32_t *visits_own,
+                                     uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
     ORR_GUARD_BEGIN
     g_last_error.clear();
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
@@ -265,11 +265,23 @@ orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, i
     if (st != ORR_OK) return st;
     if (group_width < 1 || group_width > 64 || (group_width & (group_width - 1)) != 0)
         return fail(ORR_ERR_RANGE, "group_width %d is not a power of two in [1, 64]", group_width);
-    hipError_t e = launch_walk_grouped(tree->ws, group_width, eps * eps, theta * theta, acc, visits_own,
+    hipError_t e = launch_walk_grouped(tree->ws, group_width, descend, eps * eps, theta * theta, acc, visits_own,
                                        visits_stepped, n_pp, n_pc, tree->stream);
-    if (e != hipSuccess) return hip_fail(e, "grouped walk");
+    if (e != hipSuccess) return hip_fail(e, descend ? "descend-together walk" : "grouped walk");
     return ORR_OK;
     ORR_GUARD_END
+}
+
+orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, int32_t group_width,
+                                 float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                 uint32_t *n_pc) {
+    return walk_grouped_entry(tree, eps, theta, group_width, false, acc, visits_own, visits_stepped, n_pp, n_pc);
+}
+
+orr_status orr_tree_walk_descend(const orr_tree *tree, float eps, float theta, int32_t group_width, float *acc,
+                                 uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                 uint32_t *n_pc) {
+    return walk_grouped_entry(tree, eps, theta, group_width, true, acc, visits_own, visits_stepped, n_pp, n_pc);
 }
 
 orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float eps, float theta,

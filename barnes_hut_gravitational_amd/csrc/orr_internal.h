@@ -110,8 +110,9 @@ hipError_t launch_tree_info(const Workspace &ws, hipStream_t s);
 hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s);
-// Group widths 1, 2, 4, ..., 64 (hipErrorInvalidValue otherwise).
-hipError_t launch_walk_grouped(const Workspace &ws, int width, float eps2, float theta2, float *acc,
+// Group widths 1, 2, 4, ..., 64 (hipErrorInvalidValue otherwise); descend:
+// the descend-together variant.
+hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, float eps2, float theta2, float *acc,
                                uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                                hipStream_t s);
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,

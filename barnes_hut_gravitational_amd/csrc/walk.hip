@@ -360,7 +360,11 @@ __device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, 
 // read the same addresses). kW = 1 is the independent walk; kW = 64 is the
 // coherent walk with vector instead of scalar loads. The sums and all counts
 // except visits_stepped are the same for every width.
-template <uint32_t kW, int kInv>
+// kDescend: the alternative ADR-0029 rejects ("Alternatives considered"),
+// the published warp-coherent traversal: the group opens a node when any
+// member would and every member descends with it, so a target's sum depends
+// on its group; every member acts at every node the group visits.
+template <uint32_t kW, bool kDescend, int kInv>
 __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                              const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
                                              uint32_t n_nodes, float eps2, float theta2, const WalkOut &out) {
@@ -378,10 +382,37 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
             steps += 1;
             const NodeRec nd = nodes[c];
             const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
-            const bool active = next == c;
             const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
             const float d2 = (dx * dx + dy * dy) + dz * dz;
             const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
+            if (kDescend) {
+                // The group opens c if any member with a target would; then
+                // every member descends (at a leaf, sums its particles),
+                // else every member adds c's term and the group skips c.
+                const uint64_t opening = __builtin_amdgcn_ballot_w64(valid && !far);
+                if ((opening >> first) & gmask) {
+                    if (valid) {
+                        nopen += 1;
+                        if (esc == c + 1) {
+                            const uint32_t b = nd.t.y, cnt = nd.t.z;
+                            for (uint32_t j = b; j < b + cnt; j++) {
+                                const float4 p = xs[j];
+                                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                            }
+                            pp += cnt - ((i - b) < cnt ? 1u : 0u);
+                        }
+                    }
+                    c = c + 1;
+                } else {
+                    if (valid) {
+                        add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
+                        pc += 1;
+                    }
+                    c = esc;
+                }
+                continue;
+            }
+            const bool active = next == c;
             if (active && far) {  // accept: monopole term, then wait for the escape
                 add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
                 pc += 1;
@@ -411,7 +442,7 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
-template <uint32_t kW, bool kFastInv>
+template <uint32_t kW, bool kDescend, bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__restrict__ xs,
                                                              const NodeRec *__restrict__ nodes,
                                                              const DevParams *__restrict__ prm,
@@ -421,11 +452,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__res
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
-        walk_grouped<kW, kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_grouped<kW, kDescend, kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
     else if (r2_cannot_overflow(prm, eps2))
-        walk_grouped<kW, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_grouped<kW, kDescend, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
     else
-        walk_grouped<kW, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_grouped<kW, kDescend, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
 }
 
 template <bool kFastInv>
@@ -489,7 +520,7 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
 // The fast inverse square root applies when every r^2 >= eps^2 is >= 2^-96.
 bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
 
-template <bool kFast>
+template <bool kDescend, bool kFast>
 hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, float theta2, const WalkOut &out,
                                  hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
@@ -497,8 +528,8 @@ hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, flo
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
 #define ORR_GROUPED(W)                                                                                    \
     case W:                                                                                               \
-        k_walk_grouped<W, kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2, \
-                                                               theta2, out);                              \
+        k_walk_grouped<W, kDescend, kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
+                                                                         eps2, theta2, out);              \
         break;
     switch (width) {
         ORR_GROUPED(1)
@@ -515,12 +546,16 @@ hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, flo
     return hipGetLastError();
 }
 
-hipError_t launch_walk_grouped(const Workspace &ws, int width, float eps2, float theta2, float *acc,
+hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, float eps2, float theta2, float *acc,
                                uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                                hipStream_t s) {
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    if (walk_uses_fast_inv(eps2)) return launch_walk_grouped_t<true>(ws, width, eps2, theta2, out, s);
-    return launch_walk_grouped_t<false>(ws, width, eps2, theta2, out, s);
+    const bool fast = walk_uses_fast_inv(eps2);
+    if (descend)
+        return fast ? launch_walk_grouped_t<true, true>(ws, width, eps2, theta2, out, s)
+                    : launch_walk_grouped_t<true, false>(ws, width, eps2, theta2, out, s);
+    return fast ? launch_walk_grouped_t<false, true>(ws, width, eps2, theta2, out, s)
+                : launch_walk_grouped_t<false, false>(ws, width, eps2, theta2, out, s);
 }
 
 hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,

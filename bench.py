@@ -121,6 +121,28 @@ def width_sweep(tree, acc, cnt, stream, trials=4):
     return out
 
 
+def descend_leg(tree, acc, cnt, stream, trials=4):
+    """The descend-together group walk (orr_tree_walk_descend: a group opens a
+    node when any member would, all members descending), for comparison with
+    the masked walk at the same group width."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs
+
+    out = {}
+    for w in (32, 64):
+        tree.walk_descend(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        ev[0].record(stream)
+        for k in range(trials):
+            tree.walk_descend(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        inter = int(cnt[2].long().sum().item() + cnt[3].long().sum().item())
+        out[str(w)] = {"walk_ms_median": percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5),
+                       "interactions": inter}
+    return out
+
+
 def cpu_baseline(pos, mass, trials):
     """The oracle as it stands, on this host's cores: whole evaluations of the
     workload (build, walk of every target, group union visits), median."""
@@ -214,6 +236,7 @@ def main():
     info = tree.info()
     direct = None if args.no_direct else direct_leg(dev, stream)
     widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
+    descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -250,6 +273,7 @@ def main():
         "tree": {"n_nodes": info["n_nodes"], "depth": info["depth"], "n_leaves": info["n_leaves"]},
         "direct": direct,
         "width_sweep": widths,
+        "descend_together": descend,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -170,6 +170,19 @@ orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, i
                                  float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                                  uint32_t *n_pc);
 
+/* The alternative ADR-0029 rejects ("Alternatives considered"), the
+ * published warp-coherent traversal, for comparison: groups of group_width
+ * consecutive sorted targets (1, 2, 4, ..., 64) share one node; the group
+ * opens a node when any member would, every member descending with it (at a
+ * leaf, summing its particles), and otherwise every member adds the node's
+ * term and the group skips the subtree. A target's sum then depends on its
+ * group; group_width = 1 gives the walk of orr_tree_walk. Outputs as in
+ * orr_tree_walk, with n_pp and n_pc of this walk and visits_own =
+ * visits_stepped = nodes the group visited. Errors: as orr_tree_walk_grouped. */
+orr_status orr_tree_walk_descend(const orr_tree *tree, float eps, float theta, int32_t group_width, float *acc,
+                                 uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                 uint32_t *n_pc);
+
 /* Build and walk in one call. If timings is not NULL, every phase is timed
  * with HIP events, the stream is synchronised and the input status checked
  * (ORR_ERR_NONFINITE possible). Errors: those of orr_build_tree and

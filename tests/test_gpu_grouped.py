@@ -81,3 +81,49 @@ def test_grouped_rejects_bad_widths():
         with pytest.raises(orr.OrrError) as e:
             tree.walk_grouped(EPS, THETA, w)
         assert e.value.status == orr.ORR_ERR_RANGE
+
+
+def to_caller(ot, a):
+    out = np.empty_like(a)
+    out[ot.perm] = a
+    return out
+
+
+def check_descend(pos, mass, cap, widths, theta=THETA):
+    ot = oracle.build_tree(pos, mass, cap)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, cap)
+    for w in widths:
+        print(f"[case] descend-together n={len(mass)} cap={cap} width={w}", flush=True)
+        acc, pp, pc, vis, cov = oracle.walk_descend(ot, EPS, theta, w)
+        assert np.all(cov == ot.n)
+        r = tree.walk_descend(EPS, theta, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.acc.cpu().numpy().view(np.uint32), to_caller(ot, acc).view(np.uint32))
+        assert np.array_equal(u32(r.n_pp), to_caller(ot, pp))
+        assert np.array_equal(u32(r.n_pc), to_caller(ot, pc))
+        assert np.array_equal(u32(r.visits_own), to_caller(ot, vis))
+        assert np.array_equal(u32(r.visits_stepped), to_caller(ot, vis))
+
+
+@pytest.mark.parametrize("kind,n,cap", [("plummer", 3000, 16), ("merger", 2001, 32), ("uniform", 700, 8),
+                                        ("plummer", 1, 32)])
+def test_descend_small(kind, n, cap):
+    pos, mass = inputs.make(kind, n)
+    check_descend(pos, mass, cap, WIDTHS)
+
+
+def test_descend_plummer_131k():
+    pos, mass = inputs.make_config("plummer_131k")
+    check_descend(pos, mass, inputs.LEAF_CAP, (32, 64))
+
+
+def test_descend_width_one_is_the_masked_walk():
+    pos, mass = inputs.make("merger", 4000)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, 32)
+    d, m = tree.walk_descend(EPS, THETA, 1), tree.walk(EPS, THETA, "coherent")
+    torch.cuda.synchronize()
+    assert torch.equal(d.acc.view(torch.int32), m.acc.view(torch.int32))
+    for f in ("visits_own", "n_pp", "n_pc"):
+        assert torch.equal(getattr(d, f), getattr(m, f))
