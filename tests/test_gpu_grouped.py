@@ -127,3 +127,28 @@ def test_descend_width_one_is_the_masked_walk():
     assert torch.equal(d.acc.view(torch.int32), m.acc.view(torch.int32))
     for f in ("visits_own", "n_pp", "n_pc"):
         assert torch.equal(getattr(d, f), getattr(m, f))
+
+
+def test_descend_more_accurate_but_group_dependent():
+    # The trade ADR-0029 describes: descending with the group sums more
+    # particles individually (smaller error against the float64 direct sum)
+    # but the result changes with the group width.
+    print("[case] descend-together accuracy, plummer_131k", flush=True)
+    pos, mass = inputs.make_config("plummer_131k")
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, inputs.LEAF_CAP)
+    rows = np.random.default_rng(3).choice(len(mass), 800, replace=False)
+    ref = oracle.direct_fp64(pos, mass, EPS, rows)
+
+    def rms(r):
+        a = r.acc.cpu().numpy()[rows].astype(np.float64)
+        e = np.linalg.norm(a - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        return float(np.sqrt(np.mean(e ** 2)))
+
+    masked = tree.walk(EPS, THETA, "coherent")
+    d64 = tree.walk_descend(EPS, THETA, 64)
+    d32 = tree.walk_descend(EPS, THETA, 32)
+    torch.cuda.synchronize()
+    print(f"rms masked {rms(masked):.3e} descend64 {rms(d64):.3e} descend32 {rms(d32):.3e}", flush=True)
+    assert rms(d64) < rms(masked)
+    assert not torch.equal(d64.acc.view(torch.int32), d32.acc.view(torch.int32))
