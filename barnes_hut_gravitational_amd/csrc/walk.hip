@@ -23,10 +23,8 @@
 // performance page's "Where one evaluation goes" table).
 #include "orr_internal.h"
 #include "term.h"
+#include "walk_common.h"
 
-#ifndef ORR_WALK_BLOCK
-#define ORR_WALK_BLOCK 256
-#endif
 #ifndef ORR_PACK_KMAX
 #define ORR_PACK_KMAX 8  // pack leaf rows when at most this many lanes open the leaf
 #endif
@@ -34,8 +32,6 @@
 namespace orr {
 
 namespace {
-
-constexpr uint32_t kWalkBlock = ORR_WALK_BLOCK;  // threads per block (multiple of 64)
 
 // Orders the wave's LDS accesses around a hand-over between lanes (LDS
 // requests of one wave are served in order; this keeps the compiler's order).
@@ -123,14 +119,6 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
     }
 }
 
-// Blocks are handed to the 8 XCDs round-robin; the independent walk gives
-// each XCD a contiguous run of target blocks, so that its L2 holds one region
-// of the tree for the per-lane node loads.
-__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nblocks) {
-    const uint32_t x = b & 7u, q = nblocks >> 3, r = nblocks & 7u;
-    return x * q + min(x, r) + (b >> 3);
-}
-
 // Sorted targets of this lane's wave: wave slot s of the grid runs target
 // wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
 // schedule get no targets.
@@ -138,31 +126,6 @@ __device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict_
     const uint32_t slot = blockIdx.x * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t w = slot < n_waves ? min(order[slot], n_waves) : n_waves;
     return w * 64u + (threadIdx.x & 63u);
-}
-
-struct WalkOut {
-    float *acc;
-    uint32_t *visits_own, *visits_stepped, *n_pp, *n_pc;
-};
-
-__device__ __forceinline__ void write_out(const WalkOut &o, uint32_t dst, float ax, float ay, float az,
-                                          uint32_t vown, uint32_t vstep, uint32_t pp, uint32_t pc) {
-    if (o.acc) {
-        o.acc[3ull * dst] = ax;
-        o.acc[3ull * dst + 1] = ay;
-        o.acc[3ull * dst + 2] = az;
-    }
-    if (o.visits_own) o.visits_own[dst] = vown;
-    if (o.visits_stepped) o.visits_stepped[dst] = vstep;
-    if (o.n_pp) o.n_pp[dst] = pp;
-    if (o.n_pc) o.n_pc[dst] = pc;
-}
-
-// r2 <= 3 (side (1 + 2^-20))^2 + eps2 for every pair inside the root cube,
-// coms included; below this bound no r2 can overflow float.
-__device__ __forceinline__ bool r2_cannot_overflow(const DevParams *prm, float eps2) {
-    const double s = (double)prm->side * (1.0 + 0x1p-20);
-    return 3.0 * s * s + (double)eps2 < 1e38;
 }
 
 // Wave-private LDS of the packed leaf evaluation.
@@ -350,115 +313,6 @@ __device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, 
     write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
 }
 
-// Walk of one target whose group of kW consecutive lanes (kW = 1..64, a
-// power of two) shares one node index: the sub-group of the solver page at
-// any width ("The sub-group width" of the performance page measures 16 and
-// 32 lanes). The group steps through the union of its members' walks with
-// the advance rule of the coherent walk applied to the group's lanes only.
-// The node index is a vector register, equal across the group; node records
-// and leaf particles come through per-lane vector loads (the lanes of a group
-// read the same addresses). kW = 1 is the independent walk; kW = 64 is the
-// coherent walk with vector instead of scalar loads. The sums and all counts
-// except visits_stepped are the same for every width.
-// kDescend: the alternative ADR-0029 rejects ("Alternatives considered"),
-// the published warp-coherent traversal: the group opens a node when any
-// member would and every member descends with it, so a target's sum depends
-// on its group; every member acts at every node the group visits.
-template <uint32_t kW, bool kDescend, int kInv>
-__device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
-                                             const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
-                                             uint32_t n_nodes, float eps2, float theta2, const WalkOut &out) {
-    static_assert(kW >= 1 && kW <= 64 && (kW & (kW - 1)) == 0, "group width");
-    const bool valid = i < n;
-    const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
-    float ax = 0.0f, ay = 0.0f, az = 0.0f;
-    uint32_t pp = 0, pc = 0, nopen = 0, steps = 0;
-    const uint32_t first = __lane_id() & ~(kW - 1);  // first lane of this lane's group
-    const uint64_t gmask = kW == 64 ? ~0ull : ((1ull << kW) - 1ull);
-    uint32_t c = 0;  // the group's node
-    while (__builtin_amdgcn_ballot_w64(c < n_nodes)) {
-        if (c < n_nodes) {
-            steps += 1;
-            const NodeRec nd = nodes[c];
-            const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
-            const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
-            const float d2 = (dx * dx + dy * dy) + dz * dz;
-            const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
-            if (kDescend) {
-                // The group opens c if any member with a target would; then
-                // every member descends (at a leaf, sums its particles),
-                // else every member adds c's term and the group skips c.
-                const uint64_t opening = __builtin_amdgcn_ballot_w64(valid && !far);
-                if ((opening >> first) & gmask) {
-                    if (valid) {
-                        nopen += 1;
-                        if (esc == c + 1) {
-                            const uint32_t b = nd.t.y, cnt = nd.t.z;
-                            for (uint32_t j = b; j < b + cnt; j++) {
-                                const float4 p = xs[j];
-                                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
-                            }
-                            pp += cnt - ((i - b) < cnt ? 1u : 0u);
-                        }
-                    }
-                    c = c + 1;
-                } else {
-                    if (valid) {
-                        add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
-                        pc += 1;
-                    }
-                    c = esc;
-                }
-                continue;
-            }
-            const bool active = next == c;
-            if (active && far) {  // accept: monopole term, then wait for the escape
-                add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
-                pc += 1;
-                next = esc;
-            }
-            if (active && !far) {
-                nopen += 1;
-                if (esc == c + 1) {  // an opened leaf: its particles in sorted order
-                    const uint32_t b = nd.t.y, cnt = nd.t.z;
-                    for (uint32_t j = b; j < b + cnt; j++) {
-                        const float4 p = xs[j];
-                        add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
-                    }
-                    pp += cnt - ((i - b) < cnt ? 1u : 0u);
-                    next = esc;
-                } else {
-                    next = c + 1;
-                }
-            }
-            // The smallest index a lane of the group wants: c + 1 if one of
-            // them opened an internal c (waiting lanes want at least the
-            // escape), else the escape, which is c + 1 for a leaf.
-            const uint64_t down = __builtin_amdgcn_ballot_w64(next == c + 1);
-            c = ((down >> first) & gmask) ? c + 1 : esc;
-        }
-    }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
-}
-
-template <uint32_t kW, bool kDescend, bool kFastInv>
-__global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__restrict__ xs,
-                                                             const NodeRec *__restrict__ nodes,
-                                                             const DevParams *__restrict__ prm,
-                                                             const uint32_t *__restrict__ perm, uint32_t n,
-                                                             uint32_t max_nodes, float eps2, float theta2,
-                                                             WalkOut out) {
-    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
-    const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
-    if (!kFastInv)
-        walk_grouped<kW, kDescend, kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
-    else if (r2_cannot_overflow(prm, eps2))
-        walk_grouped<kW, kDescend, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
-    else
-        walk_grouped<kW, kDescend, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
-}
-
 template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
                                                                  const NodeRec *__restrict__ nodes,
@@ -519,44 +373,6 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
 
 // The fast inverse square root applies when every r^2 >= eps^2 is >= 2^-96.
 bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
-
-template <bool kDescend, bool kFast>
-hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, float theta2, const WalkOut &out,
-                                 hipStream_t s) {
-    const uint32_t n = (uint32_t)ws.n;
-    const uint32_t nb = (uint32_t)ws.max_nodes;
-    const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
-#define ORR_GROUPED(W)                                                                                    \
-    case W:                                                                                               \
-        k_walk_grouped<W, kDescend, kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
-                                                                         eps2, theta2, out);              \
-        break;
-    switch (width) {
-        ORR_GROUPED(1)
-        ORR_GROUPED(2)
-        ORR_GROUPED(4)
-        ORR_GROUPED(8)
-        ORR_GROUPED(16)
-        ORR_GROUPED(32)
-        ORR_GROUPED(64)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef ORR_GROUPED
-    return hipGetLastError();
-}
-
-hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, float eps2, float theta2, float *acc,
-                               uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
-                               hipStream_t s) {
-    const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    const bool fast = walk_uses_fast_inv(eps2);
-    if (descend)
-        return fast ? launch_walk_grouped_t<true, true>(ws, width, eps2, theta2, out, s)
-                    : launch_walk_grouped_t<true, false>(ws, width, eps2, theta2, out, s);
-    return fast ? launch_walk_grouped_t<false, true>(ws, width, eps2, theta2, out, s)
-                : launch_walk_grouped_t<false, false>(ws, width, eps2, theta2, out, s);
-}
 
 hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
