@@ -1,12 +1,14 @@
 // The two tree walks (enum TreeTraversal of the orrery solver page).
 //
 // Coherent walk (solver page, "The mitigation"; ADR-0029, Decision): one
-// 64-lane wave walks one node index kept in a scalar register. Every lane
-// keeps `next`, the node its own walk wants; lanes with next == c act at c,
-// the others wait. The wave moves to the smallest `next` of its lanes, which
-// is c + 1 if an acting lane opened an internal node and escape[c] otherwise
-// (a lane waiting at c skipped an ancestor of c, so its next is at least
-// escape[c]); that is one ballot per node. Node records are wave-uniform and
+// 64-lane wave walks one node index kept in a scalar register. The wave moves
+// to the smallest node any lane's own walk wants: c + 1 if a lane opened c
+// and escape[c] otherwise (a lane waiting at c skipped an ancestor of c, so
+// it wants at least escape[c]). A lane that accepts c waits for escape[c]
+// (`next`); every other lane wants exactly the wave's next node, so `next`
+// changes only on acceptance and the lanes acting at c are those with
+// next <= c. The advance is one scalar select on the mask of opening lanes.
+// Node records are wave-uniform and
 // come through scalar loads. An opened leaf is read once for all its opening
 // lanes: its particles are staged in the wave's LDS with one coalesced load;
 // when few lanes open it, their terms are also packed across the wave's
@@ -152,44 +154,43 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         steps += 1;
         const NodeRec nd = nodes[c];  // one scalar load of 32 bytes
         const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
-        const bool active = next == c;
+        // A lane that did not accept at the wave's previous node wants exactly
+        // the node the wave visits next (it opened that node, so it wants the
+        // node after it, which is the smallest index any lane can want), so
+        // `next` only changes when a lane accepts a cell: it then waits for
+        // the escape. The lanes acting at c are those with next <= c.
+        const bool active = next <= c;
         const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
         const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
+        // Lanes opening c, from the two comparison masks.
+        const uint64_t m_open = __builtin_amdgcn_ballot_w64(active) &
+                                ~__builtin_amdgcn_fcmpf(__uint_as_float(nd.t.w), theta2 * d2, 4 /* ordered < */);
         // Divergent branches below are skipped when no lane takes them.
         if (active && far) {  // accept: monopole term, then wait for the escape
             add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
             pc += 1;
             next = esc;
         }
-        if (esc == c + 1) {  // leaf
-            const bool opening = active && !far;
-            const uint64_t m_open = __builtin_amdgcn_ballot_w64(opening);
-            if (m_open) {
+        const bool opening = active && !far;
+        if (opening) nopen += 1;
+        if (m_open) {
+            if (esc == c + 1) {  // a leaf that some lane opens
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
                 const uint32_t g = pack_width((uint32_t)__popcll(m_open), cnt);
                 if (g == 1) {
                     leaf_masked<kInv>(xs, b, cnt, opening, xi, eps2, ax, ay, az, lds.src[wv]);
                 } else {
-                    leaf_packed<kInv>(xs, b, cnt, g, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv],
-                                      lds.prod[wv]);
+                    leaf_packed<kInv>(xs, b, cnt, g, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv],
+                                      lds.src[wv], lds.prod[wv]);
                 }
-                if (opening) {
-                    pp += cnt - ((i - b) < cnt ? 1u : 0u);
-                    nopen += 1;
-                    next = esc;
-                }
+                if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
-            c = esc;
-        } else {
-            if (active && !far) {  // open an internal node: descend
-                nopen += 1;
-                next = c + 1;
-            }
-            // The smallest index any lane wants: c + 1 if some lane descended
-            // (only those lanes now want c + 1), else the escape.
-            c = __builtin_amdgcn_ballot_w64(next == c + 1) ? c + 1 : esc;
         }
+        // The smallest index any lane wants: c + 1 if some lane opened c (a
+        // waiting lane wants the escape of a skipped ancestor of c, at least
+        // escape[c]; for a leaf escape[c] = c + 1 anyway), else the escape.
+        c = m_open ? c + 1 : esc;
     }
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
