@@ -8,11 +8,11 @@
 // (`next`); every other lane wants exactly the wave's next node, so `next`
 // changes only on acceptance and the lanes acting at c are those with
 // next <= c. The advance is one scalar select on the mask of opening lanes.
-// Node records are wave-uniform and
-// come through scalar loads. An opened leaf is read once for all its opening
-// lanes: its particles are staged in the wave's LDS with one coalesced load;
-// when few lanes open it, their terms are also packed across the wave's
-// lanes. Target waves start in the order of a cost estimate (longest first).
+// Node records are wave-uniform and come through scalar loads. An opened leaf
+// is read once for all its opening lanes: its particles are staged in the
+// wave's LDS with one coalesced load; when few lanes open it, their terms are
+// also packed across the wave's lanes. Target waves start in the order of a
+// cost estimate (longest first).
 //
 // Independent walk (enum TreeTraversal, kIndependent): one lane per target,
 // each following its own node index with per-lane vector loads; the measured
