@@ -135,7 +135,7 @@ struct WalkLds {
     float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64];
 };
 
-template <int kInv>
+template <int kInv, bool kOff32>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
                                               uint32_t n_nodes, float eps2, float theta2, const WalkOut &out,
@@ -148,11 +148,15 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     // visits_own = accepted nodes + opened nodes, so no per-step counter
     uint32_t pp = 0, pc = 0, nopen = 0;
     uint32_t steps = 0;  // wave-uniform: visits_stepped
+    const char *node_bytes = reinterpret_cast<const char *>(nodes);
     uint32_t c = 0;
     while (c < n_nodes) {
         c = __builtin_amdgcn_readfirstlane(c);
         steps += 1;
-        const NodeRec nd = nodes[c];  // one scalar load of 32 bytes
+        // One scalar load of 32 bytes; kOff32: at a 32-bit byte offset from
+        // the array (the launch checks that 32 n_nodes fits), which saves the
+        // 64-bit address arithmetic of every step.
+        const NodeRec nd = kOff32 ? *reinterpret_cast<const NodeRec *>(node_bytes + (c << 5)) : nodes[c];
         const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
         // A lane that did not accept at the wave's previous node wants exactly
         // the node the wave visits next (it opened that node, so it wants the
@@ -167,8 +171,10 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         const uint64_t m_open = __builtin_amdgcn_ballot_w64(active) &
                                 ~__builtin_amdgcn_fcmpf(__uint_as_float(nd.t.w), theta2 * d2, 4 /* ordered < */);
         // Divergent branches below are skipped when no lane takes them.
+        float mass_c = nd.g.w;
+        __asm__ volatile("" : "+s"(mass_c));  // keeps the node mass in its register rather than loading it again
         if (active && far) {  // accept: monopole term, then wait for the escape
-            add_term_r2<kInv>(nd.g.w, dx, dy, dz, d2 + eps2, ax, ay, az);
+            add_term_r2<kInv>(mass_c, dx, dy, dz, d2 + eps2, ax, ay, az);
             pc += 1;
             next = esc;
         }
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t
     }
 }
 
-template <bool kFastInv>
+template <bool kFastInv, bool kOff32>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
@@ -274,11 +280,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
     const uint32_t i = scheduled_target(order, n_waves);
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
-        walk_coherent<kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvIeee, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else if (r2_cannot_overflow(prm, eps2))  // uniform
-        walk_coherent<kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvFastNoClamp, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else
-        walk_coherent<kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvFast, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
 }
 
 template <int kInv>
@@ -361,8 +367,12 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
     if (coherent) {
         k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
         k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
-        k_walk_coherent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, eps2,
-                                                             theta2, ws.wave_order, nw, out);
+        if ((uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull)
+            k_walk_coherent<kFast, true><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
+                                                                       eps2, theta2, ws.wave_order, nw, out);
+        else
+            k_walk_coherent<kFast, false><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
+                                                                        eps2, theta2, ws.wave_order, nw, out);
     } else {
         k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
                                                                 eps2, theta2, out);
