@@ -145,8 +145,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
     const uint32_t wv = threadIdx.x >> 6;
-    // visits_own = accepted nodes + opened nodes, so no per-step counter
-    uint32_t pp = 0, pc = 0, nopen = 0;
+    uint32_t pp = 0, pc = 0, vown = 0;
     uint32_t steps = 0;  // wave-uniform: visits_stepped
     const char *node_bytes = reinterpret_cast<const char *>(nodes);
     uint32_t c = 0;
@@ -179,7 +178,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
             next = esc;
         }
         const bool opening = active && !far;
-        if (opening) nopen += 1;
+        if (active) vown += 1;
         if (m_open) {
             if (esc == c + 1) {  // a leaf that some lane opens
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
@@ -198,7 +197,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         // escape[c]; for a leaf escape[c] = c + 1 anyway), else the escape.
         c = m_open ? c + 1 : esc;
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
+    if (valid) write_out(out, perm[i], ax, ay, az, vown, steps, pp, pc);
 }
 
 // Walk schedule. How long a wave runs grows with the particle density
