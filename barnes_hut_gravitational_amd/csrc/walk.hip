@@ -28,7 +28,7 @@
 #include "walk_common.h"
 
 #ifndef ORR_PACK_KMAX
-#define ORR_PACK_KMAX 8  // pack leaf rows when at most this many lanes open the leaf
+#define ORR_PACK_KMAX 64  // pack leaf rows when at most this many lanes open the leaf (64: always)
 #endif
 
 namespace orr {
@@ -43,11 +43,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Particles per row when k lanes open a leaf of cnt particles: the wave is
-// split into g slots of 64/g lanes (g = 1, 2, 4, 8), each slot one particle,
-// each lane of a slot one opening lane.
+// split into g slots of 64/g lanes (g = 64 / k rounded down to a power of
+// two), each slot one particle, each lane of a slot one opening lane; no
+// wider than the leaf needs. g = 1: no packing.
 __device__ __forceinline__ uint32_t pack_width(uint32_t k, uint32_t cnt) {
-    uint32_t g = k > ORR_PACK_KMAX ? 1u : k <= 8 ? 8u : k <= 16 ? 4u : k <= 32 ? 2u : 1u;
-    while (g > 1 && (g >> 1) >= cnt) g >>= 1;  // no wider than the leaf
+    if (k > ORR_PACK_KMAX) return 1u;
+    uint32_t g = 64u >> (32u - __clz(k - 1u));  // 64 / (k rounded up to a power of two); k >= 1
+    while (g > 1 && (g >> 1) >= cnt) g >>= 1;
     return g;
 }
 
@@ -81,36 +83,44 @@ __device__ __forceinline__ void leaf_masked(const float4 *__restrict__ xs, uint3
     }
 }
 
-// A leaf opened by the lanes of m_open, packed g > 1 particles per row: lane
-// (slot q, position r) computes the term of the row's particle q for the
-// r-th opening lane; each opening lane then adds its products in particle
-// order, so its sum is the one its own walk makes. Per wave LDS: tgt = the
-// opening lanes' positions, src = up to 64 of the leaf's particles, prod =
-// one row of products.
-template <int kInv>
-__device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint32_t g,
-                                            uint64_t m_open, bool opening, const float4 &xi, float eps2, float &ax,
-                                            float &ay, float &az, float4 *tgt, float4 *src, float4 *prod) {
+// A leaf opened by the lanes of m_open, packed kG > 1 particles per row:
+// lane (slot q, position r) computes the term product of the row's particle
+// q for the r-th opening lane; each opening lane then adds its kG products of
+// the row in particle order, so its sum is the one its own walk makes. Slots
+// past the leaf's end hold +0 products, and adding +0 leaves every
+// accumulator unchanged (an accumulator that starts at +0 never becomes -0
+// under round-to-nearest), so the rows need no tail test. Per wave LDS:
+// tgt = the opening lanes' positions, src = up to 64 of the leaf's particles,
+// prod = one row of products.
+template <int kInv, uint32_t kG>
+__device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint64_t m_open,
+                                            bool opening, const float4 &xi, float eps2, float &ax, float &ay,
+                                            float &az, float4 *tgt, float4 *src, float4 *prod) {
+    constexpr uint32_t kSlot = 64u / kG;  // lanes per slot: opening lanes served per particle
     const uint32_t lane = __lane_id();
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_open >> 32),
                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m_open, 0u));
     const uint32_t k = (uint32_t)__popcll(m_open);
-    const uint32_t lw = 6u - (31u - __clz(g));  // log2(64 / g)
-    const uint32_t q = lane >> lw, r = lane & ((1u << lw) - 1u);
+    const uint32_t q = lane / kSlot, r = lane % kSlot;
     if (opening) tgt[rank] = xi;
     for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
         const uint32_t cc = min(cnt - c0, 64u);
         if (lane < cc) src[lane] = xs[b + c0 + lane];
         wave_lds_sync();
-        for (uint32_t j0 = 0; j0 < cc; j0 += g) {
-            if (r < k && j0 + q < cc) {
-                const float4 p = src[j0 + q], t = tgt[r];
-                prod[lane] = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
+        for (uint32_t j0 = 0; j0 < cc; j0 += kG) {
+            if (r < k) {
+                float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (j0 + q < cc) {
+                    const float4 p = src[j0 + q], t = tgt[r];
+                    v = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
+                }
+                prod[lane] = v;
             }
             wave_lds_sync();
             if (opening) {
-                for (uint32_t qq = 0; qq < g && j0 + qq < cc; qq++) {
-                    const float4 v = prod[(qq << lw) + rank];
+#pragma unroll
+                for (uint32_t qq = 0; qq < kG; qq++) {
+                    const float4 v = prod[qq * kSlot + rank];
                     ax += v.x;
                     ay += v.y;
                     az += v.z;
@@ -186,8 +196,21 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
                 if (g == 1) {
                     leaf_masked<kInv>(xs, b, cnt, opening, xi, eps2, ax, ay, az, lds.src[wv]);
                 } else {
-                    leaf_packed<kInv>(xs, b, cnt, g, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv],
-                                      lds.src[wv], lds.prod[wv]);
+#define ORR_LEAF_PACKED(G)                                                                                 \
+    case G:                                                                                                \
+        leaf_packed<kInv, G>(xs, b, cnt, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv], \
+                             lds.prod[wv]);                                                                \
+        break;
+                    switch (g) {
+                        ORR_LEAF_PACKED(2)
+                        ORR_LEAF_PACKED(4)
+                        ORR_LEAF_PACKED(8)
+                        ORR_LEAF_PACKED(16)
+                        ORR_LEAF_PACKED(32)
+                        default:
+                            ORR_LEAF_PACKED(64)
+                    }
+#undef ORR_LEAF_PACKED
                 }
                 if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
