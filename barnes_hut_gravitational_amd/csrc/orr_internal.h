@@ -14,11 +14,11 @@ constexpr int kMaxLevel = 21;            // 21 bits per axis, 63-bit keys
 constexpr uint32_t kQMax = 2097151u;     // 2^21 - 1
 constexpr uint32_t kNoParent = 0xffffffffu;
 
-// Sort tiles: 256 threads x kTileItems keys.
+// Sort tiles: 512 threads x kTileItems keys.
 #ifndef ORR_SORT_ITEMS
-#define ORR_SORT_ITEMS 16
+#define ORR_SORT_ITEMS 8
 #endif
-constexpr int kTileThreads = 256;
+constexpr int kTileThreads = 512;
 constexpr int kTileItems = ORR_SORT_ITEMS;
 constexpr int kTile = kTileThreads * kTileItems;
 constexpr int kRadixBits = 8;

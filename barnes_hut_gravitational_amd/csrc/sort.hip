@@ -12,7 +12,7 @@
 //   * k_morton_hist computes every key once and the 8 digit histograms of all
 //     keys; k_digit_offsets turns them into the first output slot of each
 //     digit in each pass.
-//   * k_onesweep, one launch per pass: a tile of 4096 keys (256 threads x 16)
+//   * k_onesweep, one launch per pass: a tile of 4096 keys (512 threads x 8)
 //     takes a ticket (its position in the output), ranks its keys stably
 //     inside each wave (lanes with the same digit found with 8 ballots),
 //     publishes its digit counts, and adds the counts of the tiles before it
@@ -20,7 +20,9 @@
 //     until one carries an inclusive prefix. Tickets are taken in the order
 //     blocks start, so every predecessor is running or done and publishes its
 //     counts without waiting on anyone; each wait is nevertheless bounded and
-//     reports an error.
+//     reports an error. The tile is then reordered by digit in LDS and
+//     written out in that order: each digit's run of the tile lands in one
+//     contiguous stretch of the output, stored by consecutive threads.
 #include "orr_internal.h"
 
 namespace orr {
@@ -125,8 +127,17 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
 __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restrict__ part, uint32_t nparts,
                                                         uint32_t *__restrict__ offs) {
     const int p = blockIdx.x, d = threadIdx.x & (kRadixBins - 1), q = threadIdx.x >> kRadixBits;
+    // All loads first (nparts <= kSortHistBlocks), then the sum in block order.
+    constexpr int kPer = kSortHistBlocks / 4;
+    uint32_t c[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        const uint32_t b = q + 4u * j;
+        c[j] = b < nparts ? part[(uint64_t)b * kRadixPasses * kRadixBins + p * kRadixBins + d] : 0u;
+    }
     uint32_t s = 0;
-    for (uint32_t b = q; b < nparts; b += 4) s += part[(uint64_t)b * kRadixPasses * kRadixBins + p * kRadixBins + d];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) s += c[j];
     __shared__ uint32_t sum[4][kRadixBins];
     __shared__ uint32_t wsum[4];
     sum[q][d] = s;
@@ -150,27 +161,35 @@ __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restri
     }
 }
 
-// One pass over a tile of kTile keys. Wave w owns elements [kTile t +
-// w kTile/4, + kTile/4), lane l of round r element w kTile/4 + 64 r + l, so
-// (w, r, l) order is input order.
+// One pass over a tile of kTile keys. With W = kTileThreads / 64 waves, wave
+// w owns elements [kTile t + w kTile/W, + kTile/W), lane l of round r element
+// w kTile/W + 64 r + l, so (w, r, l) order is input order. The tile is reordered by digit in LDS and
+// written out in that order, so consecutive threads store consecutive slots.
 template <bool kGather>
-__global__ __launch_bounds__(256) void k_onesweep(const uint64_t *__restrict__ keys_in,
+__global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__restrict__ keys_in,
                                                   const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
                                                   const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
                                                   DevParams *prm, uint64_t *__restrict__ keys_out,
                                                   uint32_t *__restrict__ vals_out, const float *__restrict__ pos,
                                                   const float *__restrict__ mass, float4 *__restrict__ xs) {
+    constexpr int kWaves = kTileThreads / 64;
+    static_assert(kWaves * kRadixBins * 4 <= kTile * 8, "counts fit in the key buffer");
+    __shared__ uint64_t s_keys[kTile];  // first the per-wave digit counts, then the tile's keys by digit
+    __shared__ uint32_t s_vals[kTile];
+    __shared__ uint32_t s_delta[kRadixBins];  // output slot minus tile slot of each digit
+    __shared__ uint32_t s_wsum[kRadixBins / 64];
     __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_cnt[4][kRadixBins];  // running, then total, count per wave and digit
-    __shared__ uint32_t s_base[4][kRadixBins];  // output slot of wave w's first digit-d element
+    uint32_t(*s_cnt)[kRadixBins] = reinterpret_cast<uint32_t(*)[kRadixBins]>(s_keys);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     const int shift = pass * kRadixBits;
-    for (int k = threadIdx.x; k < 4 * kRadixBins; k += 256) (&s_cnt[0][0])[k] = 0;
+    for (int k = threadIdx.x; k < kWaves * kRadixBins; k += kTileThreads) (&s_cnt[0][0])[k] = 0;
     if (threadIdx.x == 0) s_tile = atomicAdd(&prm->sort_ticket[pass], 1u);
     __syncthreads();
     const uint32_t tile = s_tile;
-    const uint64_t base = (uint64_t)tile * kTile + (uint64_t)w * (kTile / 4);
+    const uint64_t t0 = (uint64_t)tile * kTile;
+    const uint32_t tile_n = (uint32_t)min<uint64_t>(kTile, n - t0);
+    const uint64_t base = t0 + (uint64_t)w * (kTile / kWaves);
 
     uint64_t key[kTileItems];
     uint32_t val[kTileItems], rank[kTileItems];
@@ -193,30 +212,54 @@ __global__ __launch_bounds__(256) void k_onesweep(const uint64_t *__restrict__ k
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    {
+    // Digit threads: tile totals, their scan over digits (the tile slot of
+    // each digit's first element), the look-back over earlier tiles.
+    uint32_t tot = 0, inc = 0;
+    if (threadIdx.x < kRadixBins) {
         const int d = threadIdx.x;
-        uint32_t tot = 0, wb[4];
-        for (int k = 0; k < 4; k++) {
-            wb[k] = tot;
-            tot += s_cnt[k][d];
+        for (int k = 0; k < kWaves; k++) tot += s_cnt[k][d];
+        inc = tot;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += t;
         }
+        if (lane == 63) s_wsum[w] = inc;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRadixBins) {
+        const int d = threadIdx.x;
+        uint32_t local = inc - tot;
+        for (int k = 0; k < w; k++) local += s_wsum[k];
         const uint32_t excl = look_back(lb_words + d, tile, kRadixBins, tot, &prm->bad_input);
-        const uint32_t first = digit_offs[pass * kRadixBins + d] + excl;
-        for (int k = 0; k < 4; k++) s_base[k][d] = first + wb[k];
+        s_delta[d] = digit_offs[pass * kRadixBins + d] + excl - local;
+        uint32_t run = local;
+        for (int k = 0; k < kWaves; k++) {  // in place: column d is this thread's alone
+            const uint32_t c = s_cnt[k][d];
+            s_cnt[k][d] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    uint32_t slot[kTileItems];
+    for (int r = 0; r < kTileItems; r++) {
+        const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
+        slot[r] = s_cnt[w][d] + rank[r];
     }
     __syncthreads();
     for (int r = 0; r < kTileItems; r++) {
-        const uint64_t e = base + (uint64_t)r * 64 + lane;
-        if (e < n) {
-            const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
-            const uint32_t o = s_base[w][d] + rank[r];
-            keys_out[o] = key[r];
-            vals_out[o] = val[r];
-            if (kGather) {
-                const uint64_t j = val[r];
-                xs[o] = make_float4(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], mass[j]);
-            }
+        if (base + (uint64_t)r * 64 + lane < n) {
+            s_keys[slot[r]] = key[r];
+            s_vals[slot[r]] = val[r];
         }
+    }
+    __syncthreads();
+    for (uint32_t j = threadIdx.x; j < tile_n; j += kTileThreads) {
+        const uint64_t k = s_keys[j];
+        const uint32_t v = s_vals[j];
+        const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
+        keys_out[o] = k;
+        vals_out[o] = v;
+        if (kGather) xs[o] = make_float4(pos[3ull * v], pos[3ull * v + 1], pos[3ull * v + 2], mass[v]);
     }
 }
 
@@ -240,10 +283,10 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
         const int src = pass & 1, dst = src ^ 1;
         uint64_t *words = ws.lb_words + (uint64_t)pass * nt * kRadixBins;
         if (pass + 1 < kRadixPasses)
-            k_onesweep<false><<<nt, 256, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
+            k_onesweep<false><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
                                                  ws.keys[dst], ws.vals[dst], nullptr, nullptr, nullptr);
         else
-            k_onesweep<true><<<nt, 256, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
+            k_onesweep<true><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
                                                 ws.keys[dst], ws.vals[dst], pos, mass, ws.xs);
     }
     return hipGetLastError();

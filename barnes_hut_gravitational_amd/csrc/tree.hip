@@ -268,40 +268,108 @@ __device__ __forceinline__ void finish_internal(uint32_t k, const uint4 &t, cons
     store_sums(k, M, sx, sy, sz, t.y, xs, nodes, msum);
 }
 
+// Sums of internal node k from its children's, in octant order (escape
+// chain), in LDS: esc and sum are indexed from the subtree root.
+__device__ __forceinline__ float4 sum_children_lds(uint32_t k, const uint32_t *esc, const float4 *sum) {
+    float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
+    for (uint32_t q = k + 1; q < esc[k]; q = max(esc[q], q + 1)) {
+        const float4 cs = sum[q];
+        M += cs.w;
+        sx += cs.x;
+        sy += cs.y;
+        sz += cs.z;
+    }
+    return make_float4(sx, sy, sz, M);
+}
+
 // One workgroup per cut subtree (grid-stride over the cut list): the internal
 // nodes of [r, escape(r)) level by level, deepest first (leaves are done).
+// A subtree of at most kCutLdsNodes nodes is staged in LDS (escapes, levels,
+// sums) and reduced there; a larger one is reduced in global memory.
+constexpr uint32_t kCutLdsNodes = 2048;
+
 __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ xs, NodeRec *nodes,
                                                      const uint8_t *__restrict__ level,
                                                      const uint32_t *__restrict__ cut_list,
                                                      const DevParams *__restrict__ prm, uint32_t max_nodes,
                                                      float4 *msum) {
+    __shared__ float4 s_sum[kCutLdsNodes];
+    __shared__ uint32_t s_esc[kCutLdsNodes];
+    __shared__ uint8_t s_lvl[kCutLdsNodes];
     __shared__ int s_lmax;
     const uint32_t n_cut = prm->n_cut;
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     for (uint32_t e = blockIdx.x; e < n_cut; e += gridDim.x) {
         const uint32_t r = cut_list[e];
         const uint32_t end = min(max(nodes[r].t.x, r + 1), nn);
+        const uint32_t m = end - r;
         const int lmin = level[r];
         if (threadIdx.x == 0) s_lmax = lmin;
-        __syncthreads();
+        __syncthreads();  // also: the previous subtree is done with LDS
         int lm = lmin;
-        for (uint32_t k = r + threadIdx.x; k < end; k += 256) lm = max(lm, (int)level[k]);
+        if (m <= kCutLdsNodes) {
+            for (uint32_t k = threadIdx.x; k < m; k += 256) {
+                const uint32_t ek = min(max(nodes[r + k].t.x, r + k + 1), end) - r;  // stays inside the subtree
+                const int l = level[r + k];
+                s_esc[k] = ek;
+                s_lvl[k] = (uint8_t)l;
+                lm = max(lm, l);
+                if (ek == k + 1) s_sum[k] = msum[r + k];  // leaf: summed at build
+            }
+        } else {
+            for (uint32_t k = r + threadIdx.x; k < end; k += 256) lm = max(lm, (int)level[k]);
+        }
         atomicMax(&s_lmax, lm);
         __syncthreads();
         const int lmax = s_lmax;
-        for (int l = lmax; l >= lmin; l--) {
-            for (uint32_t k = r + threadIdx.x; k < end; k += 256) {
-                if (level[k] != l) continue;
-                const uint4 t = nodes[k].t;
-                if (t.x != k + 1) finish_internal(k, t, xs, nodes, msum);
+        if (m <= kCutLdsNodes) {
+            for (int l = lmax; l >= lmin; l--) {
+                for (uint32_t k = threadIdx.x; k < m; k += 256)
+                    if (s_lvl[k] == l && s_esc[k] != k + 1) s_sum[k] = sum_children_lds(k, s_esc, s_sum);
+                __syncthreads();
             }
-            __syncthreads();
+            for (uint32_t k = threadIdx.x; k < m; k += 256) {
+                if (s_esc[k] == k + 1) continue;
+                const float4 c = s_sum[k];
+                store_sums(r + k, c.w, c.x, c.y, c.z, nodes[r + k].t.y, xs, nodes, msum);
+            }
+        } else {
+            for (int l = lmax; l >= lmin; l--) {
+                for (uint32_t k = r + threadIdx.x; k < end; k += 256) {
+                    if (level[k] != l) continue;
+                    const uint4 t = nodes[k].t;
+                    if (t.x != k + 1) finish_internal(k, t, xs, nodes, msum);
+                }
+                __syncthreads();
+            }
         }
     }
 }
 
 // One workgroup: the internal nodes above the cut, level by level, deepest
-// first, their children read from the recorded lists.
+// first, their children read from the recorded lists. The first
+// kTopCached * 1024 entries keep their node, level and children in
+// registers; any further ones are read again at every level.
+constexpr int kTopCached = 4;
+
+__device__ __forceinline__ void finish_top(uint32_t k, uint32_t nk, const uint32_t *kid,
+                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum) {
+    float4 cs[8];
+#pragma unroll
+    for (uint32_t j = 0; j < 8; j++)
+        if (j < nk) cs[j] = msum[kid[j]];
+    float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
+#pragma unroll
+    for (uint32_t j = 0; j < 8; j++) {
+        if (j >= nk) break;
+        M += cs[j].w;
+        sx += cs[j].x;
+        sy += cs[j].y;
+        sz += cs[j].z;
+    }
+    store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
+}
+
 __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__ xs, NodeRec *nodes,
                                                       const uint8_t *__restrict__ level,
                                                       const uint32_t *__restrict__ top_list,
@@ -313,29 +381,42 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
         s_lmin = kMaxLevel + 1;
         s_lmax = -1;
     }
+    uint32_t ck[kTopCached], cnk[kTopCached], ckid[kTopCached][8];
+    int cl[kTopCached];
+#pragma unroll
+    for (int j = 0; j < kTopCached; j++) {
+        const uint32_t e = threadIdx.x + 1024u * j;
+        ck[j] = e < n_top ? top_list[e] : 0u;
+        cnk[j] = e < n_top ? kids[9 * e] : 0u;
+#pragma unroll
+        for (int q = 0; q < 8; q++) ckid[j][q] = e < n_top ? kids[9 * e + 1 + q] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kTopCached; j++) cl[j] = threadIdx.x + 1024u * j < n_top ? (int)level[ck[j]] : -1;
     __syncthreads();
-    for (uint32_t e = threadIdx.x; e < n_top; e += 1024) {
+#pragma unroll
+    for (int j = 0; j < kTopCached; j++)
+        if (cl[j] >= 0) {
+            atomicMin(&s_lmin, cl[j]);
+            atomicMax(&s_lmax, cl[j]);
+        }
+    for (uint32_t e = threadIdx.x + 1024u * kTopCached; e < n_top; e += 1024) {
         const int l = level[top_list[e]];
         atomicMin(&s_lmin, l);
         atomicMax(&s_lmax, l);
     }
     __syncthreads();
     for (int l = s_lmax; l >= s_lmin; l--) {
-        for (uint32_t e = threadIdx.x; e < n_top; e += 1024) {
+#pragma unroll
+        for (int j = 0; j < kTopCached; j++)
+            if (cl[j] == l && cnk[j] != 0) finish_top(ck[j], cnk[j], ckid[j], xs, nodes, msum);
+        for (uint32_t e = threadIdx.x + 1024u * kTopCached; e < n_top; e += 1024) {
             const uint32_t k = top_list[e];
             const uint32_t nk = kids[9 * e];
             if (level[k] != l || nk == 0) continue;  // other level, or a leaf (done)
-            float4 cs[8];
-            for (uint32_t j = 0; j < 8; j++)
-                if (j < nk) cs[j] = msum[kids[9 * e + 1 + j]];
-            float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
-            for (uint32_t j = 0; j < nk; j++) {
-                M += cs[j].w;
-                sx += cs[j].x;
-                sy += cs[j].y;
-                sz += cs[j].z;
-            }
-            store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
+            uint32_t kid[8];
+            for (uint32_t q = 0; q < 8; q++) kid[q] = q < nk ? kids[9 * e + 1 + q] : 0u;
+            finish_top(k, nk, kid, xs, nodes, msum);
         }
         __syncthreads();
     }

@@ -257,15 +257,27 @@ __global__ __launch_bounds__(256) void k_wave_cost(const uint32_t *__restrict__ 
 }
 
 // One block: counting sort of the waves by decreasing cost. Waves of equal
-// cost may come out in any order.
+// cost may come out in any order. The first kOrderCached costs of each
+// thread are loaded once, all at the start.
+constexpr int kOrderCached = 16;
+
 __global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t *__restrict__ cost,
                                                                   uint32_t n_waves, uint32_t *__restrict__ order) {
     __shared__ uint32_t bins[kWaveCostBins];
     __shared__ uint32_t wsum[kWaveOrderThreads / 64];
     const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
+    uint32_t cb[kOrderCached];  // cost bins of waves t + j kWaveOrderThreads
+#pragma unroll
+    for (int j = 0; j < kOrderCached; j++) {
+        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
+        cb[j] = w < n_waves ? min(cost[w], (uint32_t)kWaveCostBins - 1u) : 0u;
+    }
     for (uint32_t b = t; b < (uint32_t)kWaveCostBins; b += kWaveOrderThreads) bins[b] = 0u;
     __syncthreads();
-    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads)
+#pragma unroll
+    for (int j = 0; j < kOrderCached; j++)
+        if (t + (uint32_t)j * kWaveOrderThreads < n_waves) atomicAdd(&bins[cb[j]], 1u);
+    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads)
         atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
     __syncthreads();
     // Exclusive scan in decreasing cost; thread t owns bins b0 = top - 2t and b0 - 1.
@@ -284,7 +296,12 @@ __global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t
     bins[b0] = excl;
     bins[b1] = excl + c0;
     __syncthreads();
-    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads) {
+#pragma unroll
+    for (int j = 0; j < kOrderCached; j++) {
+        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
+        if (w < n_waves) order[atomicAdd(&bins[cb[j]], 1u)] = w;
+    }
+    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads) {
         const uint32_t pos = atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
         order[pos] = w;
     }
