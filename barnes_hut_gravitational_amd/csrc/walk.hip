@@ -131,6 +131,15 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
     }
 }
 
+// v + 1 on the lanes whose bit is set in mask, v elsewhere: one add with the
+// mask as carry-in.
+__device__ __forceinline__ uint32_t add_lane_bit(uint32_t v, uint64_t mask) {
+    uint32_t r;
+    uint64_t carry;
+    __asm__("v_addc_co_u32_e64 %0, %1, 0, %2, %3" : "=v"(r), "=s"(carry) : "v"(v), "s"(mask));
+    return r;
+}
+
 // Sorted targets of this lane's wave: wave slot s of the grid runs target
 // wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
 // schedule get no targets.
@@ -155,7 +164,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
     const uint32_t wv = threadIdx.x >> 6;
-    uint32_t pp = 0, pc = 0, vown = 0;
+    uint32_t pp = 0, pc = 0, nopen = 0;  // visits_own = pc + nopen: every acting lane accepts or opens
     uint32_t steps = 0;  // wave-uniform: visits_stepped
     const char *node_bytes = reinterpret_cast<const char *>(nodes);
     uint32_t c = 0;
@@ -188,8 +197,8 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
             next = esc;
         }
         const bool opening = active && !far;
-        if (active) vown += 1;
         if (m_open) {
+            nopen = add_lane_bit(nopen, m_open);
             if (esc == c + 1) {  // a leaf that some lane opens
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
                 const uint32_t g = pack_width((uint32_t)__popcll(m_open), cnt);
@@ -220,7 +229,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         // escape[c]; for a leaf escape[c] = c + 1 anyway), else the escape.
         c = m_open ? c + 1 : esc;
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, vown, steps, pp, pc);
+    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
 // Walk schedule. How long a wave runs grows with the particle density
