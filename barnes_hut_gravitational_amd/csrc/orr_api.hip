@@ -248,9 +248,23 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
     orr_status st = check_walk_args(eps, theta, (int)traversal);
     if (st != ORR_OK) return st;
-    hipError_t e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT, eps * eps, theta * theta, acc,
-                               visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    hipError_t e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
+                               eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "walk");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_walk_min_advance(const orr_tree *tree, float eps, float theta, float *acc, uint32_t *visits_own,
+                                     uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    orr_status st = check_walk_args(eps, theta, ORR_TRAVERSAL_COHERENT);
+    if (st != ORR_OK) return st;
+    hipError_t e = launch_walk(tree->ws, kWalkCoherentMin, eps * eps, theta * theta, acc, visits_own, visits_stepped,
+                               n_pp, n_pc, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "min-advance walk");
     return ORR_OK;
     ORR_GUARD_END
 }
@@ -300,8 +314,8 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     hipError_t e = tm.init(timings != nullptr, t.stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((st = build_into(pos, mass, t.ws, t.stream, tm)) != ORR_OK) return st;
-    e = launch_walk(t.ws, traversal == ORR_TRAVERSAL_COHERENT, eps * eps, theta * theta, acc, visits_own,
-                    visits_stepped, n_pp, n_pc, t.stream);
+    e = launch_walk(t.ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent, eps * eps,
+                    theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, t.stream);
     if (e != hipSuccess) return hip_fail(e, "walk");
     if (!timings) return ORR_OK;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -107,7 +107,10 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
 hipError_t launch_build(const Workspace &ws, hipStream_t s);
 hipError_t launch_moments(const Workspace &ws, hipStream_t s);
 hipError_t launch_tree_info(const Workspace &ws, hipStream_t s);
-hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
+// Walk kinds: the independent walk, the coherent walk (ballot advance), the
+// coherent walk advancing by an explicit wave minimum (same results).
+enum { kWalkIndependent = 0, kWalkCoherent = 1, kWalkCoherentMin = 2 };
+hipError_t launch_walk(const Workspace &ws, int mode, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s);
 // Group widths 1, 2, 4, ..., 64 (hipErrorInvalidValue otherwise); descend:

@@ -140,6 +140,31 @@ __device__ __forceinline__ uint32_t add_lane_bit(uint32_t v, uint64_t mask) {
     return r;
 }
 
+// Smallest value over the wave's 64 lanes, wave-uniform: DPP minima within
+// rows of 16 lanes (two quad permutations, two row rotations), two row
+// broadcasts that carry the minimum to the last lane, then that lane's value.
+// Each step is one v_min_u32 with a DPP source; rows outside row_mask keep
+// their value. The s_nop before each step covers the wait a DPP read needs
+// after a VALU write of the same register. Needs every lane active.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    __asm__ volatile(
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_min_u32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Sorted targets of this lane's wave: wave slot s of the grid runs target
 // wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
 // schedule get no targets.
@@ -154,7 +179,13 @@ struct WalkLds {
     float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64];
 };
 
-template <int kInv, bool kOff32>
+// kMin: the wave advances to the minimum of the lanes' `next` (every lane
+// keeps its own next node, c + 1 after opening), found with a DPP
+// reduction, instead of the select on the opening mask. Both rules give the
+// same node sequence (the next node any lane wants is c + 1 if some lane
+// opened c and escape[c] otherwise); kMin exists to measure the cost of the
+// explicit reduction.
+template <int kInv, bool kOff32, bool kMin>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
                                               uint32_t n_nodes, float eps2, float theta2, const WalkOut &out,
@@ -224,10 +255,16 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
                 if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
         }
-        // The smallest index any lane wants: c + 1 if some lane opened c (a
-        // waiting lane wants the escape of a skipped ancestor of c, at least
-        // escape[c]; for a leaf escape[c] = c + 1 anyway), else the escape.
-        c = m_open ? c + 1 : esc;
+        if (kMin) {
+            if (opening) next = c + 1;
+            c = max(wave_min_u32(next), c + 1);  // the max only guards progress; the minimum exceeds c
+        } else {
+            // The smallest index any lane wants: c + 1 if some lane opened c
+            // (a waiting lane wants the escape of a skipped ancestor of c, at
+            // least escape[c]; for a leaf escape[c] = c + 1 anyway), else the
+            // escape.
+            c = m_open ? c + 1 : esc;
+        }
     }
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
@@ -316,7 +353,7 @@ __global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t
     }
 }
 
-template <bool kFastInv, bool kOff32>
+template <bool kFastInv, bool kOff32, bool kMin>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
@@ -328,11 +365,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__re
     const uint32_t i = scheduled_target(order, n_waves);
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
-        walk_coherent<kInvIeee, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvIeee, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else if (r2_cannot_overflow(prm, eps2))  // uniform
-        walk_coherent<kInvFastNoClamp, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvFastNoClamp, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
     else
-        walk_coherent<kInvFast, kOff32>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvFast, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
 }
 
 template <int kInv>
@@ -406,21 +443,30 @@ __global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint6
 __global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
 
 template <bool kFast>
-hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float theta2, const WalkOut &out,
+hipError_t launch_walk_t(const Workspace &ws, int mode, float eps2, float theta2, const WalkOut &out,
                          hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
     const uint32_t nb = (uint32_t)ws.max_nodes;
     const uint32_t nw = (uint32_t)ws.n_waves;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
-    if (coherent) {
+    if (mode != kWalkIndependent) {
         k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
         k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
-        if ((uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull)
-            k_walk_coherent<kFast, true><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
-                                                                       eps2, theta2, ws.wave_order, nw, out);
-        else
-            k_walk_coherent<kFast, false><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
-                                                                        eps2, theta2, ws.wave_order, nw, out);
+        const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
+#define ORR_COHERENT(OFF32, MIN)                                                                               \
+    k_walk_coherent<kFast, OFF32, MIN><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
+                                                                     eps2, theta2, ws.wave_order, nw, out)
+        if (mode == kWalkCoherentMin) {
+            if (off32)
+                ORR_COHERENT(true, true);
+            else
+                ORR_COHERENT(false, true);
+        } else if (off32) {
+            ORR_COHERENT(true, false);
+        } else {
+            ORR_COHERENT(false, false);
+        }
+#undef ORR_COHERENT
     } else {
         k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
                                                                 eps2, theta2, out);
@@ -433,12 +479,12 @@ hipError_t launch_walk_t(const Workspace &ws, int coherent, float eps2, float th
 // The fast inverse square root applies when every r^2 >= eps^2 is >= 2^-96.
 bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
 
-hipError_t launch_walk(const Workspace &ws, int coherent, float eps2, float theta2, float *acc,
+hipError_t launch_walk(const Workspace &ws, int mode, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s) {
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, coherent, eps2, theta2, out, s);
-    return launch_walk_t<false>(ws, coherent, eps2, theta2, out, s);
+    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, mode, eps2, theta2, out, s);
+    return launch_walk_t<false>(ws, mode, eps2, theta2, out, s);
 }
 
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,

@@ -20,7 +20,7 @@ ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_
 TRAVERSALS = {"independent": 0, "coherent": 1}
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
-            "orr_tree_walk_descend", "orr_eval_forces",
+            "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_eval_forces",
             "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
             "orr_selftest_inv_sqrt", "orr_tree_free")
 
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_walk.argtypes = [_vp, f32, f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_grouped.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_descend.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
+        L.orr_tree_walk_min_advance.argtypes = [_vp, f32, f32, _vp, _vp, _vp, _vp, _vp]
         L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
                                       _vp, ctypes.POINTER(Timings)]
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_free.argtypes = [_vp]
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
-                     "orr_eval_forces",
+                     "orr_tree_walk_min_advance", "orr_eval_forces",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
                      "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
@@ -209,6 +210,14 @@ class Tree:
         """The descend-together group walk (orr_tree_walk_descend)."""
         acc, cnt = out if out is not None else _outputs(self.n, self.device)
         _check(lib().orr_tree_walk_descend(self._h, eps, theta, group_width, _ptr(acc), *[_ptr(c) for c in cnt]))
+        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+
+    def walk_min_advance(self, eps=0.05, theta=0.5, out=None) -> Result:
+        """The coherent walk advancing by an explicit wave minimum of the
+        lanes' next nodes (orr_tree_walk_min_advance); same outputs as the
+        coherent walk."""
+        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        _check(lib().orr_tree_walk_min_advance(self._h, eps, theta, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
     def info(self) -> dict:

@@ -143,6 +143,29 @@ def descend_leg(tree, acc, cnt, stream, trials=4):
     return out
 
 
+def advance_leg(tree, acc, cnt, stream, trials=6):
+    """Cost of the wave advance rule: the coherent walk (select between c + 1
+    and the escape on the mask of opening lanes) against the same walk taking
+    an explicit DPP minimum of the lanes' next nodes at every step
+    (orr_tree_walk_min_advance); both visit the same nodes."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs
+
+    runs = {"mask_select": lambda: tree.walk(inputs.EPS, inputs.THETA, traversal="coherent", out=(acc, cnt)),
+            "dpp_min": lambda: tree.walk_min_advance(inputs.EPS, inputs.THETA, out=(acc, cnt))}
+    out = {}
+    for name, run in runs.items():
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        ev[0].record(stream)
+        for k in range(trials):
+            run()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        out[name] = {"walk_ms_median": percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5)}
+    return out
+
+
 def cpu_baseline(pos, mass, trials):
     """The oracle as it stands, on this host's cores: whole evaluations of the
     workload (build, walk of every target, group union visits), median."""
@@ -237,6 +260,7 @@ def main():
     direct = None if args.no_direct else direct_leg(dev, stream)
     widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
+    advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -274,6 +298,7 @@ def main():
         "direct": direct,
         "width_sweep": widths,
         "descend_together": descend,
+        "advance_rule": advance,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -170,6 +170,19 @@ orr_status orr_tree_walk_grouped(const orr_tree *tree, float eps, float theta, i
                                  float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                                  uint32_t *n_pc);
 
+/* The coherent walk of orr_tree_walk with the wave's next node found as the
+ * minimum of its lanes' next nodes (the advance the solver page describes
+ * for its sub-groups, "The mitigation"): every lane keeps its own next node
+ * and the wave takes a DPP minimum over them at every step, where
+ * orr_tree_walk selects between c + 1 and the escape from the mask of
+ * opening lanes. Both rules visit the same nodes in the same order, so every
+ * output equals the coherent orr_tree_walk's bit for bit; this entry exists
+ * to measure the reduction's cost. Arguments, outputs and errors as
+ * orr_tree_walk with traversal = ORR_TRAVERSAL_COHERENT. */
+orr_status orr_tree_walk_min_advance(const orr_tree *tree, float eps, float theta, float *acc,
+                                     uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                                     uint32_t *n_pc);
+
 /* The alternative ADR-0029 rejects ("Alternatives considered"), the
  * published warp-coherent traversal, for comparison: groups of group_width
  * consecutive sorted targets (1, 2, 4, ..., 64) share one node; the group

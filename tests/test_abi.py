@@ -86,6 +86,8 @@ def test_build_and_walk_argument_errors():
     assert h.value is None
     assert L.orr_tree_walk(None, 0.05, 0.5, 1, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_grouped(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_walk_descend(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_walk_min_advance(None, 0.05, 0.5, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_check(None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_export(None, None, None, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
