@@ -29,6 +29,7 @@
 // sorted order; internal: its children in octant order), so every bit depends
 // only on the tree.
 #include "orr_internal.h"
+#include "schedule.h"
 
 namespace orr {
 
@@ -51,10 +52,16 @@ __device__ __forceinline__ uint32_t base_at(const uint32_t *__restrict__ tile_pr
 
 // One block of 256 particles i in [256 b, 256 b + 256), i <= n. Writes
 // info[i] = first(i) | D(i) << 8, loc[i] = nodes started by the block's
-// particles before i, and tile_sum[b] = nodes started by the block.
+// particles before i, and tile_sum[b] = nodes started by the block. Each
+// wave of 64 particles is also one target wave of the coherent walk; it
+// writes that wave's cost estimate for the walk schedule: summed leaf depth
+// D plus 32 times the levels between its deepest leaf and the smallest cell
+// holding all its targets (whole levels of the common prefix of its first
+// and last key; bit 63 is always zero). At most 64 * 21 + 32 * 21.
 __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__ keys, uint32_t n, uint32_t cap,
                                                     uint32_t *__restrict__ info, uint32_t *__restrict__ loc,
-                                                    uint32_t *__restrict__ tile_sum) {
+                                                    uint32_t *__restrict__ tile_sum,
+                                                    uint32_t *__restrict__ wave_cost) {
     __shared__ uint64_t sk[256 + 2 * 256];
     __shared__ signed char sw[256 + 256];
     __shared__ uint32_t s_wsum[4];
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__
     }
     __syncthreads();
     const int64_t i = B + threadIdx.x;
-    uint32_t nst = 0;
+    uint32_t nst = 0, depth = 0;
     if (i < (int64_t)n) {
         int m = -1;
         for (int t = threadIdx.x; t <= threadIdx.x + (int)cap; t++) m = max(m, (int)sw[t]);
@@ -82,8 +89,23 @@ __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__
         const int first = (i == 0) ? 0 : lcp_digits(sk[threadIdx.x + cap - 1], sk[threadIdx.x + cap]) + 1;
         info[i] = (uint32_t)first | ((uint32_t)D << 8);
         nst = D >= first ? (uint32_t)(D - first + 1) : 0u;
+        depth = (uint32_t)D;
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    {
+        uint32_t sum = depth, deepest = depth;
+        for (int o = 32; o > 0; o >>= 1) {
+            sum += __shfl_xor(sum, o, 64);
+            deepest = max(deepest, (uint32_t)__shfl_xor(deepest, o, 64));
+        }
+        if (lane == 0 && i < (int64_t)n) {
+            const int64_t last = min(i + 63, (int64_t)n - 1);
+            const uint64_t klast = last - wbeg < wlen ? sk[last - wbeg] : keys[last];
+            const uint64_t x = sk[threadIdx.x + cap] ^ klast;
+            const uint32_t enclosing = (x == 0ull ? 63u : (uint32_t)__clzll(x) - 1u) / 3u;
+            wave_cost[i >> 6] = sum + 32u * (deepest > enclosing ? deepest - enclosing : 0u);
+        }
+    }
     uint32_t inc = nst;
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t t = __shfl_up(inc, o, 64);
@@ -370,11 +392,22 @@ __device__ __forceinline__ void finish_top(uint32_t k, uint32_t nk, const uint32
     store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
 }
 
+// k_moments_top: block 0 finishes the moments above the cut; block 1 orders
+// the coherent walk's target waves (schedule.h), independent work of one
+// block that runs beside it instead of in a launch of its own.
+static_assert(kWaveOrderThreads == 1024, "the schedule block has the moments block's size");
+
 __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__ xs, NodeRec *nodes,
                                                       const uint8_t *__restrict__ level,
                                                       const uint32_t *__restrict__ top_list,
                                                       const uint32_t *__restrict__ kids,
-                                                      const DevParams *__restrict__ prm, float4 *msum) {
+                                                      const DevParams *__restrict__ prm, float4 *msum,
+                                                      const uint32_t *__restrict__ wave_cost, uint32_t n_waves,
+                                                      uint32_t *__restrict__ wave_order) {
+    if (blockIdx.x == 1) {
+        wave_order_block(wave_cost, n_waves, wave_order);
+        return;
+    }
     __shared__ int s_lmin, s_lmax;
     const uint32_t n_top = prm->n_top;
     if (threadIdx.x == 0) {
@@ -461,7 +494,8 @@ hipError_t launch_build(const Workspace &ws, hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
     const uint32_t scan_tiles = (uint32_t)ceil_div(ws.n + 1, kScanTile);
     const unsigned node_blocks = (unsigned)ceil_div(ws.max_nodes, 256);
-    k_tree_count<<<scan_tiles, 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info, ws.base, ws.tile_sum);
+    k_tree_count<<<scan_tiles, 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info, ws.base, ws.tile_sum,
+                                            ws.wave_cost);
     k_tile_scan<<<1, 1024, 0, s>>>(ws.tile_sum, scan_tiles, ws.prm);
     k_tree_stub<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.tile_sum, ws.base, n, ws.nodes, ws.level);
     k_tree_ends<<<node_blocks, 256, 0, s>>>(ws.keys[0], n, ws.tile_sum, ws.base, ws.prm, (uint32_t)ws.max_nodes,
@@ -474,7 +508,8 @@ hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 2));
     k_moments_cut<<<blocks, 256, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.cut_list, ws.prm, (uint32_t)ws.max_nodes,
                                          ws.msum);
-    k_moments_top<<<1, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum);
+    k_moments_top<<<2, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum,
+                                     ws.wave_cost, (uint32_t)ws.n_waves, ws.wave_order);
     return hipGetLastError();
 }
 

@@ -269,89 +269,8 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
-// Walk schedule. How long a wave runs grows with the particle density
-// around its targets, which the depth of a target's leaf measures, and with
-// how spread out its 64 targets are: the wave steps through the union of
-// their walks, which grows when the targets span a large cell. The cost of a
-// wave is its summed leaf depth plus 32 times the levels between its deepest
-// leaf and the smallest cell holding all its targets (from the common prefix
-// of its first and last sorted key). Target waves start in order of
-// decreasing cost, so the longest ones start first and the last to start are
-// short: longest-first list scheduling, which keeps the grid's tail short
-// when a wave runs for a large part of the whole launch. The schedule decides
-// only when a wave runs, never what it computes.
-constexpr int kWaveOrderThreads = kWaveCostBins / 2;
-static_assert(64 * kMaxLevel + 32 * kMaxLevel < kWaveCostBins, "wave cost range");
-
-__global__ __launch_bounds__(256) void k_wave_cost(const uint32_t *__restrict__ info,
-                                                   const uint64_t *__restrict__ keys, uint32_t n,
-                                                   uint32_t *__restrict__ cost) {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-    const uint32_t d = i < n ? (info[i] >> 8) & 0xffu : 0u;  // leaf depth of sorted target i
-    uint32_t sum = d, deepest = d;
-    for (int o = 32; o > 0; o >>= 1) {
-        sum += __shfl_xor(sum, o, 64);
-        deepest = max(deepest, __shfl_xor(deepest, o, 64));
-    }
-    if ((threadIdx.x & 63u) == 0u && i < n) {
-        const uint64_t x = keys[i] ^ keys[min(i + 63u, n - 1u)];
-        // Level of the smallest cell holding the wave's targets: whole levels
-        // of the common key prefix below bit 63 (always zero).
-        const uint32_t enclosing = (x == 0ull ? 63u : (uint32_t)__clzll(x) - 1u) / 3u;
-        cost[i >> 6] = sum + 32u * (deepest > enclosing ? deepest - enclosing : 0u);  // <= 64*21 + 32*21 < 2048
-    }
-}
-
-// One block: counting sort of the waves by decreasing cost. Waves of equal
-// cost may come out in any order. The first kOrderCached costs of each
-// thread are loaded once, all at the start.
-constexpr int kOrderCached = 16;
-
-__global__ __launch_bounds__(kWaveOrderThreads) void k_wave_order(const uint32_t *__restrict__ cost,
-                                                                  uint32_t n_waves, uint32_t *__restrict__ order) {
-    __shared__ uint32_t bins[kWaveCostBins];
-    __shared__ uint32_t wsum[kWaveOrderThreads / 64];
-    const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
-    uint32_t cb[kOrderCached];  // cost bins of waves t + j kWaveOrderThreads
-#pragma unroll
-    for (int j = 0; j < kOrderCached; j++) {
-        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
-        cb[j] = w < n_waves ? min(cost[w], (uint32_t)kWaveCostBins - 1u) : 0u;
-    }
-    for (uint32_t b = t; b < (uint32_t)kWaveCostBins; b += kWaveOrderThreads) bins[b] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kOrderCached; j++)
-        if (t + (uint32_t)j * kWaveOrderThreads < n_waves) atomicAdd(&bins[cb[j]], 1u);
-    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads)
-        atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
-    __syncthreads();
-    // Exclusive scan in decreasing cost; thread t owns bins b0 = top - 2t and b0 - 1.
-    const uint32_t b0 = (uint32_t)kWaveCostBins - 1u - 2u * t, b1 = b0 - 1u;
-    const uint32_t c0 = bins[b0], c1 = bins[b1];
-    uint32_t x = c0 + c1;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= (uint32_t)o) x += y;
-    }
-    if (lane == 63u) wsum[wv] = x;
-    __syncthreads();
-    uint32_t before = 0u;
-    for (uint32_t k = 0; k < wv; k++) before += wsum[k];
-    const uint32_t excl = before + x - (c0 + c1);
-    bins[b0] = excl;
-    bins[b1] = excl + c0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kOrderCached; j++) {
-        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
-        if (w < n_waves) order[atomicAdd(&bins[cb[j]], 1u)] = w;
-    }
-    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads) {
-        const uint32_t pos = atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
-        order[pos] = w;
-    }
-}
+// The walk schedule (the order in which target waves start) is computed by
+// the tree build (schedule.h).
 
 template <bool kFastInv, bool kOff32, bool kMin>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
@@ -450,8 +369,6 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, float eps2, float theta2
     const uint32_t nw = (uint32_t)ws.n_waves;
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
     if (mode != kWalkIndependent) {
-        k_wave_cost<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.keys[0], n, ws.wave_cost);
-        k_wave_order<<<1, kWaveOrderThreads, 0, s>>>(ws.wave_cost, nw, ws.wave_order);
         const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
 #define ORR_COHERENT(OFF32, MIN)                                                                               \
     k_walk_coherent<kFast, OFF32, MIN><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
