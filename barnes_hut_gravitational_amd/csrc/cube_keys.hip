@@ -4,7 +4,8 @@
 // sort in front of the tree build; the root cube is the reading stated in
 // include/orr.h: corner = component-wise minimum, side = largest extent.
 // HBM-bound streaming reduction (12 B of position + 4 B of mass per
-// particle). The final kernel also resets the build's device counters.
+// particle) into per-block partials; every block of the key kernel
+// (sort.hip) combines them into the cube itself.
 #include "orr_internal.h"
 
 namespace orr {
@@ -28,7 +29,30 @@ __global__ __launch_bounds__(256) void k_cube_partial(const float *__restrict__ 
     float mn0 = INFINITY, mn1 = INFINITY, mn2 = INFINITY;
     float mx0 = -INFINITY, mx1 = -INFINITY, mx2 = -INFINITY;
     uint32_t bad = 0;
-    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += gridDim.x * 256u) {
+    const uint32_t stride = gridDim.x * 256u;
+    uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    for (; i + 3u * stride < n; i += 4u * stride) {  // four particles' loads in flight
+        float x[4], y[4], z[4], m[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint64_t j = i + (uint64_t)k * stride;
+            x[k] = pos[3 * j];
+            y[k] = pos[3 * j + 1];
+            z[k] = pos[3 * j + 2];
+            m[k] = mass[j];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            bad |= !(isfinite(x[k]) && isfinite(y[k]) && isfinite(z[k]) && isfinite(m[k]) && m[k] >= 0.0f);
+            mn0 = fminf(mn0, x[k]);
+            mn1 = fminf(mn1, y[k]);
+            mn2 = fminf(mn2, z[k]);
+            mx0 = fmaxf(mx0, x[k]);
+            mx1 = fmaxf(mx1, y[k]);
+            mx2 = fmaxf(mx2, z[k]);
+        }
+    }
+    for (; i < n; i += stride) {
         float x = pos[3ull * i], y = pos[3ull * i + 1], z = pos[3ull * i + 2], m = mass[i];
         bad |= !(isfinite(x) && isfinite(y) && isfinite(z) && isfinite(m) && m >= 0.0f);
         mn0 = fminf(mn0, x);
@@ -58,52 +82,12 @@ __global__ __launch_bounds__(256) void k_cube_partial(const float *__restrict__ 
     }
 }
 
-// One block: combine the partials, write lo, side, scale and the flag.
-__global__ __launch_bounds__(64) void k_cube_final(const float *__restrict__ part, int nparts,
-                                                   DevParams *__restrict__ prm) {
-    const int lane = threadIdx.x;
-    float r[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    uint32_t bad = 0;
-    for (int b = lane; b < nparts; b += 64) {
-        for (int k = 0; k < 3; k++) r[k] = fminf(r[k], part[8 * b + k]);
-        for (int k = 3; k < 6; k++) r[k] = fmaxf(r[k], part[8 * b + k]);
-        bad |= __float_as_uint(part[8 * b + 6]);
-    }
-    for (int k = 0; k < 3; k++) r[k] = wave_min(r[k]);
-    for (int k = 3; k < 6; k++) r[k] = wave_max(r[k]);
-    bad = __ballot(bad != 0) != 0ull;
-    if (lane == 0) {
-        float lo[3], side = 0.0f;
-        for (int a = 0; a < 3; a++) {
-            lo[a] = r[a] + 0.0f;  // -0 becomes +0: a unique corner
-            float ext = r[3 + a] - lo[a];
-            if (ext > side) side = ext;
-        }
-        if (!isfinite(side) || !isfinite(lo[0]) || !isfinite(lo[1]) || !isfinite(lo[2])) {
-            bad = 1;  // keep the rest of the build well-formed
-            side = 1.0f;
-            for (int a = 0; a < 3; a++)
-                if (!isfinite(lo[a])) lo[a] = 0.0f;
-        }
-        if (side == 0.0f) side = 1.0f;
-        for (int a = 0; a < 3; a++) prm->lo[a] = lo[a];
-        prm->side = side;
-        prm->scale = 2097152.0f / side;  // correctly rounded division
-        prm->bad_input = bad;
-        prm->n_nodes = 0;
-        for (int p = 0; p < kRadixPasses; p++) prm->sort_ticket[p] = 0;
-        prm->n_cut = 0;
-        prm->n_top = 0;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_cube(const float *pos, const float *mass, const Workspace &ws, hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
     int blocks = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));
     k_cube_partial<<<blocks, 256, 0, s>>>(pos, mass, n, ws.cube_part);
-    k_cube_final<<<1, 64, 0, s>>>(ws.cube_part, blocks, ws.prm);
     return hipGetLastError();
 }
 

@@ -94,27 +94,107 @@ __device__ __forceinline__ uint32_t quantise(float x, float lo, float scale) {
     return t >= 0.0f ? (uint32_t)t : 0u;
 }
 
+__device__ __forceinline__ float wave_min(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// The root cube from the per-block partials of k_cube_partial (min x, y, z,
+// max x, y, z, flag bits), by one wave: corner lo = the minima (-0 made +0,
+// so the corner is unique), side = the largest extent (1 if it is 0 or not
+// finite, the latter flagged), scale = 2^21 / side correctly rounded. Every
+// block of the key kernel computes the same values from the same partials.
+__device__ __forceinline__ void cube_from_partials(const float *__restrict__ part, int nparts, float lo[3],
+                                                   float &side, uint32_t &bad) {
+    const int lane = threadIdx.x & 63;
+    float r[6] = {INFINITY, INFINITY, INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    uint32_t b = 0;
+    for (int q = lane; q < nparts; q += 64) {
+        for (int k = 0; k < 3; k++) r[k] = fminf(r[k], part[8 * q + k]);
+        for (int k = 3; k < 6; k++) r[k] = fmaxf(r[k], part[8 * q + k]);
+        b |= __float_as_uint(part[8 * q + 6]);
+    }
+    for (int k = 0; k < 3; k++) r[k] = wave_min(r[k]);
+    for (int k = 3; k < 6; k++) r[k] = wave_max(r[k]);
+    bad = __ballot(b != 0) != 0ull;
+    side = 0.0f;
+    for (int a = 0; a < 3; a++) {
+        lo[a] = r[a] + 0.0f;
+        const float ext = r[3 + a] - lo[a];
+        if (ext > side) side = ext;
+    }
+    if (!isfinite(side) || !isfinite(lo[0]) || !isfinite(lo[1]) || !isfinite(lo[2])) {
+        bad = 1;  // keep the rest of the build well-formed
+        side = 1.0f;
+        for (int a = 0; a < 3; a++)
+            if (!isfinite(lo[a])) lo[a] = 0.0f;
+    }
+    if (side == 0.0f) side = 1.0f;
+}
+
 // Keys and the identity payload; each block's 8 digit histograms to
-// part[block][pass][digit]; zeroes the look-back words of the build.
+// part[block][pass][digit]; zeroes the look-back words of the build. Each
+// block first forms the root cube from the partials; block 0 also stores it
+// in prm with the input flag and resets the build's device counters.
 __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ pos, uint32_t n,
-                                                     const DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
+                                                     const float *__restrict__ cube_part, int cube_parts,
+                                                     DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
                                                      uint32_t *__restrict__ idx, uint32_t *__restrict__ part,
                                                      uint64_t *__restrict__ lb_words, uint64_t n_lb_words) {
     __shared__ uint32_t h[kRadixPasses * kRadixBins];
+    __shared__ float s_cube[4];
     for (int k = threadIdx.x; k < kRadixPasses * kRadixBins; k += 256) h[k] = 0;
+    if (threadIdx.x < 64) {
+        float lo[3], side;
+        uint32_t bad;
+        cube_from_partials(cube_part, cube_parts, lo, side, bad);
+        const float scale = 2097152.0f / side;  // correctly rounded division
+        if (threadIdx.x == 0) {
+            s_cube[0] = lo[0];
+            s_cube[1] = lo[1];
+            s_cube[2] = lo[2];
+            s_cube[3] = scale;
+            if (blockIdx.x == 0) {
+                for (int a = 0; a < 3; a++) prm->lo[a] = lo[a];
+                prm->side = side;
+                prm->scale = scale;
+                prm->bad_input = bad;
+                prm->n_nodes = 0;
+                for (int q = 0; q < kRadixPasses; q++) prm->sort_ticket[q] = 0;
+                prm->n_cut = 0;
+                prm->n_top = 0;
+            }
+        }
+    }
     __syncthreads();
-    const float lx = prm->lo[0], ly = prm->lo[1], lz = prm->lo[2], sc = prm->scale;
+    const float lx = s_cube[0], ly = s_cube[1], lz = s_cube[2], sc = s_cube[3];
     const uint32_t stride = gridDim.x * 256u;
-    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n; i += stride) {
-        const uint32_t qx = quantise(pos[3ull * i], lx, sc);
-        const uint32_t qy = quantise(pos[3ull * i + 1], ly, sc);
-        const uint32_t qz = quantise(pos[3ull * i + 2], lz, sc);
-        const uint64_t key = (spread3(qx) << 2) | (spread3(qy) << 1) | spread3(qz);
+    auto one = [&](uint32_t i, float x, float y, float z) {
+        const uint64_t key = (spread3(quantise(x, lx, sc)) << 2) | (spread3(quantise(y, ly, sc)) << 1) |
+                             spread3(quantise(z, lz, sc));
         keys[i] = key;
         idx[i] = i;
         for (int p = 0; p < kRadixPasses; p++)
             atomicAdd(&h[p * kRadixBins + ((uint32_t)(key >> (p * kRadixBits)) & (kRadixBins - 1))], 1u);
+    };
+    uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    for (; i + 3u * stride < n; i += 4u * stride) {  // four particles' loads in flight
+        float x[4], y[4], z[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint64_t j = i + (uint64_t)k * stride;
+            x[k] = pos[3 * j];
+            y[k] = pos[3 * j + 1];
+            z[k] = pos[3 * j + 2];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) one(i + k * stride, x[k], y[k], z[k]);
     }
+    for (; i < n; i += stride) one(i, pos[3ull * i], pos[3ull * i + 1], pos[3ull * i + 2]);
     __syncthreads();
     for (int k = threadIdx.x; k < kRadixPasses * kRadixBins; k += 256)
         part[(uint64_t)blockIdx.x * kRadixPasses * kRadixBins + k] = h[k];
@@ -272,8 +352,9 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
     const uint32_t n = (uint32_t)ws.n;
     const uint32_t nt = (uint32_t)ws.n_tiles;
     const uint32_t hb = morton_hist_blocks(ws.n);
-    k_morton_hist<<<hb, 256, 0, s>>>(pos, n, ws.prm, ws.keys[0], ws.vals[0], ws.hist_part, ws.lb_words,
-                                     (uint64_t)ws.n_lb_words);
+    const int cube_parts = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));  // as launch_cube
+    k_morton_hist<<<hb, 256, 0, s>>>(pos, n, ws.cube_part, cube_parts, ws.prm, ws.keys[0], ws.vals[0], ws.hist_part,
+                                     ws.lb_words, (uint64_t)ws.n_lb_words);
     k_digit_offsets<<<kRadixPasses, 1024, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
     if (after_keys) {
         hipError_t e = hipEventRecord(after_keys, s);
