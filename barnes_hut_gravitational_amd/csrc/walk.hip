@@ -103,6 +103,8 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
     const uint32_t k = (uint32_t)__popcll(m_open);
     const uint32_t q = lane / kSlot, r = lane % kSlot;
     if (opening) tgt[rank] = xi;
+    wave_lds_sync();
+    const float4 t = r < k ? tgt[r] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
         const uint32_t cc = min(cnt - c0, 64u);
         if (lane < cc) src[lane] = xs[b + c0 + lane];
@@ -111,7 +113,7 @@ __device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint3
             if (r < k) {
                 float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 if (j0 + q < cc) {
-                    const float4 p = src[j0 + q], t = tgt[r];
+                    const float4 p = src[j0 + q];
                     v = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
                 }
                 prod[lane] = v;
@@ -165,6 +167,67 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// A leaf opened by k <= 16 lanes, packed kG >= 4 particles per row as in
+// leaf_packed, with the sums spread over lanes: the accumulator component c
+// of opening lane r is carried by lane 16 c + r, which adds the row's kG
+// products of that component in particle order (one add per product instead
+// of three in the opening lane). The accumulators go to those lanes through
+// LDS before the leaf and come back after it; every accumulator sees the same
+// additions in the same order as its own lane would make.
+template <int kInv, uint32_t kG>
+__device__ __forceinline__ void leaf_chain(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint64_t m_open,
+                                           bool opening, const float4 &xi, float eps2, float &ax, float &ay,
+                                           float &az, float4 *tgt, float4 *src, float *prod, float4 *acc) {
+    constexpr uint32_t kSlot = 64u / kG;  // >= 16 >= k
+    const uint32_t lane = __lane_id();
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_open >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m_open, 0u));
+    const uint32_t k = (uint32_t)__popcll(m_open);
+    const uint32_t q = lane / kSlot, r = lane % kSlot;
+    const uint32_t cr = lane & 15u, cc = lane >> 4;  // chain lane: opening lane cr, component cc
+    const bool chain = cr < k && cc < 3u;
+    if (opening) {
+        tgt[rank] = xi;
+        acc[rank] = make_float4(ax, ay, az, 0.0f);
+    }
+    wave_lds_sync();
+    float a = chain ? reinterpret_cast<const float *>(acc)[4u * cr + cc] : 0.0f;
+    const float4 t = r < k ? tgt[r] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
+        const uint32_t n0 = min(cnt - c0, 64u);
+        if (lane < n0) src[lane] = xs[b + c0 + lane];
+        wave_lds_sync();
+        for (uint32_t j0 = 0; j0 < n0; j0 += kG) {
+            if (r < k) {
+                float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (j0 + q < n0) {
+                    const float4 p = src[j0 + q];
+                    v = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
+                }
+                prod[r * kG + q] = v.x;
+                prod[64u + r * kG + q] = v.y;
+                prod[128u + r * kG + q] = v.z;
+            }
+            wave_lds_sync();
+            if (chain) {
+                const float *pc = prod + 64u * cc + cr * kG;
+#pragma unroll
+                for (uint32_t qq = 0; qq < kG; qq++) a += pc[qq];
+            }
+            wave_lds_sync();
+        }
+    }
+    if (chain) reinterpret_cast<float *>(acc)[4u * cr + cc] = a;
+    wave_lds_sync();
+    if (opening) {
+        const float4 v = acc[rank];
+        ax = v.x;
+        ay = v.y;
+        az = v.z;
+    }
+    wave_lds_sync();
+}
+
 // Sorted targets of this lane's wave: wave slot s of the grid runs target
 // wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
 // schedule get no targets.
@@ -176,7 +239,7 @@ __device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict_
 
 // Wave-private LDS of the packed leaf evaluation.
 struct WalkLds {
-    float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64];
+    float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64], acc[kWalkBlock / 64][64];
 };
 
 // kMin: the wave advances to the minimum of the lanes' `next` (every lane
@@ -241,16 +304,22 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         leaf_packed<kInv, G>(xs, b, cnt, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv], \
                              lds.prod[wv]);                                                                \
         break;
-                    switch (g) {
+#define ORR_LEAF_CHAIN(G)                                                                                 \
+    case G:                                                                                               \
+        leaf_chain<kInv, G>(xs, b, cnt, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv], \
+                            reinterpret_cast<float *>(lds.prod[wv]), lds.acc[wv]);                        \
+        break;
+                    switch (g) {  // g >= 4: at most 16 opening lanes
                         ORR_LEAF_PACKED(2)
-                        ORR_LEAF_PACKED(4)
-                        ORR_LEAF_PACKED(8)
-                        ORR_LEAF_PACKED(16)
-                        ORR_LEAF_PACKED(32)
+                        ORR_LEAF_CHAIN(4)
+                        ORR_LEAF_CHAIN(8)
+                        ORR_LEAF_CHAIN(16)
+                        ORR_LEAF_CHAIN(32)
                         default:
-                            ORR_LEAF_PACKED(64)
+                            ORR_LEAF_CHAIN(64)
                     }
 #undef ORR_LEAF_PACKED
+#undef ORR_LEAF_CHAIN
                 }
                 if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
@@ -272,8 +341,10 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
 // The walk schedule (the order in which target waves start) is computed by
 // the tree build (schedule.h).
 
+// Eight waves per SIMD (at most 64 VGPRs): the occupancy the walk's issue
+// rate needs; without the bound the unrolled leaf sums take more registers.
 template <bool kFastInv, bool kOff32, bool kMin>
-__global__ __launch_bounds__(kWalkBlock) void k_walk_coherent(const float4 *__restrict__ xs,
+__global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
                                                               const uint32_t *__restrict__ perm, uint32_t n,
