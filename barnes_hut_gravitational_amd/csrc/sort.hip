@@ -13,11 +13,13 @@
 //     keys; k_digit_offsets turns them into the first output slot of each
 //     digit in each pass.
 //   * k_onesweep, one launch per pass: a tile of 4096 keys (512 threads x 8)
-//     takes a ticket (its position in the output), ranks its keys stably
-//     inside each wave (lanes with the same digit found with 8 ballots),
-//     publishes its digit counts, and adds the counts of the tiles before it
-//     by decoupled look-back: walking back over predecessors' published words
-//     until one carries an inclusive prefix. Tickets are taken in the order
+//     takes a ticket (its position in the output), counts its digits and
+//     publishes the counts at once, ranks its keys stably inside each wave
+//     (lanes with the same digit found with 8 ballots), and then adds the
+//     counts of the tiles before it by decoupled look-back: walking back over
+//     predecessors' published words, four per step, until one carries an
+//     inclusive prefix. Publishing before the ranking lets the successors'
+//     walks find the counts sooner. Tickets are taken in the order
 //     blocks start, so every predecessor is running or done and publishes its
 //     counts without waiting on anyone; each wait is nevertheless bounded and
 //     reports an error. The tile is then reordered by digit in LDS and
@@ -41,34 +43,49 @@ __device__ __forceinline__ void lb_store(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive prefix over earlier tiles of one value: publish `mine` as an
-// aggregate, walk back to the nearest inclusive word, publish the inclusive
-// value. Returns the exclusive prefix; sets *err on a wait that never ends.
-__device__ __forceinline__ uint32_t look_back(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine,
-                                              uint32_t *err) {
-    if (tile == 0) {
-        lb_store(words, kStInclusive | mine);
-        return 0;
-    }
-    lb_store(words + (uint64_t)tile * stride, kStAggregate | mine);
+#ifndef ORR_LB_WIN
+#define ORR_LB_WIN 4
+#endif
+// Publishes a tile's value for one digit: inclusive for tile 0, else an
+// aggregate that successors can add while the tile works on.
+__device__ __forceinline__ void lb_publish(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine) {
+    lb_store(words + (uint64_t)tile * stride, (tile == 0 ? kStInclusive : kStAggregate) | mine);
+}
+
+// Exclusive prefix over earlier tiles of one value, after lb_publish: walks
+// back over the predecessors' words, ORR_LB_WIN at a time, adding aggregates
+// until an inclusive value, then publishes its own inclusive value. Sets
+// *err on a wait that never ends.
+__device__ __forceinline__ uint32_t lb_resolve(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine,
+                                               uint32_t *err) {
+    if (tile == 0) return 0;
     uint32_t excl = 0, spins = 0;
     int64_t t = (int64_t)tile - 1;
-    while (t >= 0) {
-        const uint64_t v = lb_load(words + (uint64_t)t * stride);
-        const uint64_t st = v & ~0xffffffffull;
-        if (st == kStInclusive) {
-            excl += (uint32_t)v;
-            break;
+    while (true) {
+        uint64_t v[ORR_LB_WIN];
+#pragma unroll
+        for (int k = 0; k < ORR_LB_WIN; k++)
+            v[k] = t - k >= 0 ? lb_load(words + (uint64_t)(t - k) * stride) : kStInclusive;
+        int used = 0;
+        bool done = false;
+#pragma unroll
+        for (int k = 0; k < ORR_LB_WIN; k++) {
+            if (done || used < k) continue;
+            const uint64_t st = v[k] & ~0xffffffffull;
+            if (st == kStInclusive) {
+                excl += (uint32_t)v[k];
+                done = true;
+            } else if (st == kStAggregate) {
+                excl += (uint32_t)v[k];
+                used = k + 1;
+            }
         }
-        if (st == kStAggregate) {
-            excl += (uint32_t)v;
-            t--;
-            continue;
-        }
-        if (++spins > kSpinLimit) {  // a predecessor never published: give up, flagged
+        if (done) break;
+        if (used == 0 && ++spins > kSpinLimit) {  // a predecessor never published: give up, flagged
             atomicOr(err, 2u);
             break;
         }
+        t -= used;
     }
     lb_store(words + (uint64_t)tile * stride, kStInclusive | (excl + mine));
     return excl;
@@ -258,12 +275,14 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
     __shared__ uint32_t s_vals[kTile];
     __shared__ uint32_t s_delta[kRadixBins];  // output slot minus tile slot of each digit
     __shared__ uint32_t s_wsum[kRadixBins / 64];
+    __shared__ uint32_t s_hist[kRadixBins];
     __shared__ uint32_t s_tile;
     uint32_t(*s_cnt)[kRadixBins] = reinterpret_cast<uint32_t(*)[kRadixBins]>(s_keys);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     const int shift = pass * kRadixBits;
     for (int k = threadIdx.x; k < kWaves * kRadixBins; k += kTileThreads) (&s_cnt[0][0])[k] = 0;
+    if (threadIdx.x < kRadixBins) s_hist[threadIdx.x] = 0;
     if (threadIdx.x == 0) s_tile = atomicAdd(&prm->sort_ticket[pass], 1u);
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -278,6 +297,12 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         key[r] = e < n ? keys_in[e] : 0ull;
         val[r] = e < n ? vals_in[e] : 0u;
     }
+    // The tile's digit counts first, published at once, so that later tiles
+    // can add them while this one ranks its keys.
+    for (int r = 0; r < kTileItems; r++)
+        if (base + (uint64_t)r * 64 + lane < n) atomicAdd(&s_hist[(uint32_t)(key[r] >> shift) & (kRadixBins - 1)], 1u);
+    __syncthreads();
+    if (threadIdx.x < kRadixBins) lb_publish(lb_words + threadIdx.x, tile, kRadixBins, s_hist[threadIdx.x]);
     for (int r = 0; r < kTileItems; r++) {
         const bool valid = base + (uint64_t)r * 64 + lane < n;
         const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
@@ -310,7 +335,7 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         const int d = threadIdx.x;
         uint32_t local = inc - tot;
         for (int k = 0; k < w; k++) local += s_wsum[k];
-        const uint32_t excl = look_back(lb_words + d, tile, kRadixBins, tot, &prm->bad_input);
+        const uint32_t excl = lb_resolve(lb_words + d, tile, kRadixBins, tot, &prm->bad_input);
         s_delta[d] = digit_offs[pass * kRadixBins + d] + excl - local;
         uint32_t run = local;
         for (int k = 0; k < kWaves; k++) {  // in place: column d is this thread's alone
