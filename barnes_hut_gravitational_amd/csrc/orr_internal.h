@@ -72,7 +72,8 @@ struct Workspace {
     uint32_t *base;        // [n + 1] nodes started by earlier particles of the same 256-particle tile
     uint32_t *tile_sum;    // [tiles + 1] nodes started per 256-particle tile, then their exclusive scan
     NodeRec *nodes;        // [max_nodes]
-    float4 *msum;          // [max_nodes] (S, M), unnormalised sums for the parent
+    float4 *msum;          // [max_nodes >= n] (S, M), unnormalised sums for the parent; before the
+                           // build, the input particles as float4 for the sort's gather
     uint8_t *level;        // [max_nodes]
     uint32_t *cut_list;    // [max_nodes] roots of the subtrees finished by one workgroup each
     uint32_t *top_list;    // [max_top] nodes above the cut

@@ -154,10 +154,14 @@ __device__ __forceinline__ void cube_from_partials(const float *__restrict__ par
 }
 
 // Keys and the identity payload; each block's 8 digit histograms to
-// part[block][pass][digit]; zeroes the look-back words of the build. Each
+// part[block][pass][digit]; zeroes the look-back words of the build; copies
+// every particle as one float4 (x, y, z, m) in input order to xs0, which the
+// last pass gathers from (one aligned load per particle instead of a 12-byte
+// and a 4-byte one). Each
 // block first forms the root cube from the partials; block 0 also stores it
 // in prm with the input flag and resets the build's device counters.
-__global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ pos, uint32_t n,
+__global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ pos, const float *__restrict__ mass,
+                                                     float4 *__restrict__ xs0, uint32_t n,
                                                      const float *__restrict__ cube_part, int cube_parts,
                                                      DevParams *__restrict__ prm, uint64_t *__restrict__ keys,
                                                      uint32_t *__restrict__ idx, uint32_t *__restrict__ part,
@@ -190,28 +194,30 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
     __syncthreads();
     const float lx = s_cube[0], ly = s_cube[1], lz = s_cube[2], sc = s_cube[3];
     const uint32_t stride = gridDim.x * 256u;
-    auto one = [&](uint32_t i, float x, float y, float z) {
+    auto one = [&](uint32_t i, float x, float y, float z, float m) {
         const uint64_t key = (spread3(quantise(x, lx, sc)) << 2) | (spread3(quantise(y, ly, sc)) << 1) |
                              spread3(quantise(z, lz, sc));
         keys[i] = key;
         idx[i] = i;
+        xs0[i] = make_float4(x, y, z, m);
         for (int p = 0; p < kRadixPasses; p++)
             atomicAdd(&h[p * kRadixBins + ((uint32_t)(key >> (p * kRadixBits)) & (kRadixBins - 1))], 1u);
     };
     uint32_t i = blockIdx.x * 256u + threadIdx.x;
     for (; i + 3u * stride < n; i += 4u * stride) {  // four particles' loads in flight
-        float x[4], y[4], z[4];
+        float x[4], y[4], z[4], m[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             const uint64_t j = i + (uint64_t)k * stride;
             x[k] = pos[3 * j];
             y[k] = pos[3 * j + 1];
             z[k] = pos[3 * j + 2];
+            m[k] = mass[j];
         }
 #pragma unroll
-        for (int k = 0; k < 4; k++) one(i + k * stride, x[k], y[k], z[k]);
+        for (int k = 0; k < 4; k++) one(i + k * stride, x[k], y[k], z[k], m[k]);
     }
-    for (; i < n; i += stride) one(i, pos[3ull * i], pos[3ull * i + 1], pos[3ull * i + 2]);
+    for (; i < n; i += stride) one(i, pos[3ull * i], pos[3ull * i + 1], pos[3ull * i + 2], mass[i]);
     __syncthreads();
     for (int k = threadIdx.x; k < kRadixPasses * kRadixBins; k += 256)
         part[(uint64_t)blockIdx.x * kRadixPasses * kRadixBins + k] = h[k];
@@ -267,8 +273,8 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
                                                   const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
                                                   const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
                                                   DevParams *prm, uint64_t *__restrict__ keys_out,
-                                                  uint32_t *__restrict__ vals_out, const float *__restrict__ pos,
-                                                  const float *__restrict__ mass, float4 *__restrict__ xs) {
+                                                  uint32_t *__restrict__ vals_out, const float4 *__restrict__ xs0,
+                                                  float4 *__restrict__ xs) {
     constexpr int kWaves = kTileThreads / 64;
     static_assert(kWaves * kRadixBins * 4 <= kTile * 8, "counts fit in the key buffer");
     __shared__ uint64_t s_keys[kTile];  // first the per-wave digit counts, then the tile's keys by digit
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
         keys_out[o] = k;
         vals_out[o] = v;
-        if (kGather) xs[o] = make_float4(pos[3ull * v], pos[3ull * v + 1], pos[3ull * v + 2], mass[v]);
+        if (kGather) xs[o] = xs0[v];
     }
 }
 
@@ -378,8 +384,10 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
     const uint32_t nt = (uint32_t)ws.n_tiles;
     const uint32_t hb = morton_hist_blocks(ws.n);
     const int cube_parts = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));  // as launch_cube
-    k_morton_hist<<<hb, 256, 0, s>>>(pos, n, ws.cube_part, cube_parts, ws.prm, ws.keys[0], ws.vals[0], ws.hist_part,
-                                     ws.lb_words, (uint64_t)ws.n_lb_words);
+    // msum (at least n float4) holds the particles in input order until the
+    // moments need it: the last pass gathers one aligned float4 per particle.
+    k_morton_hist<<<hb, 256, 0, s>>>(pos, mass, ws.msum, n, ws.cube_part, cube_parts, ws.prm, ws.keys[0], ws.vals[0],
+                                     ws.hist_part, ws.lb_words, (uint64_t)ws.n_lb_words);
     k_digit_offsets<<<kRadixPasses, 1024, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
     if (after_keys) {
         hipError_t e = hipEventRecord(after_keys, s);
@@ -390,10 +398,10 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
         uint64_t *words = ws.lb_words + (uint64_t)pass * nt * kRadixBins;
         if (pass + 1 < kRadixPasses)
             k_onesweep<false><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
-                                                 ws.keys[dst], ws.vals[dst], nullptr, nullptr, nullptr);
+                                                 ws.keys[dst], ws.vals[dst], nullptr, nullptr);
         else
             k_onesweep<true><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
-                                                ws.keys[dst], ws.vals[dst], pos, mass, ws.xs);
+                                                ws.keys[dst], ws.vals[dst], ws.msum, ws.xs);
     }
     return hipGetLastError();
 }
