@@ -11,6 +11,7 @@
 
 #include "orr.h"
 #include "orr_internal.h"
+#include "schedule.h"
 
 namespace orr {
 
@@ -70,7 +71,7 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     w.kids = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * 9 * w.max_top));
     w.n_waves = ceil_div(n, 64);
     w.wave_cost = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * w.n_waves));
-    w.wave_order = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * w.n_waves));
+    w.wave_order = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * schedule_slots(w.n_waves)));
     w.n = n;
     w.leaf_cap = leaf_cap;
     w.max_nodes = nb;

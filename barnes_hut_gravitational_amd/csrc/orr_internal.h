@@ -79,7 +79,7 @@ struct Workspace {
     uint32_t *top_list;    // [max_top] nodes above the cut
     uint32_t *kids;        // [9 max_top] child count and children of each node above the cut
     uint32_t *wave_cost;   // [n_waves] estimated run time of a wave of 64 sorted targets
-    uint32_t *wave_order;  // [n_waves] walk schedule: target waves by decreasing cost
+    uint32_t *wave_order;  // walk schedule: 8 XCD lists of target waves by decreasing cost, their lengths
     int64_t n_waves;       // ceil(n / 64)
     int64_t max_top;
     int64_t n;

@@ -20,59 +20,86 @@ namespace orr {
 // part of the whole launch. The schedule decides only when a wave runs,
 // never what it computes.
 constexpr int kWaveOrderThreads = kWaveCostBins / 2;
+constexpr uint32_t kScheduleRegions = 64;
+// Slots of the schedule buffer for n_waves waves: the 8 lists and their lengths.
+inline int64_t schedule_slots(int64_t n_waves) {
+    return (int64_t)kScheduleRegions * ((n_waves + kScheduleRegions - 1) / kScheduleRegions) + 8;
+}
 static_assert(64 * kMaxLevel + 32 * kMaxLevel < kWaveCostBins, "wave cost range");
 
-// One block: counting sort of the waves by decreasing cost. Waves of equal
-// cost may come out in any order; in practice the LDS atomics serve a wave's
-// lanes in lane order, which keeps neighbouring waves of equal cost together
-// (spreading equal costs over sub-bins to cut atomic conflicts made the
-// 8M walk 2 % slower). The first kOrderCached costs of each thread are loaded
-// once, all at the start.
-constexpr int kOrderCached = 16;
-
+// One block: the schedule as 8 lists, one per XCD (the walk's block b runs on
+// XCD b mod 8 and takes its waves from list b mod 8, in block order). The
+// waves are cut into kScheduleRegions contiguous regions of R =
+// ceil(n_waves / kScheduleRegions) waves (neighbouring targets, whose walks
+// share nodes and leaves in the XCD's L2); the regions are dealt to the lists
+// in a snake over their total cost (ranks 0..7 to lists 0..7, ranks 8..15 to
+// lists 7..0, ...), so every list gets kScheduleRegions / 8 regions and
+// nearly the same work. List x is stored at order[x L .. x L + len_x) with L =
+// R kScheduleRegions / 8, its waves in decreasing cost (longest first);
+// len_x at order[8 L + x]. Equal costs keep the LDS atomics' order.
+constexpr uint32_t kOrderSlots = 8u * kWaveCostBins;
 __device__ __forceinline__ void wave_order_block(const uint32_t *__restrict__ cost, uint32_t n_waves,
                                                  uint32_t *__restrict__ order) {
-    __shared__ uint32_t bins[kWaveCostBins];
+    __shared__ uint32_t slots[kOrderSlots];
     __shared__ uint32_t wsum[kWaveOrderThreads / 64];
+    __shared__ uint32_t rcost[kScheduleRegions];
+    __shared__ uint32_t rlist[kScheduleRegions];
     const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
-    uint32_t cb[kOrderCached];  // cost bins of waves t + j kWaveOrderThreads
-#pragma unroll
-    for (int j = 0; j < kOrderCached; j++) {
-        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
-        cb[j] = w < n_waves ? min(cost[w], (uint32_t)kWaveCostBins - 1u) : 0u;
+    const uint32_t R = (n_waves + kScheduleRegions - 1u) / kScheduleRegions;
+    for (uint32_t b = t; b < kOrderSlots; b += kWaveOrderThreads) slots[b] = 0u;
+    if (t < kScheduleRegions) rcost[t] = 0u;
+    __syncthreads();
+    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads) atomicAdd(&rcost[w / R], cost[w]);
+    __syncthreads();
+    if (t < kScheduleRegions) {  // rank by decreasing cost (ties by index), snake over the 8 lists
+        const uint32_t mine = rcost[t];
+        uint32_t rank = 0;
+        for (uint32_t k = 0; k < kScheduleRegions; k++) {
+            const uint32_t o = rcost[k];
+            rank += (o > mine || (o == mine && k < t)) ? 1u : 0u;
+        }
+        const uint32_t round = rank / 8u, pos = rank % 8u;
+        rlist[t] = (round & 1u) ? 7u - pos : pos;
     }
-    for (uint32_t b = t; b < (uint32_t)kWaveCostBins; b += kWaveOrderThreads) bins[b] = 0u;
     __syncthreads();
+    auto slot_of = [&](uint32_t w) {
+        const uint32_t c = min(cost[w], (uint32_t)kWaveCostBins - 1u);
+        return rlist[w / R] * (uint32_t)kWaveCostBins + ((uint32_t)kWaveCostBins - 1u - c);
+    };
+    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads) atomicAdd(&slots[slot_of(w)], 1u);
+    __syncthreads();
+    // list x's segment starts at x L: scan each list's 2048 bins separately.
+    // 8 lists x 2048 bins; thread t owns list t / 128, bins 16 (t % 128) .. + 15.
+    const uint32_t L = (kScheduleRegions / 8u) * R;
+    const uint32_t list = t / 128u, part = t % 128u;
+    uint32_t c[16], tot = 0;
 #pragma unroll
-    for (int j = 0; j < kOrderCached; j++)
-        if (t + (uint32_t)j * kWaveOrderThreads < n_waves) atomicAdd(&bins[cb[j]], 1u);
-    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads)
-        atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
-    __syncthreads();
-    // Exclusive scan in decreasing cost; thread t owns bins b0 = top - 2t and b0 - 1.
-    const uint32_t b0 = (uint32_t)kWaveCostBins - 1u - 2u * t, b1 = b0 - 1u;
-    const uint32_t c0 = bins[b0], c1 = bins[b1];
-    uint32_t x = c0 + c1;
+    for (int k = 0; k < 16; k++) {
+        c[k] = slots[list * kWaveCostBins + 16u * part + k];
+        tot += c[k];
+    }
+    uint32_t x = tot;
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= (uint32_t)o) x += y;
     }
     if (lane == 63u) wsum[wv] = x;
     __syncthreads();
-    uint32_t before = 0u;
-    for (uint32_t k = 0; k < wv; k++) before += wsum[k];
-    const uint32_t excl = before + x - (c0 + c1);
-    bins[b0] = excl;
-    bins[b1] = excl + c0;
-    __syncthreads();
+    uint32_t run = list * L + x - tot;
+    if (wv & 1u) run += wsum[wv - 1];  // two waves per list
 #pragma unroll
-    for (int j = 0; j < kOrderCached; j++) {
-        const uint32_t w = t + (uint32_t)j * kWaveOrderThreads;
-        if (w < n_waves) order[atomicAdd(&bins[cb[j]], 1u)] = w;
+    for (int k = 0; k < 16; k++) {
+        slots[list * kWaveCostBins + 16u * part + k] = run;
+        run += c[k];
     }
-    for (uint32_t w = t + kOrderCached * kWaveOrderThreads; w < n_waves; w += kWaveOrderThreads) {
-        const uint32_t pos = atomicAdd(&bins[min(cost[w], (uint32_t)kWaveCostBins - 1u)], 1u);
-        order[pos] = w;
+    __syncthreads();
+    for (uint32_t w = t; w < n_waves; w += kWaveOrderThreads) order[atomicAdd(&slots[slot_of(w)], 1u)] = w;
+    // list lengths for the walk, after the 8 list segments: order[8 L + x]
+    if (t < 8u) {
+        uint32_t len = 0;
+        for (uint32_t r = 0; r < kScheduleRegions; r++)
+            if (rlist[r] == t) len += min(R, n_waves - min(n_waves, r * R));
+        order[8u * L + t] = len;
     }
 }
 

@@ -20,11 +20,13 @@
 //
 // Both add the same terms in the same order with the same float operations,
 // so their accelerations are identical bit for bit and their visits_own,
-// n_pp and n_pc equal the oracle's. Lane i handles sorted target i; outputs
-// go straight to the caller's order through perm (the scatter step of the
-// performance page's "Where one evaluation goes" table).
+// n_pp and n_pc equal the oracle's. Each lane handles one sorted target (a
+// wave the 64 targets 64 w .. 64 w + 63); outputs go straight to the
+// caller's order through perm (the scatter step of the performance page's
+// "Where one evaluation goes" table).
 #include "orr_internal.h"
 #include "term.h"
+#include "schedule.h"
 #include "walk_common.h"
 
 #ifndef ORR_PACK_KMAX
@@ -228,12 +230,15 @@ __device__ __forceinline__ void leaf_chain(const float4 *__restrict__ xs, uint32
     wave_lds_sync();
 }
 
-// Sorted targets of this lane's wave: wave slot s of the grid runs target
-// wave order[s] (targets 64 order[s] .. 64 order[s] + 63). Slots past the
-// schedule get no targets.
+// Sorted targets of this lane's wave: block b runs on XCD b mod 8 and takes
+// its waves from that XCD's list of the schedule, in block order (wave slot s
+// of the XCD runs list entry s: targets 64 w .. 64 w + 63 of wave w). Slots
+// past the list get no targets.
 __device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict__ order, uint32_t n_waves) {
-    const uint32_t slot = blockIdx.x * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t w = slot < n_waves ? min(order[slot], n_waves) : n_waves;
+    const uint32_t L = (kScheduleRegions / 8u) * ((n_waves + kScheduleRegions - 1u) / kScheduleRegions);
+    const uint32_t x = blockIdx.x & 7u;
+    const uint32_t s = (blockIdx.x >> 3) * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t w = s < order[8u * L + x] ? min(order[x * L + s], n_waves) : n_waves;
     return w * 64u + (threadIdx.x & 63u);
 }
 
@@ -338,8 +343,8 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
-// The walk schedule (the order in which target waves start) is computed by
-// the tree build (schedule.h).
+// The walk schedule (which waves each XCD runs, longest first) is computed
+// by the tree build (schedule.h).
 
 // Eight waves per SIMD (at most 64 VGPRs): the occupancy the walk's issue
 // rate needs; without the bound the unrolled leaf sums take more registers.
@@ -441,8 +446,11 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, float eps2, float theta2
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
     if (mode != kWalkIndependent) {
         const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
+        // 8 XCD lists of up to L waves each (scheduled_target)
+        const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(ws.n_waves, (int64_t)kScheduleRegions);
+        const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64));
 #define ORR_COHERENT(OFF32, MIN)                                                                               \
-    k_walk_coherent<kFast, OFF32, MIN><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
+    k_walk_coherent<kFast, OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
                                                                      eps2, theta2, ws.wave_order, nw, out)
         if (mode == kWalkCoherentMin) {
             if (off32)
