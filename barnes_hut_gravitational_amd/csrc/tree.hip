@@ -392,10 +392,10 @@ __device__ __forceinline__ void finish_top(uint32_t k, uint32_t nk, const uint32
     store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
 }
 
-// k_moments_top: block 0 finishes the moments above the cut; block 1 orders
-// the coherent walk's target waves (schedule.h), independent work of one
-// block that runs beside it instead of in a launch of its own.
-static_assert(kWaveOrderThreads == 1024, "the schedule block has the moments block's size");
+// k_moments_top: block 0 finishes the moments above the cut; blocks 1..8
+// build the coherent walk's 8 target-wave lists (schedule.h), independent
+// work that runs beside it instead of in a launch of its own.
+static_assert(kWaveOrderThreads == 1024, "the schedule blocks have the moments block's size");
 
 __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__ xs, NodeRec *nodes,
                                                       const uint8_t *__restrict__ level,
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
                                                       const DevParams *__restrict__ prm, float4 *msum,
                                                       const uint32_t *__restrict__ wave_cost, uint32_t n_waves,
                                                       uint32_t *__restrict__ wave_order) {
-    if (blockIdx.x == 1) {
-        wave_order_block(wave_cost, n_waves, wave_order);
+    if (blockIdx.x >= 1) {
+        wave_order_list(wave_cost, n_waves, wave_order, blockIdx.x - 1u);
         return;
     }
     __shared__ int s_lmin, s_lmax;
@@ -508,7 +508,7 @@ hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 2));
     k_moments_cut<<<blocks, 256, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.cut_list, ws.prm, (uint32_t)ws.max_nodes,
                                          ws.msum);
-    k_moments_top<<<2, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum,
+    k_moments_top<<<9, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum,
                                      ws.wave_cost, (uint32_t)ws.n_waves, ws.wave_order);
     return hipGetLastError();
 }
