@@ -8,6 +8,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "orr.h"
 #include "orr_internal.h"
@@ -72,6 +73,7 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     w.n_waves = ceil_div(n, 64);
     w.wave_cost = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * w.n_waves));
     w.wave_order = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * schedule_slots(w.n_waves)));
+    w.range_order = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * schedule_slots(w.n_waves)));
     w.n = n;
     w.leaf_cap = leaf_cap;
     w.max_nodes = nb;
@@ -297,6 +299,59 @@ orr_status orr_tree_walk_descend(const orr_tree *tree, float eps, float theta, i
                                  uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                                  uint32_t *n_pc) {
     return walk_grouped_entry(tree, eps, theta, group_width, true, acc, visits_own, visits_stepped, n_pp, n_pc);
+}
+
+orr_status orr_tree_walk_range(const orr_tree *tree, float eps, float theta, orr_traversal traversal,
+                               int64_t first, int64_t count, float *acc, uint32_t *visits_own,
+                               uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    orr_status st = check_walk_args(eps, theta, (int)traversal);
+    if (st != ORR_OK) return st;
+    const Workspace &ws = tree->ws;
+    if (first < 0 || count < 0 || first > ws.n || count > ws.n - first)
+        return fail(ORR_ERR_RANGE, "targets [%lld, %lld + %lld) are not inside [0, %lld)", (long long)first,
+                    (long long)first, (long long)count, (long long)ws.n);
+    if (count == 0) return ORR_OK;  // an empty range (bounds of orr_tree_shard_bounds may repeat n)
+    if (first % 64 != 0 || (count % 64 != 0 && first + count != ws.n))
+        return fail(ORR_ERR_RANGE, "targets [%lld, %lld + %lld) are not whole waves of 64", (long long)first,
+                    (long long)first, (long long)count);
+    hipError_t e;
+    const bool coherent = traversal == ORR_TRAVERSAL_COHERENT;
+    if (coherent && (e = launch_range_schedule(ws, first / 64, ceil_div(count, 64), tree->stream)) != hipSuccess)
+        return hip_fail(e, "range schedule");
+    e = launch_walk_range(ws, coherent ? kWalkCoherent : kWalkIndependent, WalkRange{first, count, ws.range_order},
+                          eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "range walk");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_tree_shard_bounds(const orr_tree *tree, int32_t k, int64_t *bounds) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree || !bounds) return fail(ORR_ERR_INVALID_ARG, "tree and bounds must not be NULL");
+    if (k < 1 || k > 65536) return fail(ORR_ERR_RANGE, "k = %d is outside [1, 65536]", k);
+    const Workspace &ws = tree->ws;
+    std::vector<uint32_t> cost((size_t)ws.n_waves);
+    hipError_t e = hipMemcpyAsync(cost.data(), ws.wave_cost, cost.size() * sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    if ((e = hipStreamSynchronize(tree->stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    uint64_t total = 0;
+    for (uint32_t c : cost) total += c;
+    // bound j: the first wave w with (cost of waves < w) * k >= j * total
+    bounds[0] = 0;
+    uint64_t before = 0;
+    size_t w = 0;
+    for (int32_t j = 1; j < k; j++) {
+        while (w < cost.size() && before * (uint64_t)k < (uint64_t)j * total) before += cost[w++];
+        bounds[j] = std::min<int64_t>((int64_t)w * 64, ws.n);
+    }
+    bounds[k] = ws.n;
+    return ORR_OK;
+    ORR_GUARD_END
 }
 
 orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float eps, float theta,

@@ -80,6 +80,7 @@ struct Workspace {
     uint32_t *kids;        // [9 max_top] child count and children of each node above the cut
     uint32_t *wave_cost;   // [n_waves] estimated run time of a wave of 64 sorted targets
     uint32_t *wave_order;  // walk schedule: 8 XCD lists of target waves by decreasing cost, their lengths
+    uint32_t *range_order;  // the same for the waves of one target range (range walks)
     int64_t n_waves;       // ceil(n / 64)
     int64_t max_top;
     int64_t n;
@@ -114,6 +115,19 @@ enum { kWalkIndependent = 0, kWalkCoherent = 1, kWalkCoherentMin = 2 };
 hipError_t launch_walk(const Workspace &ws, int mode, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s);
+// Sorted targets [first, first + count) of whole waves (first a multiple of
+// 64; count too unless the range ends at n); order: the coherent walk's
+// schedule of the range's waves (ws.wave_order for all targets, else
+// ws.range_order after launch_range_schedule).
+struct WalkRange {
+    int64_t first, count;
+    const uint32_t *order;
+};
+hipError_t launch_walk_range(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
+                             float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                             uint32_t *n_pc, hipStream_t s);
+// The walk schedule of waves [wave0, wave0 + n_waves) into ws.range_order.
+hipError_t launch_range_schedule(const Workspace &ws, int64_t wave0, int64_t n_waves, hipStream_t s);
 // Group widths 1, 2, 4, ..., 64 (hipErrorInvalidValue otherwise); descend:
 // the descend-together variant.
 hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, float eps2, float theta2, float *acc,

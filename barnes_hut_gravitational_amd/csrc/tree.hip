@@ -513,6 +513,19 @@ hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The walk schedule of a range of target waves (the range walk), one block
+// per XCD list as in k_moments_top.
+__global__ __launch_bounds__(kWaveOrderThreads) void k_range_schedule(const uint32_t *__restrict__ wave_cost,
+                                                                      uint32_t n_waves,
+                                                                      uint32_t *__restrict__ order) {
+    wave_order_list(wave_cost, n_waves, order, blockIdx.x);
+}
+
+hipError_t launch_range_schedule(const Workspace &ws, int64_t wave0, int64_t n_waves, hipStream_t s) {
+    k_range_schedule<<<8, kWaveOrderThreads, 0, s>>>(ws.wave_cost + wave0, (uint32_t)n_waves, ws.range_order);
+    return hipGetLastError();
+}
+
 hipError_t launch_tree_info(const Workspace &ws, hipStream_t s) {
     k_info_zero<<<1, 1, 0, s>>>(ws.prm);
     k_info<<<(unsigned)ceil_div(ws.max_nodes, 256), 256, 0, s>>>(ws.nodes, ws.level, (uint32_t)ws.max_nodes, ws.prm);

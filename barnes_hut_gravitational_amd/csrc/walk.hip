@@ -232,14 +232,16 @@ __device__ __forceinline__ void leaf_chain(const float4 *__restrict__ xs, uint32
 
 // Sorted targets of this lane's wave: block b runs on XCD b mod 8 and takes
 // its waves from that XCD's list of the schedule, in block order (wave slot s
-// of the XCD runs list entry s: targets 64 w .. 64 w + 63 of wave w). Slots
-// past the list get no targets.
-__device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict__ order, uint32_t n_waves) {
+// of the XCD runs list entry s: targets 64 (wave0 + w) .. + 63 of the
+// schedule's wave w, whose waves start at wave0). Slots past the list get the
+// first target past the schedule's waves, which no lane walks.
+__device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict__ order, uint32_t n_waves,
+                                                     uint32_t wave0) {
     const uint32_t L = (kScheduleRegions / 8u) * ((n_waves + kScheduleRegions - 1u) / kScheduleRegions);
     const uint32_t x = blockIdx.x & 7u;
     const uint32_t s = (blockIdx.x >> 3) * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t w = s < order[8u * L + x] ? min(order[x * L + s], n_waves) : n_waves;
-    return w * 64u + (threadIdx.x & 63u);
+    return (wave0 + w) * 64u + (threadIdx.x & 63u);
 }
 
 // Wave-private LDS of the packed leaf evaluation.
@@ -355,9 +357,9 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8
                                                               const uint32_t *__restrict__ perm, uint32_t n,
                                                               uint32_t max_nodes, float eps2, float theta2,
                                                               const uint32_t *__restrict__ order,
-                                                              uint32_t n_waves, WalkOut out) {
+                                                              uint32_t n_waves, uint32_t wave0, WalkOut out) {
     __shared__ WalkLds lds;
-    const uint32_t i = scheduled_target(order, n_waves);
+    const uint32_t i = scheduled_target(order, n_waves, wave0);  // walked if i < n
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
         walk_coherent<kInvIeee, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
@@ -404,10 +406,10 @@ template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
                                                                  const NodeRec *__restrict__ nodes,
                                                                  const DevParams *__restrict__ prm,
-                                                                 const uint32_t *__restrict__ perm, uint32_t n,
-                                                                 uint32_t max_nodes, float eps2, float theta2,
-                                                                 WalkOut out) {
-    const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
+                                                                 const uint32_t *__restrict__ perm, uint32_t first,
+                                                                 uint32_t n, uint32_t max_nodes, float eps2,
+                                                                 float theta2, WalkOut out) {
+    const uint32_t i = first + xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     if (!kFastInv)
@@ -438,20 +440,20 @@ __global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint6
 __global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
 
 template <bool kFast>
-hipError_t launch_walk_t(const Workspace &ws, int mode, float eps2, float theta2, const WalkOut &out,
-                         hipStream_t s) {
-    const uint32_t n = (uint32_t)ws.n;
+hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
+                         const WalkOut &out, hipStream_t s) {
     const uint32_t nb = (uint32_t)ws.max_nodes;
-    const uint32_t nw = (uint32_t)ws.n_waves;
-    const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
+    const uint32_t end = (uint32_t)(rg.first + rg.count);  // targets [first, end) are walked
     if (mode != kWalkIndependent) {
         const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
+        const int64_t nw = ceil_div(rg.count, (int64_t)64);
         // 8 XCD lists of up to L waves each (scheduled_target)
-        const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(ws.n_waves, (int64_t)kScheduleRegions);
+        const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(nw, (int64_t)kScheduleRegions);
         const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64));
-#define ORR_COHERENT(OFF32, MIN)                                                                               \
-    k_walk_coherent<kFast, OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
-                                                                     eps2, theta2, ws.wave_order, nw, out)
+        const uint32_t wave0 = (uint32_t)(rg.first / 64);
+#define ORR_COHERENT(OFF32, MIN)                                                                                  \
+    k_walk_coherent<kFast, OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, nb, \
+                                                                     eps2, theta2, rg.order, (uint32_t)nw, wave0, out)
         if (mode == kWalkCoherentMin) {
             if (off32)
                 ORR_COHERENT(true, true);
@@ -464,8 +466,9 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, float eps2, float theta2
         }
 #undef ORR_COHERENT
     } else {
-        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb,
-                                                                eps2, theta2, out);
+        const unsigned blocks = (unsigned)ceil_div(rg.count, (int64_t)kWalkBlock);
+        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0],
+                                                                (uint32_t)rg.first, end, nb, eps2, theta2, out);
     }
     return hipGetLastError();
 }
@@ -478,9 +481,16 @@ bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
 hipError_t launch_walk(const Workspace &ws, int mode, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                        hipStream_t s) {
+    return launch_walk_range(ws, mode, WalkRange{0, ws.n, ws.wave_order}, eps2, theta2, acc, visits_own,
+                             visits_stepped, n_pp, n_pc, s);
+}
+
+hipError_t launch_walk_range(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
+                             float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
+                             uint32_t *n_pc, hipStream_t s) {
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, mode, eps2, theta2, out, s);
-    return launch_walk_t<false>(ws, mode, eps2, theta2, out, s);
+    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, mode, rg, eps2, theta2, out, s);
+    return launch_walk_t<false>(ws, mode, rg, eps2, theta2, out, s);
 }
 
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,

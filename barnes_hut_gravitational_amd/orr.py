@@ -20,8 +20,8 @@ ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_
 TRAVERSALS = {"independent": 0, "coherent": 1}
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
-            "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_eval_forces",
-            "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
+            "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_range",
+            "orr_tree_shard_bounds", "orr_eval_forces", "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
             "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_walk_grouped.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_descend.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_min_advance.argtypes = [_vp, f32, f32, _vp, _vp, _vp, _vp, _vp]
+        L.orr_tree_walk_range.argtypes = [_vp, f32, f32, ctypes.c_int, i64, i64, _vp, _vp, _vp, _vp, _vp]
+        L.orr_tree_shard_bounds.argtypes = [_vp, i32, ctypes.POINTER(i64)]
         L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
                                       _vp, ctypes.POINTER(Timings)]
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
@@ -79,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_free.argtypes = [_vp]
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
-                     "orr_tree_walk_min_advance", "orr_eval_forces",
+                     "orr_tree_walk_min_advance", "orr_tree_walk_range", "orr_tree_shard_bounds",
+                     "orr_eval_forces",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
                      "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
@@ -219,6 +222,21 @@ class Tree:
         acc, cnt = out if out is not None else _outputs(self.n, self.device)
         _check(lib().orr_tree_walk_min_advance(self._h, eps, theta, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+
+    def walk_range(self, first, count, eps=0.05, theta=0.5, traversal="coherent", out=None) -> Result:
+        """The walk of the sorted targets [first, first + count), whole waves
+        (orr_tree_walk_range); writes only those targets' outputs."""
+        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        _check(lib().orr_tree_walk_range(self._h, eps, theta, TRAVERSALS[traversal], first, count, _ptr(acc),
+                                         *[_ptr(c) for c in cnt]))
+        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+
+    def shard_bounds(self, k: int) -> list:
+        """k + 1 bounds of contiguous target ranges of nearly equal estimated
+        walk cost (orr_tree_shard_bounds); synchronises the stream."""
+        b = (ctypes.c_int64 * (k + 1))()
+        _check(lib().orr_tree_shard_bounds(self._h, k, b))
+        return list(b)
 
     def info(self) -> dict:
         ti = TreeInfo()

@@ -33,12 +33,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="plummer_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-trials", type=int, default=5,
+    ap.add_argument("--cpu-trials", type=int, default=10,
                     help="whole oracle evaluations timed for the CPU baseline (median)")
     ap.add_argument("--no-direct", action="store_true",
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the group-width sweep of the walk (orr_tree_walk_grouped)")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the one-GPU share leg (range walks of the 8M merger split 8 ways)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -166,6 +168,54 @@ def advance_leg(tree, acc, cnt, stream, trials=6):
     return out
 
 
+def shard_leg(dev, stream, k=8, trials=4, workload="merger_8m"):
+    """One GPU's share of the 8M merger's targets: the sorted targets split
+    into k contiguous ranges of whole waves, by the estimated walk cost
+    (orr_tree_shard_bounds) and, for comparison, by count; each range walked
+    alone with the coherent walk (orr_tree_walk_range), as each of k GPUs
+    would walk its share of the same tree. The slowest range bounds the time
+    k GPUs would take for the walk."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs, orr
+
+    kind, n = inputs.CONFIGS[workload]
+    pos_np, mass_np = inputs.make(kind, n)
+    pos = torch.from_numpy(pos_np).to(dev)
+    mass = torch.from_numpy(mass_np).to(dev)
+    tree = orr.Tree(pos, mass, inputs.LEAF_CAP)
+    acc = torch.empty((n, 3), dtype=torch.float32, device=dev)
+    cnt = [torch.empty(n, dtype=torch.int32, device=dev) for _ in range(4)]
+    perm = tree.export()["perm"].long()
+
+    def timed(run):
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        ev[0].record(stream)
+        for j in range(trials):
+            run()
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        return percentile([ev[j].elapsed_time(ev[j + 1]) for j in range(trials)], 0.5)
+
+    whole = timed(lambda: tree.walk(inputs.EPS, inputs.THETA, "coherent", out=(acc, cnt)))
+    work = (cnt[2].long() + cnt[3].long())[perm]  # interactions per sorted target
+    nw = (n + 63) // 64
+    splits = {"estimated_cost": tree.shard_bounds(k),
+              "equal_count": [min(64 * ((nw * j) // k), n) for j in range(k + 1)]}
+    out = {"workload": workload, "n": n, "k": k, "whole_walk_ms": whole}
+    for name, b in splits.items():
+        ms, inter = [], []
+        for a, z in zip(b, b[1:]):
+            ms.append(timed(lambda: tree.walk_range(a, z - a, inputs.EPS, inputs.THETA, "coherent",
+                                                    out=(acc, cnt))))
+            inter.append(int(work[a:z].sum().item()))
+        out[name] = {"bounds": b, "range_ms": ms, "max_ms": max(ms), "sum_ms": sum(ms),
+                     "interactions": inter, "max_over_mean_interactions": max(inter) * k / sum(inter)}
+    del tree
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(pos, mass, trials):
     """The oracle as it stands, on this host's cores: whole evaluations of the
     workload (build, walk of every target, group union visits), median."""
@@ -261,6 +311,7 @@ def main():
     widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
     advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
+    shard = None if args.no_shard else shard_leg(dev, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -299,6 +350,7 @@ def main():
         "width_sweep": widths,
         "descend_together": descend,
         "advance_rule": advance,
+        "one_gpu_share": shard,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

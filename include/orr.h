@@ -196,6 +196,37 @@ orr_status orr_tree_walk_descend(const orr_tree *tree, float eps, float theta, i
                                  uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                                  uint32_t *n_pc);
 
+/* The walk of orr_tree_walk over one contiguous range of sorted targets,
+ * [first, first + count): the share of the targets one GPU walks when they
+ * are split over several (given the tree, every target's walk is
+ * independent of the others: ADR-0029, Consequences). The range holds whole
+ * waves: first is a multiple of 64, and so is count unless first + count = n;
+ * count = 0 (any first in [0, n]) enqueues nothing. Outputs are written for the range's targets
+ * only, at their caller indices, bit for bit as orr_tree_walk writes them
+ * (visits_stepped included, since every wave of the range is whole); all
+ * other elements are left as they were. The coherent traversal orders the
+ * range's waves by the rule of the whole walk's schedule, with one more
+ * small kernel over the range; that schedule lives in the tree's workspace
+ * until the next range walk of the tree, so range walks of one tree run one
+ * at a time in stream order (the tree's stream). Errors: those of
+ * orr_tree_walk, and ORR_ERR_RANGE for a range outside [0, n] or not made of
+ * whole waves. */
+orr_status orr_tree_walk_range(const orr_tree *tree, float eps, float theta, orr_traversal traversal,
+                               int64_t first, int64_t count, float *acc, uint32_t *visits_own,
+                               uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc);
+
+/* Split the sorted targets into k contiguous ranges of whole waves with
+ * nearly equal estimated walk cost, for orr_tree_walk_range: the cost of a
+ * wave is the estimate the coherent walk's schedule orders waves by (summed
+ * leaf depth of its 64 targets plus 32 per level between its deepest leaf and
+ * the smallest cell holding all of them). bounds (HOST memory, k + 1 int64)
+ * receives 0 = bounds[0] <= bounds[1] <= ... <= bounds[k] = n; range j is
+ * [bounds[j], bounds[j + 1]), bound j the first wave boundary at which the
+ * cost before it reaches j / k of the total. Synchronises the tree's stream.
+ * Errors: ORR_ERR_INVALID_ARG (null pointer), ORR_ERR_RANGE (k < 1 or
+ * k > 65536), ORR_ERR_HIP. */
+orr_status orr_tree_shard_bounds(const orr_tree *tree, int32_t k, int64_t *bounds);
+
 /* Build and walk in one call. If timings is not NULL, every phase is timed
  * with HIP events, the stream is synchronised and the input status checked
  * (ORR_ERR_NONFINITE possible). Errors: those of orr_build_tree and
