@@ -255,11 +255,18 @@ struct WalkLds {
 // same node sequence (the next node any lane wants is c + 1 if some lane
 // opened c and escape[c] otherwise); kMin exists to measure the cost of the
 // explicit reduction.
-template <int kInv, bool kOff32, bool kMin>
+// kPow2: theta^2 = 2^-e, and every node's s^2 times 2^e is a normal float
+// (pow2_scale_ok): then s^2 < RN(theta^2 d^2) exactly when s^2 2^e < d^2, and
+// s^2 2^e is the scalar integer sum s2_bits + s2_shift (s2_shift = e << 23),
+// one scalar instruction in place of a vector multiply on every step. Proof:
+// if 2^-e d^2 is a normal float (or 0), both sides compare the same real
+// numbers scaled by 2^e; if it is not, it is below 2^-126 <= s^2, and both
+// comparisons are false.
+template <int kInv, bool kOff32, bool kMin, bool kPow2>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
-                                              uint32_t n_nodes, float eps2, float theta2, const WalkOut &out,
-                                              WalkLds &lds) {
+                                              uint32_t n_nodes, float eps2, float theta2, uint32_t s2_shift,
+                                              const WalkOut &out, WalkLds &lds) {
     const bool valid = i < n;
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
@@ -285,10 +292,13 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         const bool active = next <= c;
         const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
-        const bool far = __uint_as_float(nd.t.w) < theta2 * d2;  // s/d < theta
+        // s/d < theta: s^2 < theta^2 d^2, or s^2 2^e < d^2 (kPow2)
+        const float lhs = kPow2 ? __uint_as_float(nd.t.w + s2_shift) : __uint_as_float(nd.t.w);
+        const float rhs = kPow2 ? d2 : theta2 * d2;
+        const bool far = lhs < rhs;
         // Lanes opening c, from the two comparison masks.
-        const uint64_t m_open = __builtin_amdgcn_ballot_w64(active) &
-                                ~__builtin_amdgcn_fcmpf(__uint_as_float(nd.t.w), theta2 * d2, 4 /* ordered < */);
+        const uint64_t m_open =
+            __builtin_amdgcn_ballot_w64(active) & ~__builtin_amdgcn_fcmpf(lhs, rhs, 4 /* ordered < */);
         // Divergent branches below are skipped when no lane takes them.
         float mass_c = nd.g.w;
         __asm__ volatile("" : "+s"(mass_c));  // keeps the node mass in its register rather than loading it again
@@ -357,16 +367,32 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8
                                                               const uint32_t *__restrict__ perm, uint32_t n,
                                                               uint32_t max_nodes, float eps2, float theta2,
                                                               const uint32_t *__restrict__ order,
-                                                              uint32_t n_waves, uint32_t wave0, WalkOut out) {
+                                                              uint32_t n_waves, uint32_t wave0, uint32_t theta2_exp,
+                                                              WalkOut out) {
     __shared__ WalkLds lds;
     const uint32_t i = scheduled_target(order, n_waves, wave0);  // walked if i < n
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
+    const uint32_t sh = theta2_exp << 23;
+    // the scaled comparison only in the production variant (uniform branches)
+    constexpr bool kScaled = kFastInv && kOff32 && !kMin;
+    const bool pow2 = kScaled && pow2_scale_ok(prm, theta2_exp);
     if (!kFastInv)
-        walk_coherent<kInvIeee, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
-    else if (r2_cannot_overflow(prm, eps2))  // uniform
-        walk_coherent<kInvFastNoClamp, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
-    else
-        walk_coherent<kInvFast, kOff32, kMin>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, lds);
+        walk_coherent<kInvIeee, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds);
+    else if (r2_cannot_overflow(prm, eps2)) {
+        if (pow2)
+            walk_coherent<kInvFastNoClamp, kOff32, kMin, kScaled>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh,
+                                                                  out, lds);
+        else
+            walk_coherent<kInvFastNoClamp, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh,
+                                                                out, lds);
+    } else {
+        if (pow2)
+            walk_coherent<kInvFast, kOff32, kMin, kScaled>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out,
+                                                           lds);
+        else
+            walk_coherent<kInvFast, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out,
+                                                         lds);
+    }
 }
 
 template <int kInv>
@@ -439,6 +465,16 @@ __global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint6
 
 __global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
 
+// e with theta2 = 2^-e exactly, 0 <= e <= 126; kNotPow2 otherwise.
+constexpr uint32_t kNotPow2 = 0xffffffffu;
+uint32_t theta2_pow2_exp(float theta2) {
+    if (!(theta2 > 0.0f && theta2 <= 1.0f)) return kNotPow2;
+    int ex = 0;
+    const float m = std::frexp(theta2, &ex);  // theta2 = m 2^ex, m in [0.5, 1)
+    if (m != 0.5f || 1 - ex > 126) return kNotPow2;
+    return (uint32_t)(1 - ex);
+}
+
 template <bool kFast>
 hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
                          const WalkOut &out, hipStream_t s) {
@@ -451,9 +487,11 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
         const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(nw, (int64_t)kScheduleRegions);
         const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64));
         const uint32_t wave0 = (uint32_t)(rg.first / 64);
+        const uint32_t e2 = theta2_pow2_exp(theta2);
 #define ORR_COHERENT(OFF32, MIN)                                                                                  \
     k_walk_coherent<kFast, OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, nb, \
-                                                                     eps2, theta2, rg.order, (uint32_t)nw, wave0, out)
+                                                                     eps2, theta2, rg.order, (uint32_t)nw, wave0,  \
+                                                                     e2, out)
         if (mode == kWalkCoherentMin) {
             if (off32)
                 ORR_COHERENT(true, true);

@@ -46,4 +46,14 @@ __device__ __forceinline__ bool r2_cannot_overflow(const DevParams *prm, float e
     return 3.0 * s * s + (double)eps2 < 1e38;
 }
 
+// Every node's s^2 is RN(side^2) 2^-2l for its level l <= 21 (s = side 2^-l
+// exactly); s^2 2^e stays a normal float for all of them when the exponent
+// field of RN(side^2) is at least 1 + 2 * 21 and at most 254 - e.
+__device__ __forceinline__ bool pow2_scale_ok(const DevParams *prm, uint32_t e) {
+    if (e > 126u) return false;
+    const float L2 = prm->side * prm->side;
+    const uint32_t ex = (__float_as_uint(L2) >> 23) & 0xffu;
+    return ex >= 1u + 2u * (uint32_t)kMaxLevel && ex + e <= 254u;
+}
+
 }  // namespace orr

@@ -194,3 +194,21 @@ def test_native_library_loaded_once():
     assert orr.LIB_PATH in maps
     runtimes = {m for m in re.findall(r"(/\S*libamdhip64\.so[.\d]*)", maps)}
     assert len({os.path.realpath(p) for p in runtimes}) == 1, runtimes
+
+
+@pytest.mark.parametrize("theta", [0.25, 0.125, 2.0 ** -10])
+def test_power_of_two_thetas(theta):
+    """theta^2 = 2^-e: the coherent walk compares s^2 2^e with d^2 (an
+    exponent add on the scalar node record) instead of s^2 with theta^2 d^2;
+    the decisions, and so every output, must stay the oracle's."""
+    pos, mass = inputs.make("plummer", 3000)
+    run_full_case(pos, mass, 16, EPS, theta)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -40, 2.0 ** -46, 2.0 ** -48, 2.0 ** 56, 2.0 ** 60])
+def test_scaled_compare_range_limits(scale):
+    """Coordinate scales on both sides of the range in which every node's
+    s^2 2^e is a normal float (the scaled comparison is used inside it, the
+    product theta^2 d^2 outside); results are the oracle's either way."""
+    pos, mass = inputs.make("plummer", 2000)
+    run_full_case((pos * np.float32(scale)).astype(np.float32), mass, 32, EPS, 0.5)
