@@ -39,6 +39,8 @@ def parse():
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the group-width sweep of the walk (orr_tree_walk_grouped)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload table (every workload, both traversals)")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-GPU share leg (range walks of the 8M merger split 8 ways)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -216,6 +218,76 @@ def shard_leg(dev, stream, k=8, trials=4, workload="merger_8m"):
     return out
 
 
+def configs_leg(dev, stream, with_cpu, trials=11, walk_trials=5):
+    """Every workload: whole evaluations (median and IQR of `trials`), the
+    walk alone with both traversals, interactions and node visits per
+    particle; with_cpu: the oracle's whole evaluation on all host threads and
+    on one, for the two smallest workloads."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from barnes_hut_gravitational_amd import inputs, orr
+
+    table = {}
+    for name, (kind, n) in inputs.CONFIGS.items():
+        pos_np, mass_np = inputs.make(kind, n)
+        pos = torch.from_numpy(pos_np).to(dev)
+        mass = torch.from_numpy(mass_np).to(dev)
+        ws = orr.new_workspace(n, inputs.LEAF_CAP, dev)
+        acc = torch.empty((n, 3), dtype=torch.float32, device=dev)
+        cnt = [torch.empty(n, dtype=torch.int32, device=dev) for _ in range(4)]
+        kw = dict(eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP, workspace=ws, out=(acc, cnt))
+        for _ in range(2):
+            orr.orr_eval_forces(pos, mass, traversal="coherent", **kw)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for k in range(trials):
+            orr.orr_eval_forces(pos, mass, traversal="coherent", **kw)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        full = [ev[k].elapsed_time(ev[k + 1]) for k in range(trials)]
+        inter = int(cnt[2].long().sum().item() + cnt[3].long().sum().item())
+        own = float(cnt[0].double().mean().item())
+        stepped = float(cnt[1].double().mean().item())
+        tree = orr.Tree(pos, mass, inputs.LEAF_CAP, workspace=ws)
+        walk = {}
+        for tr in ("coherent", "independent"):
+            tree.walk(inputs.EPS, inputs.THETA, tr, out=(acc, cnt))
+            wev = [torch.cuda.Event(enable_timing=True) for _ in range(walk_trials + 1)]
+            wev[0].record(stream)
+            for k in range(walk_trials):
+                tree.walk(inputs.EPS, inputs.THETA, tr, out=(acc, cnt))
+                wev[k + 1].record(stream)
+            torch.cuda.synchronize()
+            walk[tr] = percentile([wev[k].elapsed_time(wev[k + 1]) for k in range(walk_trials)], 0.5)
+        row = {"n": n, "eval_ms_median": percentile(full, 0.5),
+               "eval_ms_iqr": percentile(full, 0.75) - percentile(full, 0.25),
+               "walk_ms_median": walk, "coherent_speedup_walk": walk["independent"] / walk["coherent"],
+               "interactions": inter, "interactions_per_s_eval": inter / (percentile(full, 0.5) * 1e-3),
+               "interactions_per_s_walk": inter / (walk["coherent"] * 1e-3),
+               "visits_own_per_particle": own, "visits_stepped_per_particle": stepped,
+               "redundancy": stepped / own, "n_nodes": tree.info()["n_nodes"]}
+        if with_cpu and n <= 131072:
+            cpu = {}
+            for threads, reps in ((oracle.num_threads(), 5), (1, 3)):
+                all_threads = oracle.num_threads()
+                oracle.set_num_threads(threads)
+                times = []
+                for _ in range(reps):
+                    t0 = time.perf_counter()
+                    oracle.evaluate(pos_np, mass_np, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
+                    times.append(time.perf_counter() - t0)
+                oracle.set_num_threads(all_threads)
+                cpu[str(threads)] = {"eval_ms_median": percentile(times, 0.5) * 1e3, "trials": reps}
+            row["oracle_eval"] = cpu
+        table[name] = row
+        del tree, ws, acc, cnt, pos, mass
+        torch.cuda.empty_cache()
+    return table
+
+
 def cpu_baseline(pos, mass, trials):
     """The oracle as it stands, on this host's cores: whole evaluations of the
     workload (build, walk of every target, group union visits), median."""
@@ -312,6 +384,7 @@ def main():
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
     advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
     shard = None if args.no_shard else shard_leg(dev, stream)
+    configs = None if args.no_configs else configs_leg(dev, stream, not args.no_cpu_baseline)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
@@ -351,6 +424,7 @@ def main():
         "descend_together": descend,
         "advance_rule": advance,
         "one_gpu_share": shard,
+        "configs": configs,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

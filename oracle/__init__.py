@@ -76,12 +76,19 @@ def lib():
                                           _f32p, _u32p, _u32p, _u32p, _u32p]
         L.oracle_walk_descend.restype = ctypes.c_int
         L.oracle_direct_fp32.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(k: int) -> None:
+    """Threads of the OpenMP loops over targets (timing only)."""
+    lib().oracle_set_num_threads(int(k))
 
 
 def max_nodes(n: int, leaf_cap: int) -> int:

@@ -45,6 +45,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the later parallel loops (timing only; results do not depend on it). */
+void oracle_set_num_threads(int k) {
+#ifdef _OPENMP
+    if (k >= 1) omp_set_num_threads(k);
+#else
+    (void)k;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Root cell. [PERF] "Where one evaluation goes" names a Morton sort; the    */
 /* pages do not say how the root cube is chosen. Reading: a tight cube whose */
