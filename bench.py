@@ -406,6 +406,7 @@ def main():
                    "leaf_cap": inputs.LEAF_CAP, "traversal": "coherent", "seed": inputs.SEED},
         "roofline": {"bound": "alu", "kernel": "k_walk_coherent", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
+                     "frac_of_unpacked_peak": achieved / (PEAK_FP32_TFLOPS / 2),
                      "traffic": walk_traffic_bytes() if args.workload == "plummer_1m" else None,
                      "flops_per_interaction": FLOPS_PER_INTERACTION, "walk_ms_mean": walk_mean},
         "step_ms_median": percentile(step_ms, 0.5),
