@@ -251,6 +251,8 @@ def configs_leg(dev, stream, with_cpu, trials=11, walk_trials=5):
         inter = int(cnt[2].long().sum().item() + cnt[3].long().sum().item())
         own = float(cnt[0].double().mean().item())
         stepped = float(cnt[1].double().mean().item())
+        pp_mean = float(cnt[2].double().mean().item())
+        pc_mean = float(cnt[3].double().mean().item())
         tree = orr.Tree(pos, mass, inputs.LEAF_CAP, workspace=ws)
         walk = {}
         for tr in ("coherent", "independent"):
@@ -268,7 +270,8 @@ def configs_leg(dev, stream, with_cpu, trials=11, walk_trials=5):
                "interactions": inter, "interactions_per_s_eval": inter / (percentile(full, 0.5) * 1e-3),
                "interactions_per_s_walk": inter / (walk["coherent"] * 1e-3),
                "visits_own_per_particle": own, "visits_stepped_per_particle": stepped,
-               "redundancy": stepped / own, "n_nodes": tree.info()["n_nodes"]}
+               "redundancy": stepped / own, "particle_terms_per_particle": pp_mean,
+               "cells_per_particle": pc_mean, "n_nodes": tree.info()["n_nodes"]}
         if with_cpu and n <= 131072:
             cpu = {}
             for threads, reps in ((oracle.num_threads(), 5), (1, 3)):
