@@ -208,16 +208,25 @@ __device__ __forceinline__ void store_sums(uint32_t k, float M, float sx, float 
     nodes[k].g = g;
 }
 
-// Leaf: its particles in sorted order.
+// Leaf: its particles in sorted order (loads issued four at a time, the sums
+// still one particle after the other).
 __device__ __forceinline__ void finish_leaf(uint32_t k, uint32_t first, uint32_t count, const float4 *__restrict__ xs,
                                             NodeRec *nodes, float4 *msum) {
     float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
-    for (uint32_t j = first; j < first + count; j++) {
-        const float4 p = xs[j];
-        M += p.w;
-        sx += p.w * p.x;
-        sy += p.w * p.y;
-        sz += p.w * p.z;
+    const uint32_t end = first + count;
+    for (uint32_t j0 = first; j0 < end; j0 += 4) {
+        float4 p[4];
+#pragma unroll
+        for (uint32_t u = 0; u < 4; u++) p[u] = j0 + u < end ? xs[j0 + u] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (uint32_t u = 0; u < 4; u++) {
+            if (j0 + u < end) {
+                M += p[u].w;
+                sx += p[u].w * p[u].x;
+                sy += p[u].w * p[u].y;
+                sz += p[u].w * p[u].z;
+            }
+        }
     }
     store_sums(k, M, sx, sy, sz, first, xs, nodes, msum);
 }
@@ -232,15 +241,27 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
                                                    const uint8_t *__restrict__ level, uint32_t *__restrict__ top_list,
                                                    const float4 *__restrict__ xs, float4 *msum) {
     const uint32_t k = blockIdx.x * 256u + threadIdx.x;
-    if (k >= min(prm->n_nodes, max_nodes)) return;
+    const uint32_t nn = min(prm->n_nodes, max_nodes);
+    if (k >= nn) return;
     const int l = level[k];
     const uint32_t i = nodes[k].t.y;
-    const int sh = 3 * (kMaxLevel - l);
-    const uint32_t end = l == 0 ? n : cell_end(keys, n, i, sh, keys[i] >> sh);
+    // In preorder a node is a leaf iff the next node is not its first child
+    // (level not above its own); a leaf's particles end where the next node's
+    // begin, and its escape is the next index. Internal nodes search for the
+    // end of their cell.
+    const bool leaf = k + 1 >= nn || (int)level[k + 1] <= l;
+    uint32_t end, esc;
+    if (leaf) {
+        end = k + 1 < nn ? nodes[k + 1].t.y : n;
+        esc = k + 1;
+    } else {
+        const int sh = 3 * (kMaxLevel - l);
+        end = l == 0 ? n : cell_end(keys, n, i, sh, keys[i] >> sh);
+        esc = base_at(tile_pre, loc, end);
+    }
     const uint32_t count = end - i;
     const float s = ldexpf(prm->side, -l);  // exact
     const float s2 = s * s;
-    const uint32_t esc = base_at(tile_pre, loc, end);
     nodes[k].t = make_uint4(esc, i, count, __float_as_uint(s2));
     if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = k;
     if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum);
