@@ -98,9 +98,28 @@ def direct_leg(dev, stream, trials=5):
     n = len(mass_np)
     inter = n * (n - 1)
     achieved = FLOPS_PER_INTERACTION * inter / (t * 1e-3) / 1e12
-    return {"workload": "plummer_131k", "kernel": "k_direct", "ms_median": t, "interactions": inter,
-            "interactions_per_s": inter / (t * 1e-3), "achieved": achieved, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_TFLOPS}
+    out = {"workload": "plummer_131k", "kernel": "k_direct", "ms_median": t, "interactions": inter,
+           "interactions_per_s": inter / (t * 1e-3), "achieved": achieved, "unit": "TFLOP/s",
+           "frac": achieved / PEAK_FP32_TFLOPS}
+    # the tree's approximation error at theta 0.5 against the float32 direct
+    # sum on every target (the pages' "Accuracy" question), at 131k and 1M
+    err = {}
+    for name in ("plummer_131k", "plummer_1m"):
+        if name != "plummer_131k":
+            pos_np, mass_np = inputs.make_config(name)
+            P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
+            acc = torch.empty((len(mass_np), 3), dtype=torch.float32, device=dev)
+            orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
+        tree = orr.orr_eval_forces(P, M, eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP).acc
+        torch.cuda.synchronize()
+        d = (tree.double() - acc.double()).norm(dim=1)
+        a = acc.double().norm(dim=1)
+        rel = d / a
+        err[name] = {"rel_rms": float(rel.pow(2).mean().sqrt()), "rel_median": float(rel.median()),
+                     "rel_p99": float(torch.quantile(rel, 0.99)), "rel_max": float(rel.max()),
+                     "rms_over_rms": float(d.pow(2).mean().sqrt() / a.pow(2).mean().sqrt())}
+    out["tree_error_vs_direct"] = err
+    return out
 
 
 def width_sweep(tree, acc, cnt, stream, trials=4):
@@ -218,15 +237,12 @@ def shard_leg(dev, stream, k=8, trials=4, workload="merger_8m"):
     return out
 
 
-def configs_leg(dev, stream, with_cpu, trials=11, walk_trials=5):
+def configs_leg(dev, stream, trials=11, walk_trials=5):
     """Every workload: whole evaluations (median and IQR of `trials`), the
     walk alone with both traversals, interactions and node visits per
-    particle; with_cpu: the oracle's whole evaluation on all host threads and
-    on one, for the two smallest workloads."""
-    import numpy as np
+    particle."""
     import torch
 
-    import oracle
     from barnes_hut_gravitational_amd import inputs, orr
 
     table = {}
@@ -272,19 +288,6 @@ def configs_leg(dev, stream, with_cpu, trials=11, walk_trials=5):
                "visits_own_per_particle": own, "visits_stepped_per_particle": stepped,
                "redundancy": stepped / own, "particle_terms_per_particle": pp_mean,
                "cells_per_particle": pc_mean, "n_nodes": tree.info()["n_nodes"]}
-        if with_cpu and n <= 131072:
-            cpu = {}
-            for threads, reps in ((oracle.num_threads(), 5), (1, 3)):
-                all_threads = oracle.num_threads()
-                oracle.set_num_threads(threads)
-                times = []
-                for _ in range(reps):
-                    t0 = time.perf_counter()
-                    oracle.evaluate(pos_np, mass_np, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
-                    times.append(time.perf_counter() - t0)
-                oracle.set_num_threads(all_threads)
-                cpu[str(threads)] = {"eval_ms_median": percentile(times, 0.5) * 1e3, "trials": reps}
-            row["oracle_eval"] = cpu
         table[name] = row
         del tree, ws, acc, cnt, pos, mass
         torch.cuda.empty_cache()
@@ -306,10 +309,28 @@ def cpu_baseline(pos, mass, trials):
         times.append(time.perf_counter() - t0)
         inter = int(r.n_pp.sum(dtype=np.int64) + r.n_pc.sum(dtype=np.int64))
     med = percentile(times, 0.5)
-    return {"value": inter / med, "unit": "interactions/s", "cores": oracle.num_threads(), "kind": "oracle",
+    # the two smallest workloads, on all host threads and on one
+    small = {}
+    all_threads = oracle.num_threads()
+    for name in ("plummer_16k", "plummer_131k"):
+        kind, n = inputs.CONFIGS[name]
+        p, m = inputs.make(kind, n)
+        row = {}
+        for threads, reps in ((all_threads, 5), (1, 3)):
+            oracle.set_num_threads(threads)
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                oracle.evaluate(p, m, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
+                ts.append(time.perf_counter() - t0)
+            row[str(threads)] = {"eval_ms_median": percentile(ts, 0.5) * 1e3, "trials": reps}
+        oracle.set_num_threads(all_threads)
+        small[name] = row
+    return {"value": inter / med, "unit": "interactions/s", "cores": all_threads, "kind": "oracle",
             "sample": f"{trials} whole oracle evaluations of the workload (tree build serial; walk and group "
-                      f"union visits OpenMP over targets), median {med * 1e3:.0f} ms, total {sum(times):.1f} s",
-            "eval_ms": med * 1e3}
+                      f"union visits OpenMP over targets), median {med * 1e3:.0f} ms, total {sum(times):.1f} s; "
+                      "then Plummer 16k and 131k on all threads (5 each) and on one (3 each)",
+            "eval_ms": med * 1e3, "small_workloads_eval_ms_by_threads": small}
 
 
 def main():
@@ -387,7 +408,7 @@ def main():
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
     advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
     shard = None if args.no_shard else shard_leg(dev, stream)
-    configs = None if args.no_configs else configs_leg(dev, stream, not args.no_cpu_baseline)
+    configs = None if args.no_configs else configs_leg(dev, stream)
 
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
