@@ -11,8 +11,9 @@
 // Node records are wave-uniform and come through scalar loads. An opened leaf
 // is read once for all its opening lanes: its particles are staged in the
 // wave's LDS with one coalesced load; when few lanes open it, their terms are
-// also packed across the wave's lanes. Target waves start in the order of a
-// cost estimate (longest first).
+// also packed across the wave's lanes. Each XCD takes its target waves from
+// its own list of the schedule (schedule.h), longest first; a range walk
+// takes them from the schedule of its range.
 //
 // Independent walk (enum TreeTraversal, kIndependent): one lane per target,
 // each following its own node index with per-lane vector loads; the measured
