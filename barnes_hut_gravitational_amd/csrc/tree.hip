@@ -19,7 +19,8 @@
 // (nodes started by particles before i) + (l - first(i)), an exclusive scan
 // (tile prefix + prefix inside the tile). A node ending at particle e has
 // escape = the first node starting at e or later, which is the scan value at
-// e. Each node's end is then searched in parallel, one thread per node.
+// e. Then one thread per node finds its end: a leaf ends where the next node
+// in preorder begins; an internal node's end is searched in the keys.
 //
 // Moments bottom-up without device-wide synchronisation: the tree is cut into
 // subtrees of at most kCutParticles particles ("cut" nodes: the largest nodes
