@@ -37,6 +37,8 @@ def parse():
                     help="whole oracle evaluations timed for the CPU baseline (median)")
     ap.add_argument("--no-direct", action="store_true",
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the tree's error against the direct sum (direct sums at 131k and 1M)")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the group-width sweep of the walk (orr_tree_walk_grouped)")
     ap.add_argument("--no-configs", action="store_true",
@@ -79,7 +81,7 @@ def walk_traffic_bytes():
     return None
 
 
-def direct_leg(dev, stream, trials=5):
+def direct_leg(dev, stream, trials=5, accuracy=True):
     """The all-pairs direct sum (orr_direct_forces) with the walk's term on the
     Plummer sphere of 131,072 particles: every lane does useful work on every
     term, so this is the issue-bound rate of the exact term itself."""
@@ -106,7 +108,7 @@ def direct_leg(dev, stream, trials=5):
     # the tree's approximation error at theta 0.5 against the float32 direct
     # sum on every target (the pages' "Accuracy" question), at 131k and 1M
     err = {}
-    for name in ("plummer_131k", "plummer_1m"):
+    for name in ("plummer_131k", "plummer_1m") if accuracy else ():
         if name != "plummer_131k":
             pos_np, mass_np = inputs.make_config(name)
             P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
@@ -120,7 +122,7 @@ def direct_leg(dev, stream, trials=5):
         err[name] = {"rel_rms": float(rel.pow(2).mean().sqrt()), "rel_median": float(rel.median()),
                      "rel_p99": float(torch.quantile(rel, 0.99)), "rel_max": float(rel.max()),
                      "rms_over_rms": float(d.pow(2).mean().sqrt() / a.pow(2).mean().sqrt())}
-    out["tree_error_vs_direct"] = err
+    out["tree_error_vs_direct"] = err or None
     return out
 
 
@@ -451,7 +453,7 @@ def main():
         walk_ms[tr] = [wev[k].elapsed_time(wev[k + 1]) for k in range(args.steps)]
     phases = orr.orr_eval_forces(pos, mass, traversal="coherent", timings=True, **kw).timings
     info = tree.info()
-    direct = None if args.no_direct else direct_leg(dev, stream)
+    direct = None if args.no_direct else direct_leg(dev, stream, accuracy=not args.no_accuracy)
     widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
     advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
