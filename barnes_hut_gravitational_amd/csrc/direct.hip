@@ -58,10 +58,9 @@ __global__ __launch_bounds__(kDirectBlock) void k_direct(const float *__restrict
 
 hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, float *acc, hipStream_t s) {
     const unsigned blocks = (unsigned)ceil_div(n, kDirectBlock);
-    if (eps2 >= 0x1p-96f)  // every r2 >= eps2 lies in the short inverse square root's domain
-        k_direct<kInvFast><<<blocks, kDirectBlock, 0, s>>>(pos, mass, (uint32_t)n, eps2, acc);
-    else
-        k_direct<kInvIeee><<<blocks, kDirectBlock, 0, s>>>(pos, mass, (uint32_t)n, eps2, acc);
+    // every r2 >= eps2 >= 2^-96 (the entry's range check on eps) lies in the
+    // short inverse square root's domain
+    k_direct<kInvFast><<<blocks, kDirectBlock, 0, s>>>(pos, mass, (uint32_t)n, eps2, acc);
     return hipGetLastError();
 }
 

@@ -104,8 +104,28 @@ orr_status check_sizes(int64_t n, int32_t leaf_cap) {
     return ORR_OK;
 }
 
+// The target's own term is m * 0 * eps^-3 (d = 0). It is +0, as the force law
+// wants, only while eps^-3 evaluated as the term evaluates it, the cube of
+// RN(1 / RN(sqrt(RN(eps * eps)))), is finite; for smaller eps it is 0 * inf
+// = NaN on every target. The bound lies near eps = 1.43e-13, where eps^2 is
+// far above 2^-96, the lower end of the walk's inverse square root domain.
+bool eps_in_range(float eps) {
+    if (!(std::isfinite(eps) && eps > 0.0f)) return false;
+    const float e2 = eps * eps;
+    if (!(e2 >= 0x1p-96f)) return false;
+    const float inv = 1.0f / std::sqrt(e2);
+    return std::isfinite((inv * inv) * inv);
+}
+
+orr_status check_eps(float eps) {
+    if (!eps_in_range(eps))
+        return fail(ORR_ERR_RANGE, "eps must be finite with a finite float32 eps^-3, about eps >= 1.43e-13 (got %g)",
+                    eps);
+    return ORR_OK;
+}
+
 orr_status check_walk_args(float eps, float theta, int traversal) {
-    if (!(std::isfinite(eps) && eps > 0.0f)) return fail(ORR_ERR_RANGE, "eps must be finite and > 0 (got %g)", eps);
+    if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
     if (!(std::isfinite(theta) && theta >= 0.0f))
         return fail(ORR_ERR_RANGE, "theta must be finite and >= 0 (got %g)", theta);
     if (traversal != ORR_TRAVERSAL_INDEPENDENT && traversal != ORR_TRAVERSAL_COHERENT)
@@ -245,15 +265,28 @@ orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_
 }
 
 orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_traversal traversal, float *acc,
-                         uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
+                         uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
+                         orr_timings *timings) {
     ORR_GUARD_BEGIN
     g_last_error.clear();
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
     orr_status st = check_walk_args(eps, theta, (int)traversal);
     if (st != ORR_OK) return st;
-    hipError_t e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
-                               eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    PhaseTimer tm;
+    hipError_t e = tm.init(timings != nullptr, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent, eps * eps,
+                    theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "walk");
+    if (!timings) return ORR_OK;
+    if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    DevParams prm;
+    if ((st = read_params(tree, &prm)) != ORR_OK) return st;
+    *timings = orr_timings{};
+    timings->walk_ms = tm.ms(0, 1);
+    timings->total_ms = timings->walk_ms;
+    if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
     return ORR_OK;
     ORR_GUARD_END
 }
@@ -383,7 +416,28 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     timings->build_ms = tm.ms(2, 3);
     timings->moments_ms = tm.ms(3, 4);
     timings->walk_ms = tm.ms(4, 5);
+    timings->scatter_ms = 0.0f;  // the walk stores its outputs in caller order
     timings->total_ms = tm.ms(0, 5);
+    if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_workspace_check(const void *workspace, size_t workspace_bytes, void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!workspace) return fail(ORR_ERR_INVALID_ARG, "workspace must not be NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(ORR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < sizeof(DevParams))
+        return fail(ORR_ERR_WORKSPACE, "workspace has %zu bytes, fewer than one build's parameters", workspace_bytes);
+    orr_tree t;
+    t.ws = Workspace{};
+    t.ws.prm = static_cast<DevParams *>(const_cast<void *>(workspace));  // the workspace starts with them
+    t.stream = static_cast<hipStream_t>(hip_stream);
+    DevParams prm;
+    orr_status st = read_params(&t, &prm);
+    if (st != ORR_OK) return st;
     if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
     return ORR_OK;
     ORR_GUARD_END
@@ -470,7 +524,7 @@ orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, flo
     g_last_error.clear();
     if (!pos || !mass || !acc) return fail(ORR_ERR_INVALID_ARG, "pos, mass and acc must not be NULL");
     if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
-    if (!(std::isfinite(eps) && eps > 0.0f)) return fail(ORR_ERR_RANGE, "eps must be finite and > 0 (got %g)", eps);
+    if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
     hipError_t e = launch_direct(pos, mass, n, eps * eps, acc, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "direct sum");
     return ORR_OK;

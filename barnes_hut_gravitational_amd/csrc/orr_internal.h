@@ -135,7 +135,6 @@ hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, flo
                                hipStream_t s);
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
                                     uint32_t *examples, hipStream_t s);
-bool walk_uses_fast_inv(float eps2);
 hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, float *acc, hipStream_t s);
 uint32_t morton_hist_blocks(int64_t n);
 

@@ -40,15 +40,16 @@ __device__ __forceinline__ float inv_sqrt_rn(float x) {
 
 // a += m * d * r2^(-3/2) with r2 = |d|^2 + eps^2 given, every step one
 // correctly rounded float operation (the library is compiled without
-// contraction). kInv: 0 = the general IEEE square root and division;
-// 1 = inv_sqrt_rn (same cube on its domain); 2 = inv_sqrt_rn without the
-// overflow clamp.
-enum { kInvIeee = 0, kInvFast = 1, kInvFastNoClamp = 2 };
+// contraction). The entry points admit only eps with eps^2 >= 2^-96 (a finite
+// inverse cube of eps needs far more), so every r2 lies in inv_sqrt_rn's
+// domain. kInv: 1 = inv_sqrt_rn (the cube of the IEEE square root and
+// division on that domain); 2 = the same without the overflow clamp.
+enum { kInvFast = 1, kInvFastNoClamp = 2 };
 
 template <int kInv>
 __device__ __forceinline__ void add_term_r2(float m, float dx, float dy, float dz, float r2, float &ax, float &ay,
                                             float &az) {
-    const float inv = kInv == kInvIeee ? 1.0f / sqrtf(r2) : inv_sqrt_rn<kInv == kInvFast>(r2);
+    const float inv = inv_sqrt_rn<kInv == kInvFast>(r2);
     const float f = m * ((inv * inv) * inv);
     ax += f * dx;
     ay += f * dy;
@@ -67,7 +68,7 @@ __device__ __forceinline__ void add_term(float m, float dx, float dy, float dz, 
 template <int kInv>
 __device__ __forceinline__ float4 term_product(float m, float dx, float dy, float dz, float eps2) {
     const float r2 = ((dx * dx + dy * dy) + dz * dz) + eps2;
-    const float inv = kInv == kInvIeee ? 1.0f / sqrtf(r2) : inv_sqrt_rn<kInv == kInvFast>(r2);
+    const float inv = inv_sqrt_rn<kInv == kInvFast>(r2);
     const float f = m * ((inv * inv) * inv);
     return make_float4(f * dx, f * dy, f * dz, 0.0f);
 }

@@ -263,7 +263,10 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
     const uint32_t count = end - i;
     const float s = ldexpf(prm->side, -l);  // exact
     const float s2 = s * s;
-    nodes[k].t = make_uint4(esc, i, count, __float_as_uint(s2));
+    // begin (t.y) was stored by k_tree_stub and is read here by the previous
+    // node's thread (a leaf's end): store only the fields computed here.
+    nodes[k].t.x = esc;
+    *reinterpret_cast<uint2 *>(&nodes[k].t.z) = make_uint2(count, __float_as_uint(s2));
     if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = k;
     if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum);
 }

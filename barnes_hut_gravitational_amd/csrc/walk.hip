@@ -361,7 +361,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
 
 // Eight waves per SIMD (at most 64 VGPRs): the occupancy the walk's issue
 // rate needs; without the bound the unrolled leaf sums take more registers.
-template <bool kFastInv, bool kOff32, bool kMin>
+template <bool kOff32, bool kMin>
 __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
@@ -375,11 +375,9 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const uint32_t sh = theta2_exp << 23;
     // the scaled comparison only in the production variant (uniform branches)
-    constexpr bool kScaled = kFastInv && kOff32 && !kMin;
+    constexpr bool kScaled = kOff32 && !kMin;
     const bool pow2 = kScaled && pow2_scale_ok(prm, theta2_exp);
-    if (!kFastInv)
-        walk_coherent<kInvIeee, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds);
-    else if (r2_cannot_overflow(prm, eps2)) {
+    if (r2_cannot_overflow(prm, eps2)) {
         if (pow2)
             walk_coherent<kInvFastNoClamp, kOff32, kMin, kScaled>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh,
                                                                   out, lds);
@@ -429,7 +427,6 @@ __device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, 
     write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
 }
 
-template <bool kFastInv>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
                                                                  const NodeRec *__restrict__ nodes,
                                                                  const DevParams *__restrict__ prm,
@@ -439,9 +436,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
     const uint32_t i = first + xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
-    if (!kFastInv)
-        walk_independent<kInvIeee>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
-    else if (r2_cannot_overflow(prm, eps2))
+    if (r2_cannot_overflow(prm, eps2))
         walk_independent<kInvFastNoClamp>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
     else
         walk_independent<kInvFast>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
@@ -476,7 +471,6 @@ uint32_t theta2_pow2_exp(float theta2) {
     return (uint32_t)(1 - ex);
 }
 
-template <bool kFast>
 hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
                          const WalkOut &out, hipStream_t s) {
     const uint32_t nb = (uint32_t)ws.max_nodes;
@@ -490,7 +484,7 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
         const uint32_t wave0 = (uint32_t)(rg.first / 64);
         const uint32_t e2 = theta2_pow2_exp(theta2);
 #define ORR_COHERENT(OFF32, MIN)                                                                                  \
-    k_walk_coherent<kFast, OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, nb, \
+    k_walk_coherent<OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, nb, \
                                                                      eps2, theta2, rg.order, (uint32_t)nw, wave0,  \
                                                                      e2, out)
         if (mode == kWalkCoherentMin) {
@@ -506,16 +500,13 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
 #undef ORR_COHERENT
     } else {
         const unsigned blocks = (unsigned)ceil_div(rg.count, (int64_t)kWalkBlock);
-        k_walk_independent<kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0],
+        k_walk_independent<<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0],
                                                                 (uint32_t)rg.first, end, nb, eps2, theta2, out);
     }
     return hipGetLastError();
 }
 
 }  // namespace
-
-// The fast inverse square root applies when every r^2 >= eps^2 is >= 2^-96.
-bool walk_uses_fast_inv(float eps2) { return eps2 >= 0x1p-96f; }
 
 hipError_t launch_walk(const Workspace &ws, int mode, float eps2, float theta2, float *acc,
                        uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
@@ -528,8 +519,7 @@ hipError_t launch_walk_range(const Workspace &ws, int mode, const WalkRange &rg,
                              float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                              uint32_t *n_pc, hipStream_t s) {
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    if (walk_uses_fast_inv(eps2)) return launch_walk_t<true>(ws, mode, rg, eps2, theta2, out, s);
-    return launch_walk_t<false>(ws, mode, rg, eps2, theta2, out, s);
+    return launch_walk_t(ws, mode, rg, eps2, theta2, out, s);
 }
 
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,

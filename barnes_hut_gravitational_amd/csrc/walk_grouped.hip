@@ -103,7 +103,7 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
     if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
-template <uint32_t kW, bool kDescend, bool kFastInv>
+template <uint32_t kW, bool kDescend>
 __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__restrict__ xs,
                                                              const NodeRec *__restrict__ nodes,
                                                              const DevParams *__restrict__ prm,
@@ -112,9 +112,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__res
                                                              WalkOut out) {
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
-    if (!kFastInv)
-        walk_grouped<kW, kDescend, kInvIeee>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
-    else if (r2_cannot_overflow(prm, eps2))
+    if (r2_cannot_overflow(prm, eps2))
         walk_grouped<kW, kDescend, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
     else
         walk_grouped<kW, kDescend, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
@@ -122,7 +120,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__res
 
 }  // namespace
 
-template <bool kDescend, bool kFast>
+template <bool kDescend>
 hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, float theta2, const WalkOut &out,
                                  hipStream_t s) {
     const uint32_t n = (uint32_t)ws.n;
@@ -130,7 +128,7 @@ hipError_t launch_walk_grouped_t(const Workspace &ws, int width, float eps2, flo
     const unsigned blocks = (unsigned)ceil_div(ws.n, kWalkBlock);
 #define ORR_GROUPED(W)                                                                                    \
     case W:                                                                                               \
-        k_walk_grouped<W, kDescend, kFast><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
+        k_walk_grouped<W, kDescend><<<blocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], n, nb, \
                                                                          eps2, theta2, out);              \
         break;
     switch (width) {
@@ -152,12 +150,8 @@ hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, flo
                                uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                                hipStream_t s) {
     const WalkOut out{acc, visits_own, visits_stepped, n_pp, n_pc};
-    const bool fast = walk_uses_fast_inv(eps2);
-    if (descend)
-        return fast ? launch_walk_grouped_t<true, true>(ws, width, eps2, theta2, out, s)
-                    : launch_walk_grouped_t<true, false>(ws, width, eps2, theta2, out, s);
-    return fast ? launch_walk_grouped_t<false, true>(ws, width, eps2, theta2, out, s)
-                : launch_walk_grouped_t<false, false>(ws, width, eps2, theta2, out, s);
+    if (descend) return launch_walk_grouped_t<true>(ws, width, eps2, theta2, out, s);
+    return launch_walk_grouped_t<false>(ws, width, eps2, theta2, out, s);
 }
 
 }  // namespace orr

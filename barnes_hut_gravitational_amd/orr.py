@@ -21,8 +21,8 @@ TRAVERSALS = {"independent": 0, "coherent": 1}
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
             "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_range",
-            "orr_tree_shard_bounds", "orr_eval_forces", "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
-            "orr_selftest_inv_sqrt", "orr_tree_free")
+            "orr_tree_shard_bounds", "orr_eval_forces", "orr_workspace_check", "orr_tree_info_get",
+            "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -36,7 +36,8 @@ class OrrError(RuntimeError):
 
 class Timings(ctypes.Structure):
     _fields_ = [(f, ctypes.c_float) for f in
-                ("cube_keys_ms", "sort_ms", "gather_ms", "build_ms", "moments_ms", "walk_ms", "total_ms")]
+                ("cube_keys_ms", "sort_ms", "gather_ms", "build_ms", "moments_ms", "walk_ms", "scatter_ms",
+                 "total_ms")]
 
     def as_dict(self):
         return {f: float(getattr(self, f)) for f, _ in self._fields_}
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.orr_workspace_bytes.argtypes = [i64, i32]
         L.orr_workspace_bytes.restype = sz
         L.orr_build_tree.argtypes = [_vp, _vp, i64, i32, _vp, sz, _vp, ctypes.POINTER(_vp)]
-        L.orr_tree_walk.argtypes = [_vp, f32, f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]
+        L.orr_tree_walk.argtypes = [_vp, f32, f32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(Timings)]
         L.orr_tree_walk_grouped.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_descend.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_min_advance.argtypes = [_vp, f32, f32, _vp, _vp, _vp, _vp, _vp]
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_shard_bounds.argtypes = [_vp, i32, ctypes.POINTER(i64)]
         L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
                                       _vp, ctypes.POINTER(Timings)]
+        L.orr_workspace_check.argtypes = [_vp, sz, _vp]
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
         L.orr_tree_check.argtypes = [_vp]
         L.orr_tree_export.argtypes = [_vp] * 9
@@ -82,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
                      "orr_tree_walk_min_advance", "orr_tree_walk_range", "orr_tree_shard_bounds",
-                     "orr_eval_forces",
+                     "orr_eval_forces", "orr_workspace_check",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
                      "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
@@ -161,6 +163,13 @@ def orr_eval_forces(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="c
     return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
 
 
+def orr_workspace_check(workspace: torch.Tensor) -> None:
+    """Raise if the most recent evaluation in this workspace had non-finite
+    input or an invalid sort (orr_workspace_check); synchronises the current
+    stream."""
+    _check(lib().orr_workspace_check(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
+
+
 def orr_direct_forces(pos, mass, *, eps=0.05, out=None) -> torch.Tensor:
     """All-pairs float32 direct sum with the walk's term (orr_direct_forces);
     returns acc [n, 3] in caller order."""
@@ -196,11 +205,14 @@ class Tree:
                                     self.workspace.numel(), _stream(pos.device), ctypes.byref(h)))
         self._h = h
 
-    def walk(self, eps=0.05, theta=0.5, traversal="coherent", out=None) -> Result:
+    def walk(self, eps=0.05, theta=0.5, traversal="coherent", out=None, timings=False) -> Result:
+        """The walk of the built tree (orr_tree_walk); timings=True times it
+        with HIP events and synchronises."""
         acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        tm = Timings() if timings else None
         _check(lib().orr_tree_walk(self._h, eps, theta, TRAVERSALS[traversal], _ptr(acc),
-                                   *[_ptr(c) for c in cnt]))
-        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+                                   *[_ptr(c) for c in cnt], ctypes.byref(tm) if tm is not None else None))
+        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
 
     def walk_grouped(self, eps=0.05, theta=0.5, group_width=32, out=None) -> Result:
         """The walk with groups of group_width targets sharing a node index

@@ -63,7 +63,8 @@
  *     while the tree is built; the evaluation still runs to completion on a
  *     well-formed (but meaningless) tree, and the condition is reported as
  *     ORR_ERR_NONFINITE by the next call that synchronises (orr_tree_info_get,
- *     orr_tree_check, or orr_eval_forces with timings requested).
+ *     orr_tree_check, orr_workspace_check, or orr_eval_forces and
+ *     orr_tree_walk with timings requested).
  */
 #ifndef ORR_H
 #define ORR_H
@@ -75,7 +76,7 @@
 extern "C" {
 #endif
 
-#define ORR_ABI_VERSION 1
+#define ORR_ABI_VERSION 2
 #define ORR_MAX_LEAF_CAP 256
 #define ORR_MAX_N 2147483647LL
 
@@ -106,6 +107,7 @@ typedef struct {
     float build_ms;     /* topology and escape indices (node staging included) */
     float moments_ms;   /* monopole moments */
     float walk_ms;      /* the traversal, scatter to caller order included */
+    float scatter_ms;   /* outputs into caller order: done by the walk's stores, so 0 (in walk_ms) */
     float total_ms;
 } orr_timings;
 
@@ -145,17 +147,25 @@ size_t orr_workspace_bytes(int64_t n, int32_t leaf_cap);
 orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_t leaf_cap,
                           void *workspace, size_t workspace_bytes, void *hip_stream, orr_tree **out);
 
-/* Enqueue a walk over a built tree, on the tree's stream. eps > 0 and finite
- * (eps = 0 would make the target's own term 0/0); theta >= 0 and finite.
+/* Enqueue a walk over a built tree, on the tree's stream.
+ * eps: finite and large enough that eps^-3, evaluated as the term evaluates
+ * it (the cube of RN(1 / RN(sqrt(RN(eps * eps))))), is a finite float: the
+ * target's own term is m * 0 * eps^-3 (d = 0) and is +0 only then (0 * inf
+ * would make every acceleration NaN). In practice eps >= 1.43e-13. Results
+ * are finite only where m * eps^-3 stays within float range for the masses m.
+ * theta >= 0 and finite.
  * acc [n][3]; visits_own = nodes where the target's own walk acted (equal for
  * both traversals); visits_stepped = nodes its wave stepped through (the
  * union of the wave's walks for the coherent traversal, the own walk for the
  * independent one); n_pp = particle terms (self excluded), n_pc = accepted
- * cells. Errors: ORR_ERR_INVALID_ARG (null tree, bad traversal),
+ * cells. timings (HOST, may be NULL): if given, the walk is timed with HIP
+ * events (walk_ms = total_ms; the other phases 0), the stream is
+ * synchronised and the build's input status checked (ORR_ERR_NONFINITE
+ * possible). Errors: ORR_ERR_INVALID_ARG (null tree, bad traversal),
  * ORR_ERR_RANGE (eps, theta), ORR_ERR_HIP. */
 orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_traversal traversal,
                          float *acc, uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
-                         uint32_t *n_pc);
+                         uint32_t *n_pc, orr_timings *timings);
 
 /* The walk with groups of group_width consecutive sorted targets (1, 2, 4,
  * ..., 64) sharing one node index: the sub-group coherence of the solver page
@@ -236,6 +246,18 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
                            uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *workspace,
                            size_t workspace_bytes, void *hip_stream, orr_timings *timings);
 
+/* Status of the most recent evaluation or build in this workspace, for
+ * callers of orr_eval_forces without timings (which returns before the
+ * device has looked at the input): synchronises hip_stream (the stream that
+ * evaluation used) and reads the workspace's parameter block. ORR_OK;
+ * ORR_ERR_NONFINITE if that input was non-finite or had a negative mass;
+ * ORR_ERR_HIP if a bounded wait of its radix sort gave up (never expected;
+ * its outputs are then invalid). Every build resets the status, so a caller
+ * that evaluates several times checks after each evaluation it relies on.
+ * Errors: ORR_ERR_INVALID_ARG (null or unaligned workspace),
+ * ORR_ERR_WORKSPACE (smaller than its parameter block), ORR_ERR_HIP. */
+orr_status orr_workspace_check(const void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Synchronise the tree's stream and report its sizes and input status.
  * Returns ORR_ERR_NONFINITE (with *out filled) if the input was non-finite. */
 orr_status orr_tree_info_get(const orr_tree *tree, orr_tree_info *out);
@@ -260,7 +282,7 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
  * particle's own term is +0). O(n^2) work. pos [n][3], mass [n], acc [n][3]:
  * device pointers, caller-owned; enqueued on hip_stream; no workspace.
  * Errors: ORR_ERR_INVALID_ARG (null pointer), ORR_ERR_RANGE (n < 1 or
- * n > ORR_MAX_N, eps not finite and > 0), ORR_ERR_HIP. */
+ * n > ORR_MAX_N, eps outside the range of orr_tree_walk), ORR_ERR_HIP. */
 orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, float eps, float *acc,
                              void *hip_stream);
 

@@ -76,6 +76,8 @@ def lib():
                                           _f32p, _u32p, _u32p, _u32p, _u32p]
         L.oracle_walk_descend.restype = ctypes.c_int
         L.oracle_direct_fp32.restype = None
+        L.oracle_eps_ok.argtypes = [_f32]
+        L.oracle_eps_ok.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.oracle_set_num_threads.restype = None
         _lib = L
@@ -200,7 +202,15 @@ def build_tree(pos, mass, leaf_cap=32) -> Tree:
     return Tree(len(mass), leaf_cap, lo, side, scale, keys, perm, ks, xs, level, begin, count, escape, geom, s2)
 
 
+def check_eps(eps):
+    """Raise unless the target's own term m * 0 * eps^-3 is +0, i.e. eps^-3 as
+    the term evaluates it in float32 is finite (about eps >= 1.43e-13)."""
+    if not lib().oracle_eps_ok(_f32(eps)):
+        raise OracleError(2, f"eps = {eps!r} (own term 0 * eps^-3 is not +0)")
+
+
 def _walk_args(t: Tree, eps, theta):
+    check_eps(eps)
     return (t.xs.reshape(-1), t.n, t.geom.reshape(-1), t.s2, t.begin, t.count, t.escape, t.n_nodes,
             _f32(eps), _f32(theta))
 
@@ -225,6 +235,7 @@ def walk_descend(t: Tree, eps, theta, width):
     """The descend-together group walk (ADR-0029, Alternatives considered):
     groups of `width` consecutive sorted targets open a node when any member
     would. Returns sorted-order (acc [n,3] f32, pp, pc, visits, covered)."""
+    check_eps(eps)
     n = t.n
     acc = np.empty((n, 3), np.float32)
     pp, pc, vis, cov = (np.empty(n, np.uint32) for _ in range(4))
@@ -239,6 +250,7 @@ def walk_descend(t: Tree, eps, theta, width):
 def walk_trace(t: Tree, eps, theta, target):
     """Visit sequence of one sorted target: (node [k], action [k]) with action
     0 = accepted, 1 = opened leaf, 2 = opened internal node."""
+    check_eps(eps)
     buf = np.empty(t.n_nodes, np.uint64)
     k = lib().oracle_walk_trace(t.xs.reshape(-1), t.geom.reshape(-1), t.s2, t.begin, t.count, t.escape,
                                 t.n_nodes, _f32(eps), _f32(theta), int(target), buf, len(buf))
@@ -274,6 +286,7 @@ def group_walk(t: Tree, eps, theta, width=64, rule="min"):
 def direct_fp32(pos, mass, eps, targets=None):
     """Float32 direct sum in index order with the walk's term, for caller-order
     targets (all if None); the target's own term (+0) is included."""
+    check_eps(eps)
     pos, mass = _f32c(pos), _f32c(mass)
     n = len(mass)
     targets = np.arange(n, dtype=np.int64) if targets is None else np.ascontiguousarray(targets, np.int64)
@@ -304,6 +317,7 @@ class Result:
 
 def evaluate(pos, mass, eps=0.05, theta=0.5, leaf_cap=32, width=64) -> Result:
     """The whole force evaluation: build, walk every target, scatter to caller order."""
+    check_eps(eps)
     t = build_tree(pos, mass, leaf_cap)
     acc_s, pp_s, pc_s, vis_s = walk(t, eps, theta)
     groups = union_visits(t, eps, theta, width)

@@ -271,6 +271,18 @@ static void add_term(float m, float dx, float dy, float dz, float eps2, float a[
     a[2] += f * dz;
 }
 
+/* The target's own term is m * 0 * eps^-3 (d = 0), +0 as the force law     */
+/* wants only while eps^-3, evaluated as add_term evaluates it, is finite:   */
+/* 1 if so, 0 if eps is not finite and positive or that cube overflows (the  */
+/* own term, and so every sum, would be 0 * inf = NaN).                      */
+int oracle_eps_ok(float eps) {
+    if (!(isfinite(eps) && eps > 0.0f)) return 0;
+    float eps2 = eps * eps;
+    if (!(eps2 > 0.0f)) return 0;
+    float inv = 1.0f / sqrtf(eps2);
+    return isfinite((inv * inv) * inv) ? 1 : 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* One target's stackless walk ([ADR29] Decision; [SOLVER] "What is not      */
 /* given up": each target is summed over exactly the nodes its own walk      */

@@ -44,6 +44,10 @@ def check_tree(tree: orr.Tree, ot: oracle.Tree):
 
 
 def rel_err(acc: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row vector relative error. Both sides must be finite: a NaN or an
+    infinity is never within any tolerance (NaN compares false both ways)."""
+    assert np.isfinite(acc).all(), "non-finite GPU acceleration"
+    assert np.isfinite(ref).all(), "non-finite reference acceleration"
     num = np.linalg.norm(acc.astype(np.float64) - ref, axis=1)
     den = np.linalg.norm(ref.astype(np.float64), axis=1)
     return np.where(den > 0, num / np.where(den > 0, den, 1), np.where(num > 0, np.inf, 0.0))
@@ -64,6 +68,7 @@ def check_walk(r: orr.Result, ref: oracle.Result, traversal: str, rows=None):
 
 def check_acc_bitwise(r: orr.Result, ref_acc: np.ndarray, rows=None):
     sel = slice(None) if rows is None else rows
+    assert np.isfinite(ref_acc).all(), "non-finite reference acceleration"
     assert np.array_equal(r.acc.cpu().numpy()[sel].view(np.uint32), ref_acc.view(np.uint32))
 
 

@@ -11,6 +11,8 @@ import pytest
 
 from barnes_hut_gravitational_amd import orr
 
+from eps_bound import self_term_finite, smallest_eps
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "orr.h")
 
@@ -36,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_static_strings_and_version():
     L = orr.lib()
-    assert orr.abi_version() == 1
+    assert orr.abi_version() == 2
     assert L.orr_traversal_name(0) == b"independent" and L.orr_traversal_name(1) == b"coherent"
     assert L.orr_traversal_name(7) == b"invalid"
     assert L.orr_status_string(0) == b"ok" and L.orr_status_string(5) == b"workspace too small"
@@ -84,7 +86,7 @@ def test_build_and_walk_argument_errors():
     assert L.orr_build_tree(1, 1, 100, 32, 256, 1 << 30, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_build_tree(1, 1, 0, 32, 256, 1 << 30, None, ctypes.byref(h)) == orr.ORR_ERR_RANGE
     assert h.value is None
-    assert L.orr_tree_walk(None, 0.05, 0.5, 1, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_walk(None, 0.05, 0.5, 1, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_grouped(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_descend(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_min_advance(None, 0.05, 0.5, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
@@ -92,6 +94,9 @@ def test_build_and_walk_argument_errors():
     assert L.orr_tree_shard_bounds(None, 8, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_check(None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_workspace_check(None, 1 << 20, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_workspace_check(256 + 8, 1 << 20, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_workspace_check(256, 64, None) == orr.ORR_ERR_WORKSPACE
     assert L.orr_tree_export(None, None, None, None, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_selftest_inv_sqrt(0, 1, None, 1, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_selftest_inv_sqrt(5, 1, 1, 1, None) == orr.ORR_ERR_INVALID_ARG
@@ -115,3 +120,16 @@ def test_binding_rejects_host_tensors():
 
     with pytest.raises(orr.OrrError):
         orr.orr_eval_forces(torch.zeros(4, 3), torch.ones(4))
+
+
+def test_eps_lower_bound():
+    """eps is rejected exactly where the own term's eps^-3 overflows float32
+    (it would be 0 * inf = NaN on every target). An admitted eps passes on to
+    the traversal check (bad traversal 2), so no device work is started."""
+    lo, below = smallest_eps()
+    assert 1.4e-13 < lo < 1.5e-13 and self_term_finite(lo) and not self_term_finite(below)
+    for eps in (1e-30, 1e-20, 1e-14, below):
+        assert _eval(eps=eps, tr=2)[0] == orr.ORR_ERR_RANGE, eps
+        assert orr.lib().orr_direct_forces(1, 1, 100, eps, 1, None) == orr.ORR_ERR_RANGE
+    for eps in (lo, 1e-12, 1e-3, 0.05):
+        assert _eval(eps=eps, tr=2)[0] == orr.ORR_ERR_INVALID_ARG, eps

@@ -9,6 +9,7 @@ import torch
 import oracle
 from barnes_hut_gravitational_amd import inputs, orr
 
+from eps_bound import smallest_eps
 from parity import to_dev
 
 pytestmark = pytest.mark.gpu
@@ -60,12 +61,14 @@ def test_direct_131k_sampled_bitwise():
     assert same_bits(a[idx], oracle.direct_fp32(pos, mass, EPS, idx))
 
 
-def test_direct_tiny_eps_ieee_path_and_coincident_points():
-    print("[case] direct tiny eps and duplicates", flush=True)
+def test_direct_smallest_eps_and_coincident_points():
+    print("[case] direct smallest eps and duplicates", flush=True)
     pos, mass = inputs.make("plummer", 700)
-    pos[10:20] = pos[10]  # coincident particles: d = 0 gives exact +0 terms
-    for eps in (1e-30, 1e-3):
-        assert same_bits(gpu_direct(pos, mass, eps), oracle.direct_fp32(pos, mass, eps))
+    pos[10:20] = pos[10]  # coincident particles: d = 0 gives exact +0 terms while eps^-3 is finite
+    for eps in (smallest_eps()[0], 1e-3):
+        a, ref = gpu_direct(pos, mass, eps), oracle.direct_fp32(pos, mass, eps)
+        assert np.isfinite(ref).all()
+        assert same_bits(a, ref)
 
 
 def test_direct_equals_theta_zero_walk_on_gpu():

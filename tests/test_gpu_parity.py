@@ -17,6 +17,7 @@ import torch
 import oracle
 from barnes_hut_gravitational_amd import inputs, orr
 
+from eps_bound import smallest_eps
 from parity import check_acc_bitwise, check_tree, check_walk, rel_err, sampled_reference, to_dev, u32, ACC_REL_TOL
 
 pytestmark = pytest.mark.gpu
@@ -68,9 +69,20 @@ def test_inverse_sqrt_exhaustive():
     assert k == 0, [hex(v) for v in ex]
 
 
-def test_tiny_eps_uses_ieee_path():
+def test_smallest_admitted_eps_and_rejected_tiny_eps():
+    """At the smallest admitted eps (the own term's eps^-3 just below FLT_MAX)
+    every output is finite and the oracle's; just below it, and far below,
+    both sides reject eps instead of returning NaN."""
+    lo, below = smallest_eps()
     pos, mass = inputs.make("plummer", 3000)
-    run_full_case(pos, mass, 32, 1e-20, 0.5)  # eps^2 is subnormal in float32
+    run_full_case(pos, mass, 32, lo, 0.5)
+    P, M = to_dev(pos, mass)
+    for eps in (below, 1e-20):
+        with pytest.raises(orr.OrrError) as e:
+            orr.orr_eval_forces(P, M, eps=eps)
+        assert e.value.status == orr.ORR_ERR_RANGE
+        with pytest.raises(oracle.OracleError):
+            oracle.evaluate(pos, mass, eps, 0.5, 32)
 
 
 def test_unequal_masses_and_small_eps():
