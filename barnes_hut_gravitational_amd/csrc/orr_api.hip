@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -440,6 +441,69 @@ orr_status orr_workspace_check(const void *workspace, size_t workspace_bytes, vo
     if (st != ORR_OK) return st;
     if (prm.bad_input) return fail(ORR_ERR_NONFINITE, "non-finite position or mass, or negative mass, in the input");
     return ORR_OK;
+    ORR_GUARD_END
+}
+
+}  // extern "C"
+
+// Workspace of orr_eval_forces_noalloc: one fixed array in device memory per
+// GPU, loaded with the library's code object and held until the process
+// ends. In host code `scratch` names a host-side stand-in, never the device
+// memory: every host use goes through the address hipGetSymbolAddress returns
+// for the current device (kept per device in g_scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[ORR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+orr_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(ORR_ERR_HIP, "device %d is beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+            return fail(ORR_ERR_HIP, "scratch array of device %d is not 256-byte aligned", dev);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ORR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+orr_status orr_eval_forces_noalloc(const float *pos, const float *mass, int64_t n, float eps, float theta,
+                                   int32_t leaf_cap, orr_traversal traversal, float *acc, uint32_t *visits_own,
+                                   uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    orr_status st = check_sizes(n, leaf_cap);
+    if (st != ORR_OK) return st;
+    const size_t need = carve_workspace(nullptr, n, leaf_cap, nullptr);
+    if (need > (size_t)ORR_NOALLOC_SCRATCH_BYTES)
+        return fail(ORR_ERR_WORKSPACE,
+                    "n = %lld at leaf_cap %d needs %zu bytes of workspace; the allocation-free entry holds %zu",
+                    (long long)n, leaf_cap, need, (size_t)ORR_NOALLOC_SCRATCH_BYTES);
+    if (!pos || !mass) return fail(ORR_ERR_INVALID_ARG, "pos and mass must not be NULL");
+    if ((st = check_walk_args(eps, theta, (int)traversal)) != ORR_OK) return st;
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != ORR_OK) return st;
+    // the evaluation without timings enqueues kernels only (no allocation,
+    // fill, copy or host wait), and those kernels initialise every part of
+    // the workspace they read before reading it
+    return orr_eval_forces(pos, mass, n, eps, theta, leaf_cap, traversal, acc, visits_own, visits_stepped, n_pp,
+                           n_pc, ws, (size_t)ORR_NOALLOC_SCRATCH_BYTES, hip_stream, nullptr);
     ORR_GUARD_END
 }
 

@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(_HERE, "liborr.so")
 
 ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_ERR_WORKSPACE = range(6)
 TRAVERSALS = {"independent": 0, "coherent": 1}
+NOALLOC_SCRATCH_BYTES = 144 << 20  # ORR_NOALLOC_SCRATCH_BYTES of include/orr.h
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
             "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_range",
-            "orr_tree_shard_bounds", "orr_eval_forces", "orr_workspace_check", "orr_tree_info_get",
+            "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check", "orr_tree_info_get",
             "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_shard_bounds.argtypes = [_vp, i32, ctypes.POINTER(i64)]
         L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
                                       _vp, ctypes.POINTER(Timings)]
+        L.orr_eval_forces_noalloc.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                              _vp, _vp]
         L.orr_workspace_check.argtypes = [_vp, sz, _vp]
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
         L.orr_tree_check.argtypes = [_vp]
@@ -84,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
                      "orr_tree_walk_min_advance", "orr_tree_walk_range", "orr_tree_shard_bounds",
-                     "orr_eval_forces", "orr_workspace_check",
+                     "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
                      "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
@@ -161,6 +164,19 @@ def orr_eval_forces(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="c
                                _stream(pos.device), ctypes.byref(tm) if tm is not None else None)
     _check(st)
     return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
+
+
+def orr_eval_forces_noalloc(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="coherent",
+                            out=None) -> Result:
+    """orr_eval_forces with the library's fixed per-GPU workspace
+    (orr_eval_forces_noalloc): allocates no device memory itself; outputs are
+    allocated here only when `out` is not given."""
+    pos, mass = _as_inputs(pos, mass)
+    n = pos.shape[0]
+    acc, cnt = out if out is not None else _outputs(n, pos.device)
+    _check(lib().orr_eval_forces_noalloc(_ptr(pos), _ptr(mass), n, eps, theta, leaf_cap, TRAVERSALS[traversal],
+                                         _ptr(acc), *[_ptr(c) for c in cnt], _stream(pos.device)))
+    return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
 
 def orr_workspace_check(workspace: torch.Tensor) -> None:

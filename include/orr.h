@@ -246,6 +246,29 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
                            uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *workspace,
                            size_t workspace_bytes, void *hip_stream, orr_timings *timings);
 
+/* Bytes of the fixed device array that orr_eval_forces_noalloc uses as its
+ * workspace: 144 MiB per GPU, enough for n = 1,048,576 at leaf_cap 32 (any
+ * (n, leaf_cap) with orr_workspace_bytes(n, leaf_cap) <= this). */
+#define ORR_NOALLOC_SCRATCH_BYTES (144ull << 20)
+
+/* orr_eval_forces for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same evaluation, outputs and errors, with the workspace
+ * taken from a fixed array of ORR_NOALLOC_SCRATCH_BYTES in the library's own
+ * device memory instead of a caller's buffer, and no timings. It calls no
+ * device allocation or free: the array is part of the library's code object
+ * on each GPU, from its loading until the process ends, and is looked up once
+ * per device on the first call (with that device current; the stream must
+ * belong to the current device). The caller still passes inputs and outputs
+ * (device pointers). Every call on one GPU uses that GPU's one array, so calls
+ * that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and give undefined results; calls in one stream's
+ * order are safe. Errors: those of orr_eval_forces, and ORR_ERR_WORKSPACE when
+ * orr_workspace_bytes(n, leaf_cap) > ORR_NOALLOC_SCRATCH_BYTES. */
+orr_status orr_eval_forces_noalloc(const float *pos, const float *mass, int64_t n, float eps, float theta,
+                                   int32_t leaf_cap, orr_traversal traversal, float *acc, uint32_t *visits_own,
+                                   uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc, void *hip_stream);
+
 /* Status of the most recent evaluation or build in this workspace, for
  * callers of orr_eval_forces without timings (which returns before the
  * device has looked at the input): synchronises hip_stream (the stream that

@@ -133,3 +133,22 @@ def test_eps_lower_bound():
         assert orr.lib().orr_direct_forces(1, 1, 100, eps, 1, None) == orr.ORR_ERR_RANGE
     for eps in (lo, 1e-12, 1e-3, 0.05):
         assert _eval(eps=eps, tr=2)[0] == orr.ORR_ERR_INVALID_ARG, eps
+
+
+def test_noalloc_limit_and_argument_errors():
+    """The allocation-free entry refuses, before any device work, sizes whose
+    workspace exceeds its fixed array, and bad arguments as orr_eval_forces."""
+    text = open(HEADER).read()
+    m = re.search(r"#define ORR_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == orr.NOALLOC_SCRATCH_BYTES
+    assert orr.workspace_bytes(1 << 20, 32) <= orr.NOALLOC_SCRATCH_BYTES < orr.workspace_bytes(1100000, 32)
+    L = orr.lib()
+    for n, cap, status in ((1100000, 32, orr.ORR_ERR_WORKSPACE), ((1 << 20), 1, orr.ORR_ERR_WORKSPACE),
+                           (0, 32, orr.ORR_ERR_RANGE), (100, 0, orr.ORR_ERR_RANGE)):
+        assert L.orr_eval_forces_noalloc(1, 1, n, 0.05, 0.5, cap, 1, None, None, None, None, None, None) == status
+    assert L.orr_eval_forces_noalloc(None, 1, 100, 0.05, 0.5, 32, 1, None, None, None, None, None,
+                                     None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_eval_forces_noalloc(1, 1, 100, 1e-20, 0.5, 32, 1, None, None, None, None, None,
+                                     None) == orr.ORR_ERR_RANGE
+    assert L.orr_eval_forces_noalloc(1, 1, 100, 0.05, 0.5, 32, 2, None, None, None, None, None,
+                                     None) == orr.ORR_ERR_INVALID_ARG
