@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="plummer_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-trials", type=int, default=10,
+    ap.add_argument("--cpu-trials", type=int, default=3,
                     help="whole oracle evaluations timed for the CPU baseline (median)")
     ap.add_argument("--no-direct", action="store_true",
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
@@ -344,43 +344,60 @@ def scaling_leg(dev, stream, trials=11):
     return rows
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(pos, mass, trials):
     """The oracle as it stands, on this host's cores: whole evaluations of the
-    workload (build, walk of every target, group union visits), median."""
+    workload (build, walk of every target, group union visits), median; then
+    every other workload (Plummer 16k, 131k, uniform 262k: 11 evaluations on
+    all threads, and Plummer 16k and 131k 3 on one thread; the 8M merger once
+    on all threads)."""
     import numpy as np
 
     import oracle
     from barnes_hut_gravitational_amd import inputs
 
-    times, inter = [], 0
-    for _ in range(trials):
-        t0 = time.perf_counter()
-        r = oracle.evaluate(pos, mass, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
-        times.append(time.perf_counter() - t0)
-        inter = int(r.n_pp.sum(dtype=np.int64) + r.n_pc.sum(dtype=np.int64))
+    def timed(p, m, reps):
+        ts, inter = [], 0
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = oracle.evaluate(p, m, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
+            ts.append(time.perf_counter() - t0)
+            inter = int(r.n_pp.sum(dtype=np.int64) + r.n_pc.sum(dtype=np.int64))
+        return ts, inter
+
+    times, inter = timed(pos, mass, trials)
     med = percentile(times, 0.5)
-    # the two smallest workloads, on all host threads and on one
-    small = {}
     all_threads = oracle.num_threads()
-    for name in ("plummer_16k", "plummer_131k"):
+    per_config = {}
+    plan = [("plummer_16k", all_threads, 11), ("plummer_131k", all_threads, 11), ("uniform_262k", all_threads, 11),
+            ("plummer_16k", 1, 3), ("plummer_131k", 1, 3), ("merger_8m", all_threads, 1)]
+    for name, threads, reps in plan:
         kind, n = inputs.CONFIGS[name]
         p, m = inputs.make(kind, n)
-        row = {}
-        for threads, reps in ((all_threads, 5), (1, 3)):
-            oracle.set_num_threads(threads)
-            ts = []
-            for _ in range(reps):
-                t0 = time.perf_counter()
-                oracle.evaluate(p, m, inputs.EPS, inputs.THETA, inputs.LEAF_CAP)
-                ts.append(time.perf_counter() - t0)
-            row[str(threads)] = {"eval_ms_median": percentile(ts, 0.5) * 1e3, "trials": reps}
+        oracle.set_num_threads(threads)
+        ts, k = timed(p, m, reps)
         oracle.set_num_threads(all_threads)
-        small[name] = row
+        row = per_config.setdefault(name, {})
+        row[str(threads)] = {"eval_ms_median": percentile(ts, 0.5) * 1e3,
+                             "eval_ms_iqr": (percentile(ts, 0.75) - percentile(ts, 0.25)) * 1e3, "trials": reps,
+                             "interactions_per_s": k / percentile(ts, 0.5)}
+        del p, m
     return {"value": inter / med, "unit": "interactions/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{trials} whole oracle evaluations of the workload (tree build serial; walk and group "
-                      f"union visits OpenMP over targets), median {med * 1e3:.0f} ms, total {sum(times):.1f} s; "
-                      "then Plummer 16k and 131k on all threads (5 each) and on one (3 each)",
-            "eval_ms": med * 1e3, "small_workloads_eval_ms_by_threads": small}
+                      f"union visits OpenMP over targets on {all_threads} threads), median {med * 1e3:.0f} ms, "
+                      f"total {sum(times):.1f} s; then the other workloads (per_config)",
+            "eval_ms": med * 1e3, "eval_ms_iqr": (percentile(times, 0.75) - percentile(times, 0.25)) * 1e3,
+            "per_config_eval_ms_by_threads": per_config}
 
 
 def main():
@@ -422,6 +439,7 @@ def main():
         del src, dst
     for _ in range(args.warmup):
         step()
+    orr.orr_workspace_check(ws)  # raises on non-finite input or an invalid sort
     # counts of the workload (identical every step)
     inter = int(cnt[2].long().sum().item() + cnt[3].long().sum().item())
     visits_own = float(cnt[0].double().mean().item())
@@ -438,6 +456,10 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+    # the last timed evaluation: valid input and sort, and the warm-up's counts
+    orr.orr_workspace_check(ws)
+    if int(cnt[2].long().sum().item() + cnt[3].long().sum().item()) != inter:
+        raise RuntimeError("the timed evaluations' interaction count differs from the warm-up's")
 
     # the dominant kernel alone: K walks of the built tree, both traversals
     tree = orr.Tree(pos, mass, inputs.LEAF_CAP, workspace=ws)
@@ -464,6 +486,7 @@ def main():
     ms = wall_ms
     walk_mean = sum(walk_ms["coherent"]) / args.steps
     achieved = FLOPS_PER_INTERACTION * inter / (walk_mean * 1e-3) / 1e12
+    traffic = walk_traffic_bytes() if args.workload == "plummer_1m" else None
     out = {
         "metric": METRIC,
         "value": inter / (ms * 1e-3),
@@ -482,7 +505,9 @@ def main():
         "roofline": {"bound": "alu", "kernel": "k_walk_coherent", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS,
                      "frac_of_unpacked_peak": achieved / (PEAK_FP32_TFLOPS / 2),
-                     "traffic": walk_traffic_bytes() if args.workload == "plummer_1m" else None,
+                     "traffic": traffic,
+                     "hbm_gbs": traffic / (walk_mean * 1e-3) / 1e9 if traffic else None,
+                     "hbm_frac": traffic / (walk_mean * 1e-3) / 1e9 / PEAK_HBM_GBS if traffic else None,
                      "flops_per_interaction": FLOPS_PER_INTERACTION, "walk_ms_mean": walk_mean},
         "step_ms_median": percentile(step_ms, 0.5),
         "step_ms_iqr": percentile(step_ms, 0.75) - percentile(step_ms, 0.25),
@@ -501,7 +526,7 @@ def main():
         "advance_rule": advance,
         "one_gpu_share": shard,
         "configs": configs,
-        "scaling": scaling,
+        "scaling_sweep": scaling,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
