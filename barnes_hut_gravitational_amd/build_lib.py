@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liborr.so")
-SOURCES = ["cube_keys.hip", "sort.hip", "tree.hip", "walk.hip", "walk_grouped.hip", "direct.hip", "orr_api.hip"]
+SOURCES = ["cube_keys.hip", "sort.hip", "tree.hip", "walk.hip", "walk_grouped.hip", "walk_width.hip", "direct.hip", "orr_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

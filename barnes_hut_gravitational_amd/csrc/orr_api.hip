@@ -335,6 +335,25 @@ orr_status orr_tree_walk_descend(const orr_tree *tree, float eps, float theta, i
     return walk_grouped_entry(tree, eps, theta, group_width, true, acc, visits_own, visits_stepped, n_pp, n_pc);
 }
 
+orr_status orr_tree_walk_width(const orr_tree *tree, float eps, float theta, int32_t width, float *acc,
+                               uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    orr_status st = check_walk_args(eps, theta, ORR_TRAVERSAL_COHERENT);
+    if (st != ORR_OK) return st;
+    if (width != 32 && width != 64 && width != 128 && width != 256)
+        return fail(ORR_ERR_RANGE, "width %d is not 32, 64, 128 or 256", width);
+    if ((uint64_t)tree->ws.max_nodes * sizeof(NodeRec) > 0xffffffffull)
+        return fail(ORR_ERR_RANGE, "n = %lld is too large for the width walks (node array beyond 4 GiB)",
+                    (long long)tree->ws.n);
+    hipError_t e = launch_walk_width(tree->ws, width, eps * eps, theta * theta, acc, visits_own, visits_stepped,
+                                     n_pp, n_pc, tree->stream);
+    if (e != hipSuccess) return hip_fail(e, "width walk");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
 orr_status orr_tree_walk_range(const orr_tree *tree, float eps, float theta, orr_traversal traversal,
                                int64_t first, int64_t count, float *acc, uint32_t *visits_own,
                                uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc) {

@@ -133,6 +133,12 @@ hipError_t launch_range_schedule(const Workspace &ws, int64_t wave0, int64_t n_w
 hipError_t launch_walk_grouped(const Workspace &ws, int width, bool descend, float eps2, float theta2, float *acc,
                                uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
                                hipStream_t s);
+// The coherent walk at coherence width 32 (two node indices per wave), 64
+// (launch_walk), 128 or 256 (2 or 4 waves of a work-group sharing one node
+// index); hipErrorInvalidValue for other widths.
+hipError_t launch_walk_width(const Workspace &ws, int width, float eps2, float theta2, float *acc,
+                             uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc,
+                             hipStream_t s);
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
                                     uint32_t *examples, hipStream_t s);
 hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, float *acc, hipStream_t s);

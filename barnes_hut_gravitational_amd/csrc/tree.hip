@@ -265,7 +265,10 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
     const float s2 = s * s;
     // begin (t.y) was stored by k_tree_stub and is read here by the previous
     // node's thread (a leaf's end): store only the fields computed here.
-    nodes[k].t.x = esc;
+    // every record's escape lies beyond its own index (true of any tree, and
+    // enforced here whatever the keys): the coherent walk moves to it without
+    // a check of its own and still always ends
+    nodes[k].t.x = max(esc, k + 1);
     *reinterpret_cast<uint2 *>(&nodes[k].t.z) = make_uint2(count, __float_as_uint(s2));
     if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = k;
     if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum);

@@ -29,121 +29,11 @@
 #include "term.h"
 #include "schedule.h"
 #include "walk_common.h"
-
-#ifndef ORR_PACK_KMAX
-#define ORR_PACK_KMAX 64  // pack leaf rows when at most this many lanes open the leaf (64: always)
-#endif
+#include "walk_leaf.h"
 
 namespace orr {
 
 namespace {
-
-// Orders the wave's LDS accesses around a hand-over between lanes (LDS
-// requests of one wave are served in order; this keeps the compiler's order).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-// Particles per row when k lanes open a leaf of cnt particles: the wave is
-// split into g slots of 64/g lanes (g = 64 / k rounded down to a power of
-// two), each slot one particle, each lane of a slot one opening lane; no
-// wider than the leaf needs. g = 1: no packing.
-__device__ __forceinline__ uint32_t pack_width(uint32_t k, uint32_t cnt) {
-    if (k > ORR_PACK_KMAX) return 1u;
-    uint32_t g = 64u >> (32u - __clz(k - 1u));  // 64 / (k rounded up to a power of two); k >= 1
-    while (g > 1 && (g >> 1) >= cnt) g >>= 1;
-    return g;
-}
-
-// A leaf opened by many lanes: its particles are staged in the wave's LDS
-// (one coalesced load, one particle per lane) and every opening lane adds
-// them in particle order, one broadcast LDS read per particle.
-template <int kInv>
-__device__ __forceinline__ void leaf_masked(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, bool opening,
-                                            const float4 &xi, float eps2, float &ax, float &ay, float &az,
-                                            float4 *src) {
-    const uint32_t lane = __lane_id();
-    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
-        const uint32_t cc = min(cnt - c0, 64u);
-        if (lane < cc) src[lane] = xs[b + c0 + lane];
-        wave_lds_sync();
-        if (opening) {
-            uint32_t j = 0;
-            for (; j + 4u <= cc; j += 4u) {  // four reads in flight
-                const float4 p0 = src[j], p1 = src[j + 1], p2 = src[j + 2], p3 = src[j + 3];
-                add_term<kInv>(p0.w, p0.x - xi.x, p0.y - xi.y, p0.z - xi.z, eps2, ax, ay, az);
-                add_term<kInv>(p1.w, p1.x - xi.x, p1.y - xi.y, p1.z - xi.z, eps2, ax, ay, az);
-                add_term<kInv>(p2.w, p2.x - xi.x, p2.y - xi.y, p2.z - xi.z, eps2, ax, ay, az);
-                add_term<kInv>(p3.w, p3.x - xi.x, p3.y - xi.y, p3.z - xi.z, eps2, ax, ay, az);
-            }
-            for (; j < cc; j++) {
-                const float4 p = src[j];
-                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
-            }
-        }
-        wave_lds_sync();
-    }
-}
-
-// A leaf opened by the lanes of m_open, packed kG > 1 particles per row:
-// lane (slot q, position r) computes the term product of the row's particle
-// q for the r-th opening lane; each opening lane then adds its kG products of
-// the row in particle order, so its sum is the one its own walk makes. Slots
-// past the leaf's end hold +0 products, and adding +0 leaves every
-// accumulator unchanged (an accumulator that starts at +0 never becomes -0
-// under round-to-nearest), so the rows need no tail test. Per wave LDS:
-// tgt = the opening lanes' positions, src = up to 64 of the leaf's particles,
-// prod = one row of products.
-template <int kInv, uint32_t kG>
-__device__ __forceinline__ void leaf_packed(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint64_t m_open,
-                                            bool opening, const float4 &xi, float eps2, float &ax, float &ay,
-                                            float &az, float4 *tgt, float4 *src, float4 *prod) {
-    constexpr uint32_t kSlot = 64u / kG;  // lanes per slot: opening lanes served per particle
-    const uint32_t lane = __lane_id();
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_open >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m_open, 0u));
-    const uint32_t k = (uint32_t)__popcll(m_open);
-    const uint32_t q = lane / kSlot, r = lane % kSlot;
-    if (opening) tgt[rank] = xi;
-    wave_lds_sync();
-    const float4 t = r < k ? tgt[r] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
-        const uint32_t cc = min(cnt - c0, 64u);
-        if (lane < cc) src[lane] = xs[b + c0 + lane];
-        wave_lds_sync();
-        for (uint32_t j0 = 0; j0 < cc; j0 += kG) {
-            if (r < k) {
-                float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (j0 + q < cc) {
-                    const float4 p = src[j0 + q];
-                    v = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
-                }
-                prod[lane] = v;
-            }
-            wave_lds_sync();
-            if (opening) {
-#pragma unroll
-                for (uint32_t qq = 0; qq < kG; qq++) {
-                    const float4 v = prod[qq * kSlot + rank];
-                    ax += v.x;
-                    ay += v.y;
-                    az += v.z;
-                }
-            }
-            wave_lds_sync();
-        }
-    }
-}
-
-// v + 1 on the lanes whose bit is set in mask, v elsewhere: one add with the
-// mask as carry-in.
-__device__ __forceinline__ uint32_t add_lane_bit(uint32_t v, uint64_t mask) {
-    uint32_t r;
-    uint64_t carry;
-    __asm__("v_addc_co_u32_e64 %0, %1, 0, %2, %3" : "=v"(r), "=s"(carry) : "v"(v), "s"(mask));
-    return r;
-}
 
 // Smallest value over the wave's 64 lanes, wave-uniform: DPP minima within
 // rows of 16 lanes (two quad permutations, two row rotations), two row
@@ -170,92 +60,19 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// A leaf opened by k <= 16 lanes, packed kG >= 4 particles per row as in
-// leaf_packed, with the sums spread over lanes: the accumulator component c
-// of opening lane r is carried by lane 16 c + r, which adds the row's kG
-// products of that component in particle order (one add per product instead
-// of three in the opening lane). The accumulators go to those lanes through
-// LDS before the leaf and come back after it; every accumulator sees the same
-// additions in the same order as its own lane would make.
-template <int kInv, uint32_t kG>
-__device__ __forceinline__ void leaf_chain(const float4 *__restrict__ xs, uint32_t b, uint32_t cnt, uint64_t m_open,
-                                           bool opening, const float4 &xi, float eps2, float &ax, float &ay,
-                                           float &az, float4 *tgt, float4 *src, float *prod, float4 *acc) {
-    constexpr uint32_t kSlot = 64u / kG;  // >= 16 >= k
-    const uint32_t lane = __lane_id();
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m_open >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m_open, 0u));
-    const uint32_t k = (uint32_t)__popcll(m_open);
-    const uint32_t q = lane / kSlot, r = lane % kSlot;
-    const uint32_t cr = lane & 15u, cc = lane >> 4;  // chain lane: opening lane cr, component cc
-    const bool chain = cr < k && cc < 3u;
-    if (opening) {
-        tgt[rank] = xi;
-        acc[rank] = make_float4(ax, ay, az, 0.0f);
-    }
-    wave_lds_sync();
-    float a = chain ? reinterpret_cast<const float *>(acc)[4u * cr + cc] : 0.0f;
-    const float4 t = r < k ? tgt[r] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (uint32_t c0 = 0; c0 < cnt; c0 += 64) {
-        const uint32_t n0 = min(cnt - c0, 64u);
-        if (lane < n0) src[lane] = xs[b + c0 + lane];
-        wave_lds_sync();
-        for (uint32_t j0 = 0; j0 < n0; j0 += kG) {
-            if (r < k) {
-                float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                if (j0 + q < n0) {
-                    const float4 p = src[j0 + q];
-                    v = term_product<kInv>(p.w, p.x - t.x, p.y - t.y, p.z - t.z, eps2);
-                }
-                prod[r * kG + q] = v.x;
-                prod[64u + r * kG + q] = v.y;
-                prod[128u + r * kG + q] = v.z;
-            }
-            wave_lds_sync();
-            if (chain) {
-                const float *pc = prod + 64u * cc + cr * kG;
-#pragma unroll
-                for (uint32_t qq = 0; qq < kG; qq++) a += pc[qq];
-            }
-            wave_lds_sync();
-        }
-    }
-    if (chain) reinterpret_cast<float *>(acc)[4u * cr + cc] = a;
-    wave_lds_sync();
-    if (opening) {
-        const float4 v = acc[rank];
-        ax = v.x;
-        ay = v.y;
-        az = v.z;
-    }
-    wave_lds_sync();
-}
-
-// Sorted targets of this lane's wave: block b runs on XCD b mod 8 and takes
-// its waves from that XCD's list of the schedule, in block order (wave slot s
-// of the XCD runs list entry s: targets 64 (wave0 + w) .. + 63 of the
-// schedule's wave w, whose waves start at wave0). Slots past the list get the
-// first target past the schedule's waves, which no lane walks.
-__device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict__ order, uint32_t n_waves,
-                                                     uint32_t wave0) {
-    const uint32_t L = (kScheduleRegions / 8u) * ((n_waves + kScheduleRegions - 1u) / kScheduleRegions);
-    const uint32_t x = blockIdx.x & 7u;
-    const uint32_t s = (blockIdx.x >> 3) * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t w = s < order[8u * L + x] ? min(order[x * L + s], n_waves) : n_waves;
-    return (wave0 + w) * 64u + (threadIdx.x & 63u);
-}
-
-// Wave-private LDS of the packed leaf evaluation.
-struct WalkLds {
-    float4 tgt[kWalkBlock / 64][64], src[kWalkBlock / 64][64], prod[kWalkBlock / 64][64], acc[kWalkBlock / 64][64];
-};
-
 // kMin: the wave advances to the minimum of the lanes' `next` (every lane
 // keeps its own next node, c + 1 after opening), found with a DPP
 // reduction, instead of the select on the opening mask. Both rules give the
 // same node sequence (the next node any lane wants is c + 1 if some lane
 // opened c and escape[c] otherwise); kMin exists to measure the cost of the
 // explicit reduction.
+// kSplit (1, 2, 4): the target wave's 64 walks are shared by kSplit
+// hardware waves. Each runs the whole traversal (node loads, opening tests of
+// all 64 lanes, advance), so all of them step through the same nodes, and
+// each adds the terms, accepted cells and opened leaves, of its own 64 /
+// kSplit lanes only (lanes part * 64 / kSplit ..). A target's sum is made by
+// one lane in its walk's order as before; the leaf and term work of a step is
+// spread over kSplit SIMDs, for grids that leave most SIMDs idle.
 // kPow2: theta^2 = 2^-e, and every node's s^2 times 2^e is a normal float
 // (pow2_scale_ok): then s^2 < RN(theta^2 d^2) exactly when s^2 2^e < d^2, and
 // s^2 2^e is the scalar integer sum s2_bits + s2_shift (s2_shift = e << 23),
@@ -263,11 +80,15 @@ struct WalkLds {
 // if 2^-e d^2 is a normal float (or 0), both sides compare the same real
 // numbers scaled by 2^e; if it is not, it is below 2^-126 <= s^2, and both
 // comparisons are false.
-template <int kInv, bool kOff32, bool kMin, bool kPow2>
+template <int kInv, bool kOff32, bool kMin, bool kPow2, uint32_t kSplit>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
-                                              const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
-                                              uint32_t n_nodes, float eps2, float theta2, uint32_t s2_shift,
-                                              const WalkOut &out, WalkLds &lds) {
+                                              const uint32_t *__restrict__ perm, uint32_t i, uint32_t part,
+                                              uint32_t n, uint32_t n_nodes, float eps2, float theta2,
+                                              uint32_t s2_shift, const WalkOut &out, WalkLds &lds) {
+    static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4, "split");
+    constexpr uint32_t kOwn = 64u / kSplit;  // lanes whose terms this wave adds
+    const uint64_t own_mask = kSplit == 1 ? ~0ull : ((1ull << kOwn) - 1ull) << (part * kOwn);
+    const bool own = kSplit == 1 || __lane_id() / kOwn == part;
     const bool valid = i < n;
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;  // lanes without a target never act
@@ -284,13 +105,14 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         // the array (the launch checks that 32 n_nodes fits), which saves the
         // 64-bit address arithmetic of every step.
         const NodeRec nd = kOff32 ? *reinterpret_cast<const NodeRec *>(node_bytes + (c << 5)) : nodes[c];
-        const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
+        const uint32_t esc = nd.t.x;  // > c: the build stores escape = max(escape, index + 1)
+        const uint32_t c1 = c + 1;
         // A lane that did not accept at the wave's previous node wants exactly
         // the node the wave visits next (it opened that node, so it wants the
         // node after it, which is the smallest index any lane can want), so
         // `next` only changes when a lane accepts a cell: it then waits for
         // the escape. The lanes acting at c are those with next <= c.
-        const bool active = next <= c;
+        const bool active = next < c1;
         const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
         // s/d < theta: s^2 < theta^2 d^2, or s^2 2^e < d^2 (kPow2)
@@ -303,57 +125,41 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         // Divergent branches below are skipped when no lane takes them.
         float mass_c = nd.g.w;
         __asm__ volatile("" : "+s"(mass_c));  // keeps the node mass in its register rather than loading it again
-        if (active && far) {  // accept: monopole term, then wait for the escape
-            add_term_r2<kInv>(mass_c, dx, dy, dz, d2 + eps2, ax, ay, az);
-            pc += 1;
-            next = esc;
+        if (kSplit == 1) {
+            if (active && far) {  // accept: monopole term, then wait for the escape
+                add_term_r2<kInv>(mass_c, dx, dy, dz, d2 + eps2, ax, ay, az);
+                pc += 1;
+                next = esc;
+            }
+        } else {
+            if (active && far && own) {  // accept, own lanes: the monopole term
+                add_term_r2<kInv>(mass_c, dx, dy, dz, d2 + eps2, ax, ay, az);
+                pc += 1;
+            }
+            next = active && far ? esc : next;  // every lane: wait for the escape
         }
-        const bool opening = active && !far;
+        const bool opening = active && !far && own;  // own lanes opening c
         if (m_open) {
             nopen = add_lane_bit(nopen, m_open);
-            if (esc == c + 1) {  // a leaf that some lane opens
+            const uint64_t m_mine = m_open & own_mask;  // the opening lanes whose terms this wave adds
+            if (esc == c1 && m_mine) {  // a leaf that some own lane opens
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
-                const uint32_t g = pack_width((uint32_t)__popcll(m_open), cnt);
-                if (g == 1) {
-                    leaf_masked<kInv>(xs, b, cnt, opening, xi, eps2, ax, ay, az, lds.src[wv]);
-                } else {
-#define ORR_LEAF_PACKED(G)                                                                                 \
-    case G:                                                                                                \
-        leaf_packed<kInv, G>(xs, b, cnt, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv], \
-                             lds.prod[wv]);                                                                \
-        break;
-#define ORR_LEAF_CHAIN(G)                                                                                 \
-    case G:                                                                                               \
-        leaf_chain<kInv, G>(xs, b, cnt, m_open, opening, xi, eps2, ax, ay, az, lds.tgt[wv], lds.src[wv], \
-                            reinterpret_cast<float *>(lds.prod[wv]), lds.acc[wv]);                        \
-        break;
-                    switch (g) {  // g >= 4: at most 16 opening lanes
-                        ORR_LEAF_PACKED(2)
-                        ORR_LEAF_CHAIN(4)
-                        ORR_LEAF_CHAIN(8)
-                        ORR_LEAF_CHAIN(16)
-                        ORR_LEAF_CHAIN(32)
-                        default:
-                            ORR_LEAF_CHAIN(64)
-                    }
-#undef ORR_LEAF_PACKED
-#undef ORR_LEAF_CHAIN
-                }
+                leaf_terms<kInv>(xs, b, cnt, m_mine, opening, xi, eps2, ax, ay, az, lds, wv);
                 if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
         }
         if (kMin) {
-            if (opening) next = c + 1;
-            c = max(wave_min_u32(next), c + 1);  // the max only guards progress; the minimum exceeds c
+            if (active && !far) next = c1;
+            c = max(wave_min_u32(next), c1);  // the max only guards progress; the minimum exceeds c
         } else {
             // The smallest index any lane wants: c + 1 if some lane opened c
             // (a waiting lane wants the escape of a skipped ancestor of c, at
             // least escape[c]; for a leaf escape[c] = c + 1 anyway), else the
             // escape.
-            c = m_open ? c + 1 : esc;
+            c = m_open ? c1 : esc;
         }
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
+    if (valid && own) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
 }
 
 // The walk schedule (which waves each XCD runs, longest first) is computed
@@ -361,7 +167,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
 
 // Eight waves per SIMD (at most 64 VGPRs): the occupancy the walk's issue
 // rate needs; without the bound the unrolled leaf sums take more registers.
-template <bool kOff32, bool kMin>
+template <bool kOff32, bool kMin, uint32_t kSplit>
 __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
@@ -371,27 +177,27 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8
                                                               uint32_t n_waves, uint32_t wave0, uint32_t theta2_exp,
                                                               WalkOut out) {
     __shared__ WalkLds lds;
-    const uint32_t i = scheduled_target(order, n_waves, wave0);  // walked if i < n
+    uint32_t part;
+    const uint32_t i = scheduled_target<kSplit>(order, n_waves, wave0, &part);  // walked if i < n
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const uint32_t sh = theta2_exp << 23;
     // the scaled comparison only in the production variant (uniform branches)
     constexpr bool kScaled = kOff32 && !kMin;
     const bool pow2 = kScaled && pow2_scale_ok(prm, theta2_exp);
+#define ORR_WALK(INV, POW2) \
+    walk_coherent<INV, kOff32, kMin, POW2, kSplit>(xs, nodes, perm, i, part, n, n_nodes, eps2, theta2, sh, out, lds)
     if (r2_cannot_overflow(prm, eps2)) {
         if (pow2)
-            walk_coherent<kInvFastNoClamp, kOff32, kMin, kScaled>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh,
-                                                                  out, lds);
+            ORR_WALK(kInvFastNoClamp, kScaled);
         else
-            walk_coherent<kInvFastNoClamp, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh,
-                                                                out, lds);
+            ORR_WALK(kInvFastNoClamp, false);
     } else {
         if (pow2)
-            walk_coherent<kInvFast, kOff32, kMin, kScaled>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out,
-                                                           lds);
+            ORR_WALK(kInvFast, kScaled);
         else
-            walk_coherent<kInvFast, kOff32, kMin, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out,
-                                                         lds);
+            ORR_WALK(kInvFast, false);
     }
+#undef ORR_WALK
 }
 
 template <int kInv>
@@ -461,14 +267,19 @@ __global__ __launch_bounds__(256) void k_selftest_inv_sqrt(uint32_t first, uint6
 
 __global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
 
-// e with theta2 = 2^-e exactly, 0 <= e <= 126; kNotPow2 otherwise.
-constexpr uint32_t kNotPow2 = 0xffffffffu;
-uint32_t theta2_pow2_exp(float theta2) {
-    if (!(theta2 > 0.0f && theta2 <= 1.0f)) return kNotPow2;
-    int ex = 0;
-    const float m = std::frexp(theta2, &ex);  // theta2 = m 2^ex, m in [0.5, 1)
-    if (m != 0.5f || 1 - ex > 126) return kNotPow2;
-    return (uint32_t)(1 - ex);
+// Hardware waves per target wave of the coherent walk: grids of target waves
+// that fill only part of the GPU's wave slots (256 CUs x 4 SIMDs x 8 waves)
+// share each target wave's terms among 2 or 4 hardware waves (walk_coherent,
+// kSplit), so that more SIMDs work on the same walks.
+#ifndef ORR_WALK_SPLIT_FORCE
+#define ORR_WALK_SPLIT_FORCE 0
+#endif
+uint32_t walk_split(int64_t target_waves) {
+    if (ORR_WALK_SPLIT_FORCE) return ORR_WALK_SPLIT_FORCE;
+    constexpr int64_t kSlots = 256 * 4 * 8;
+    if (4 * target_waves <= kSlots / 2) return 4;
+    if (2 * target_waves <= kSlots / 2) return 2;
+    return 1;
 }
 
 hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, float eps2, float theta2,
@@ -478,24 +289,29 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
     if (mode != kWalkIndependent) {
         const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
         const int64_t nw = ceil_div(rg.count, (int64_t)64);
-        // 8 XCD lists of up to L waves each (scheduled_target)
+        // 8 XCD lists of up to L target waves each (scheduled_target)
         const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(nw, (int64_t)kScheduleRegions);
-        const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64));
+        const uint32_t split = mode == kWalkCoherentMin ? 1u : walk_split(nw);
+        const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64 / split));
         const uint32_t wave0 = (uint32_t)(rg.first / 64);
         const uint32_t e2 = theta2_pow2_exp(theta2);
-#define ORR_COHERENT(OFF32, MIN)                                                                                  \
-    k_walk_coherent<OFF32, MIN><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, nb, \
-                                                                     eps2, theta2, rg.order, (uint32_t)nw, wave0,  \
-                                                                     e2, out)
+#define ORR_COHERENT(OFF32, MIN, SPLIT)                                                                          \
+    k_walk_coherent<OFF32, MIN, SPLIT><<<cblocks, kWalkBlock, 0, s>>>(ws.xs, ws.nodes, ws.prm, ws.vals[0], end, \
+                                                                     nb, eps2, theta2, rg.order, (uint32_t)nw,  \
+                                                                     wave0, e2, out)
         if (mode == kWalkCoherentMin) {
             if (off32)
-                ORR_COHERENT(true, true);
+                ORR_COHERENT(true, true, 1);
             else
-                ORR_COHERENT(false, true);
-        } else if (off32) {
-            ORR_COHERENT(true, false);
+                ORR_COHERENT(false, true, 1);
+        } else if (!off32) {
+            ORR_COHERENT(false, false, 1);
+        } else if (split == 4) {
+            ORR_COHERENT(true, false, 4);
+        } else if (split == 2) {
+            ORR_COHERENT(true, false, 2);
         } else {
-            ORR_COHERENT(false, false);
+            ORR_COHERENT(true, false, 1);
         }
 #undef ORR_COHERENT
     } else {

@@ -3,6 +3,8 @@
 // the bound under which no r2 can overflow.
 #pragma once
 
+#include <cmath>
+
 #include "orr_internal.h"
 
 #ifndef ORR_WALK_BLOCK
@@ -54,6 +56,16 @@ __device__ __forceinline__ bool pow2_scale_ok(const DevParams *prm, uint32_t e) 
     const float L2 = prm->side * prm->side;
     const uint32_t ex = (__float_as_uint(L2) >> 23) & 0xffu;
     return ex >= 1u + 2u * (uint32_t)kMaxLevel && ex + e <= 254u;
+}
+
+// e with theta2 = 2^-e exactly, 0 <= e <= 126; kNotPow2 otherwise.
+constexpr uint32_t kNotPow2 = 0xffffffffu;
+inline uint32_t theta2_pow2_exp(float theta2) {
+    if (!(theta2 > 0.0f && theta2 <= 1.0f)) return kNotPow2;
+    int ex = 0;
+    const float m = std::frexp(theta2, &ex);  // theta2 = m 2^ex, m in [0.5, 1)
+    if (m != 0.5f || 1 - ex > 126) return kNotPow2;
+    return (uint32_t)(1 - ex);
 }
 
 }  // namespace orr

@@ -21,7 +21,7 @@ TRAVERSALS = {"independent": 0, "coherent": 1}
 NOALLOC_SCRATCH_BYTES = 144 << 20  # ORR_NOALLOC_SCRATCH_BYTES of include/orr.h
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
-            "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_range",
+            "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
             "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check", "orr_tree_info_get",
             "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_selftest_inv_sqrt", "orr_tree_free")
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_walk_grouped.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_descend.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_min_advance.argtypes = [_vp, f32, f32, _vp, _vp, _vp, _vp, _vp]
+        L.orr_tree_walk_width.argtypes = [_vp, f32, f32, i32, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_walk_range.argtypes = [_vp, f32, f32, ctypes.c_int, i64, i64, _vp, _vp, _vp, _vp, _vp]
         L.orr_tree_shard_bounds.argtypes = [_vp, i32, ctypes.POINTER(i64)]
         L.orr_eval_forces.argtypes = [_vp, _vp, i64, f32, f32, i32, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, sz,
@@ -86,8 +87,8 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_free.argtypes = [_vp]
         L.orr_tree_free.restype = None
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
-                     "orr_tree_walk_min_advance", "orr_tree_walk_range", "orr_tree_shard_bounds",
-                     "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check",
+                     "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
+                     "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
                      "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
@@ -249,6 +250,13 @@ class Tree:
         coherent walk."""
         acc, cnt = out if out is not None else _outputs(self.n, self.device)
         _check(lib().orr_tree_walk_min_advance(self._h, eps, theta, _ptr(acc), *[_ptr(c) for c in cnt]))
+        return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
+
+    def walk_width(self, eps=0.05, theta=0.5, width=64, out=None) -> Result:
+        """The coherent walk at coherence width 32, 64, 128 or 256 with the
+        production machinery (orr_tree_walk_width)."""
+        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        _check(lib().orr_tree_walk_width(self._h, eps, theta, width, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
     def walk_range(self, first, count, eps=0.05, theta=0.5, traversal="coherent", out=None) -> Result:

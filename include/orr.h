@@ -193,6 +193,22 @@ orr_status orr_tree_walk_min_advance(const orr_tree *tree, float eps, float thet
                                      uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp,
                                      uint32_t *n_pc);
 
+/* The coherent walk of orr_tree_walk at coherence width 32, 64, 128 or 256
+ * with the production walk's machinery (node records through scalar loads,
+ * opened leaves staged in LDS and packed across the wave): the performance
+ * page's "The sub-group width" question (16 against 32 lanes; would 64 pay)
+ * and the work-group coherence of ADR-0029, "Alternatives considered".
+ * width 32: each 64-lane wave holds two groups of 32 consecutive sorted
+ * targets, each with its own node index; 64: orr_tree_walk itself; 128 and
+ * 256: 2 or 4 waves of one work-group share one node index, agreed through
+ * LDS at one barrier per step. acc, visits_own, n_pp and n_pc equal
+ * orr_tree_walk's bit for bit at every width; visits_stepped = size of the
+ * union of the walks of the target's group of `width` consecutive sorted
+ * targets. Errors: those of orr_tree_walk, and ORR_ERR_RANGE for another
+ * width (or a node array beyond 4 GiB). */
+orr_status orr_tree_walk_width(const orr_tree *tree, float eps, float theta, int32_t width, float *acc,
+                               uint32_t *visits_own, uint32_t *visits_stepped, uint32_t *n_pp, uint32_t *n_pc);
+
 /* The alternative ADR-0029 rejects ("Alternatives considered"), the
  * published warp-coherent traversal, for comparison: groups of group_width
  * consecutive sorted targets (1, 2, 4, ..., 64) share one node; the group

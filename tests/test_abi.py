@@ -90,6 +90,7 @@ def test_build_and_walk_argument_errors():
     assert L.orr_tree_walk_grouped(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_descend(None, 0.05, 0.5, 32, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_min_advance(None, 0.05, 0.5, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
+    assert L.orr_tree_walk_width(None, 0.05, 0.5, 64, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_walk_range(None, 0.05, 0.5, 1, 0, 64, None, None, None, None, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_shard_bounds(None, 8, None) == orr.ORR_ERR_INVALID_ARG
     assert L.orr_tree_info_get(None, None) == orr.ORR_ERR_INVALID_ARG
