@@ -148,6 +148,29 @@ def width_sweep(tree, acc, cnt, stream, trials=4):
     return out
 
 
+def production_width_leg(tree, acc, cnt, stream, trials=4):
+    """The coherent walk at coherence width 32, 64, 128 and 256 with the
+    production machinery (orr_tree_walk_width: scalar node loads, LDS
+    leaves; two node indices per wave at 32, work-group coherence at 128 and
+    256): walk time and stepped visits per target."""
+    import torch
+    from barnes_hut_gravitational_amd import inputs
+
+    out = {}
+    for w in (32, 64, 128, 256):
+        tree.walk_width(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
+        ev[0].record(stream)
+        for k in range(trials):
+            tree.walk_width(inputs.EPS, inputs.THETA, w, out=(acc, cnt))
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        stepped = cnt[1].to(torch.int64).sum().item() / cnt[1].numel()
+        out[str(w)] = {"walk_ms_median": percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5),
+                       "visits_stepped_per_particle": stepped}
+    return out
+
+
 def descend_leg(tree, acc, cnt, stream, trials=4):
     """The descend-together group walk (orr_tree_walk_descend: a group opens a
     node when any member would, all members descending), for comparison with
@@ -477,6 +500,7 @@ def main():
     info = tree.info()
     direct = None if args.no_direct else direct_leg(dev, stream, accuracy=not args.no_accuracy)
     widths = None if args.no_width_sweep else width_sweep(tree, acc, cnt, stream)
+    prod_widths = None if args.no_width_sweep else production_width_leg(tree, acc, cnt, stream)
     descend = None if args.no_width_sweep else descend_leg(tree, acc, cnt, stream)
     advance = None if args.no_width_sweep else advance_leg(tree, acc, cnt, stream)
     shard = None if args.no_shard else shard_leg(dev, stream)
@@ -522,6 +546,7 @@ def main():
         "tree": {"n_nodes": info["n_nodes"], "depth": info["depth"], "n_leaves": info["n_leaves"]},
         "direct": direct,
         "width_sweep": widths,
+        "production_widths": prod_widths,
         "descend_together": descend,
         "advance_rule": advance,
         "one_gpu_share": shard,
