@@ -70,11 +70,3 @@ def check_acc_bitwise(r: orr.Result, ref_acc: np.ndarray, rows=None):
     sel = slice(None) if rows is None else rows
     assert np.isfinite(ref_acc).all(), "non-finite reference acceleration"
     assert np.array_equal(r.acc.cpu().numpy()[sel].view(np.uint32), ref_acc.view(np.uint32))
-
-
-def sampled_reference(ot: oracle.Tree, eps, theta, targets_sorted: np.ndarray, groups: np.ndarray, width=64):
-    """Oracle outputs for selected sorted targets, plus union visits of selected
-    groups; returned in the caller order of those targets."""
-    acc, pp, pc, vis = oracle.walk(ot, eps, theta, targets_sorted)
-    union = oracle.union_visits(ot, eps, theta, width, groups)
-    return acc, pp, pc, vis, union

@@ -171,13 +171,20 @@ def _fp64_com(t, k):
 
 
 def test_com_close_to_fp64_and_inside_cell():
+    """Every node's float32 centre of mass lies within 1e-6 of its cell side
+    of the float64 centre of mass of its particles, and within the
+    recursive-summation bound (count + 21 levels) u max|x| of the float32
+    sums (u = 2^-24); the mass is the float64 sum to 1e-5."""
     rng = np.random.default_rng(3)
     pos, _ = inputs.make("plummer", 8192)
     mass = rng.uniform(0.1, 2.0, len(pos)).astype(np.float32)
     t = oracle.build_tree(pos, mass, 16)
+    side = np.float64(t.side) * 2.0 ** -t.level.astype(np.float64)
     for k in range(t.n_nodes):
         com, scale = _fp64_com(t, k)
-        assert np.all(np.abs(t.geom[k, :3] - com) <= 1e-5 * scale + 1e-30), k
+        dev = np.abs(t.geom[k, :3] - com)
+        assert np.all(dev <= 1e-6 * side[k]), k
+        assert np.all(dev <= (int(t.count[k]) + 21) * 2.0**-24 * scale), k
         b, c = int(t.begin[k]), int(t.count[k])
         p = t.xs[b:b + c, :3]
         assert np.all(t.geom[k, :3] >= p.min(axis=0) - 1e-6 * scale)
