@@ -608,8 +608,45 @@ orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, flo
     if (!pos || !mass || !acc) return fail(ORR_ERR_INVALID_ARG, "pos, mass and acc must not be NULL");
     if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
     if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
-    hipError_t e = launch_direct(pos, mass, n, eps * eps, acc, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = launch_direct(pos, mass, n, eps * eps, nullptr, n, acc, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "direct sum");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_direct_forces_targets(const float *pos, const float *mass, int64_t n, float eps, const int64_t *targets,
+                                     int64_t n_targets, float *acc, void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!pos || !mass || !acc || !targets)
+        return fail(ORR_ERR_INVALID_ARG, "pos, mass, targets and acc must not be NULL");
+    if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
+    if (n_targets < 0 || n_targets > ORR_MAX_N)
+        return fail(ORR_ERR_RANGE, "n_targets = %lld is outside [0, %lld]", (long long)n_targets, ORR_MAX_N);
+    if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
+    if (n_targets == 0) return ORR_OK;
+    hipError_t e = launch_direct(pos, mass, n, eps * eps, targets, n_targets, acc,
+                                 static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "direct sum over targets");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
+orr_status orr_direct_forces_fp64_targets(const float *pos, const float *mass, int64_t n, double eps,
+                                          const int64_t *targets, int64_t n_targets, double *acc, void *hip_stream) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!pos || !mass || !acc || !targets)
+        return fail(ORR_ERR_INVALID_ARG, "pos, mass, targets and acc must not be NULL");
+    if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
+    if (n_targets < 0 || n_targets > ORR_MAX_N)
+        return fail(ORR_ERR_RANGE, "n_targets = %lld is outside [0, %lld]", (long long)n_targets, ORR_MAX_N);
+    if (!(std::isfinite(eps) && eps >= 0.0))
+        return fail(ORR_ERR_RANGE, "eps must be finite and >= 0 (got %g)", eps);
+    if (n_targets == 0) return ORR_OK;
+    hipError_t e = launch_direct_fp64(pos, mass, n, eps, targets, n_targets, acc,
+                                      static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "float64 direct sum over targets");
     return ORR_OK;
     ORR_GUARD_END
 }

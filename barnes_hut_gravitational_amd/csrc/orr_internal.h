@@ -141,7 +141,14 @@ hipError_t launch_walk_width(const Workspace &ws, int width, float eps2, float t
                              hipStream_t s);
 hipError_t launch_selftest_inv_sqrt(uint32_t first, uint64_t count, unsigned long long *mismatches,
                                     uint32_t *examples, hipStream_t s);
-hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, float *acc, hipStream_t s);
+// All-pairs sums for n_out targets: caller indices targets[0 .. n_out) (NaN
+// for an index outside [0, n)), or particles 0 .. n_out - 1 (n_out = n) when
+// targets is null.
+hipError_t launch_direct(const float *pos, const float *mass, int64_t n, float eps2, const int64_t *targets,
+                         int64_t n_out, float *acc, hipStream_t s);
+// Compensated float64 sums for targets[0 .. n_out) (NaN for an index outside [0, n)).
+hipError_t launch_direct_fp64(const float *pos, const float *mass, int64_t n, double eps, const int64_t *targets,
+                              int64_t n_out, double *acc, hipStream_t s);
 uint32_t morton_hist_blocks(int64_t n);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -23,7 +23,8 @@ EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_l
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
             "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
             "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check", "orr_tree_info_get",
-            "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_selftest_inv_sqrt", "orr_tree_free")
+            "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_direct_forces_targets",
+            "orr_direct_forces_fp64_targets", "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_check.argtypes = [_vp]
         L.orr_tree_export.argtypes = [_vp] * 9
         L.orr_direct_forces.argtypes = [_vp, _vp, i64, f32, _vp, _vp]
+        L.orr_direct_forces_targets.argtypes = [_vp, _vp, i64, f32, _vp, i64, _vp, _vp]
+        L.orr_direct_forces_fp64_targets.argtypes = [_vp, _vp, i64, ctypes.c_double, _vp, i64, _vp, _vp]
         L.orr_selftest_inv_sqrt.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp]
         L.orr_tree_free.argtypes = [_vp]
         L.orr_tree_free.restype = None
@@ -90,7 +93,7 @@ def lib() -> ctypes.CDLL:
                      "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
                      "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check",
                      "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
-                     "orr_selftest_inv_sqrt"):
+                     "orr_direct_forces_targets", "orr_direct_forces_fp64_targets", "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -194,6 +197,39 @@ def orr_direct_forces(pos, mass, *, eps=0.05, out=None) -> torch.Tensor:
     n = pos.shape[0]
     acc = out if out is not None else torch.empty((n, 3), dtype=torch.float32, device=pos.device)
     _check(lib().orr_direct_forces(_ptr(pos), _ptr(mass), n, eps, _ptr(acc), _stream(pos.device)))
+    return acc
+
+
+def orr_direct_forces_targets(pos, mass, targets, *, eps=0.05, out=None) -> torch.Tensor:
+    """The all-pairs float32 direct sum for the caller-order targets (a GPU
+    int64 tensor) only (orr_direct_forces_targets); returns acc [len(targets), 3]."""
+    pos, mass = _as_inputs(pos, mass)
+    if not targets.is_cuda or targets.dtype != torch.int64 or targets.dim() != 1:
+        raise OrrError(ORR_ERR_INVALID_ARG, "targets must be a 1-d int64 GPU tensor")
+    targets = targets.contiguous()
+    m = targets.shape[0]
+    acc = out if out is not None else torch.empty((m, 3), dtype=torch.float32, device=pos.device)
+    if m == 0:
+        return acc
+    _check(lib().orr_direct_forces_targets(_ptr(pos), _ptr(mass), pos.shape[0], eps, _ptr(targets), m, _ptr(acc),
+                                           _stream(pos.device)))
+    return acc
+
+
+def orr_direct_forces_fp64_targets(pos, mass, targets, *, eps=0.05, out=None) -> torch.Tensor:
+    """The compensated float64 direct sum (the accuracy reference) for the
+    caller-order targets (a GPU int64 tensor) only
+    (orr_direct_forces_fp64_targets); returns float64 acc [len(targets), 3]."""
+    pos, mass = _as_inputs(pos, mass)
+    if not targets.is_cuda or targets.dtype != torch.int64 or targets.dim() != 1:
+        raise OrrError(ORR_ERR_INVALID_ARG, "targets must be a 1-d int64 GPU tensor")
+    targets = targets.contiguous()
+    m = targets.shape[0]
+    acc = out if out is not None else torch.empty((m, 3), dtype=torch.float64, device=pos.device)
+    if m == 0:
+        return acc
+    _check(lib().orr_direct_forces_fp64_targets(_ptr(pos), _ptr(mass), pos.shape[0], float(eps), _ptr(targets), m,
+                                                _ptr(acc), _stream(pos.device)))
     return acc
 
 

@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--no-direct", action="store_true",
                     help="skip the all-pairs direct-sum leg (Plummer 131,072)")
     ap.add_argument("--no-accuracy", action="store_true",
-                    help="skip the tree's error against the direct sum (direct sums at 131k and 1M)")
+                    help="skip the errors against the float64 direct sum (65k whole; 131k, 1M, 8M sampled)")
     ap.add_argument("--no-width-sweep", action="store_true",
                     help="skip the group-width sweep of the walk (orr_tree_walk_grouped)")
     ap.add_argument("--no-configs", action="store_true",
@@ -82,47 +82,92 @@ def walk_traffic_bytes():
 
 
 def direct_leg(dev, stream, trials=5, accuracy=True):
-    """The all-pairs direct sum (orr_direct_forces) with the walk's term on the
-    Plummer sphere of 131,072 particles: every lane does useful work on every
-    term, so this is the issue-bound rate of the exact term itself."""
+    """The all-pairs direct sum (orr_direct_forces) with the walk's term: its
+    rate on the Plummer sphere of 131,072 particles (every lane does useful
+    work on every term, so this is the issue-bound rate of the exact term
+    itself); the tree/direct crossover over Plummer spheres of 2^10 .. 2^17
+    particles (the pages' GPU direct column, "Against the two solvers it has
+    to beat"); and the tree's error at theta 0.5, and the float32 direct
+    sum's, against the compensated float64 direct sum ("Accuracy";
+    orr_direct_forces_fp64_targets) on every target of Plummer 65,536 and on
+    sampled targets of Plummer 131k, 1M and the 8M merger."""
+    import math
+
+    import numpy as np
     import torch
     from barnes_hut_gravitational_amd import inputs, orr
+
+    def timed(run, reps):
+        run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for k in range(reps):
+            run()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(reps)], 0.5)
 
     pos_np, mass_np = inputs.make_config("plummer_131k")
     P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
     acc = torch.empty((len(mass_np), 3), dtype=torch.float32, device=dev)
-    orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(trials + 1)]
-    ev[0].record(stream)
-    for k in range(trials):
-        orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    t = percentile([ev[k].elapsed_time(ev[k + 1]) for k in range(trials)], 0.5)
+    t = timed(lambda: orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc), trials)
     n = len(mass_np)
     inter = n * (n - 1)
     achieved = FLOPS_PER_INTERACTION * inter / (t * 1e-3) / 1e12
     out = {"workload": "plummer_131k", "kernel": "k_direct", "ms_median": t, "interactions": inter,
            "interactions_per_s": inter / (t * 1e-3), "achieved": achieved, "unit": "TFLOP/s",
            "frac": achieved / PEAK_FP32_TFLOPS}
-    # the tree's approximation error at theta 0.5 against the float32 direct
-    # sum on every target (the pages' "Accuracy" question), at 131k and 1M
+    # tree (whole evaluation) against direct, N = 2^10 .. 2^17
+    rows, prev = {}, None
+    crossover = None
+    for e in range(10, 18):
+        nn = 1 << e
+        p_np, m_np = inputs.make("plummer", nn)
+        Pn, Mn = torch.from_numpy(p_np).to(dev), torch.from_numpy(m_np).to(dev)
+        a = torch.empty((nn, 3), dtype=torch.float32, device=dev)
+        ws = orr.new_workspace(nn, inputs.LEAF_CAP, dev)
+        cnt = [torch.empty(nn, dtype=torch.int32, device=dev) for _ in range(4)]
+        td = timed(lambda: orr.orr_direct_forces(Pn, Mn, eps=inputs.EPS, out=a), trials)
+        tt = timed(lambda: orr.orr_eval_forces(Pn, Mn, eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP,
+                                               workspace=ws, out=(a, cnt)), trials)
+        rows[str(nn)] = {"direct_ms": td, "tree_eval_ms": tt, "tree_over_direct": tt / td}
+        r = math.log(tt / td)
+        if crossover is None and prev is not None and prev[1] > 0 >= r:
+            # log-linear interpolation of the tree/direct time ratio between the two sizes
+            crossover = math.exp(math.log(prev[0]) + (math.log(nn) - math.log(prev[0])) * prev[1] / (prev[1] - r))
+        prev = (nn, r)
+        del Pn, Mn, a, ws, cnt
+    out["crossover"] = {"rows": rows, "tree_faster_from_n": crossover}
     err = {}
-    for name in ("plummer_131k", "plummer_1m") if accuracy else ():
-        if name != "plummer_131k":
-            pos_np, mass_np = inputs.make_config(name)
-            P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
-            acc = torch.empty((len(mass_np), 3), dtype=torch.float32, device=dev)
-            orr.orr_direct_forces(P, M, eps=inputs.EPS, out=acc)
-        tree = orr.orr_eval_forces(P, M, eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP).acc
-        torch.cuda.synchronize()
-        d = (tree.double() - acc.double()).norm(dim=1)
-        a = acc.double().norm(dim=1)
+
+    def summary(got, ref):
+        d = (got.double() - ref).norm(dim=1)
+        a = ref.norm(dim=1)
         rel = d / a
-        err[name] = {"rel_rms": float(rel.pow(2).mean().sqrt()), "rel_median": float(rel.median()),
-                     "rel_p99": float(torch.quantile(rel, 0.99)), "rel_max": float(rel.max()),
-                     "rms_over_rms": float(d.pow(2).mean().sqrt() / a.pow(2).mean().sqrt())}
-    out["tree_error_vs_direct"] = err or None
+        return {"rel_rms": float(rel.pow(2).mean().sqrt()), "rel_median": float(rel.median()),
+                "rel_p99": float(torch.quantile(rel, 0.99)), "rel_max": float(rel.max()),
+                "rms_over_rms": float(d.pow(2).mean().sqrt() / a.pow(2).mean().sqrt())}
+
+    # against the compensated float64 direct sum (the pages' reference) on
+    # sampled targets; the float32 direct sum's own error on the same targets
+    # beside it (the pages give 3.7e-6 rms for their GPU direct kernel at 65,536)
+    samples = {"plummer_65k": ("plummer", 65536, None), "plummer_131k": ("plummer", 131072, 32768),
+               "plummer_1m": ("plummer", 1 << 20, 32768), "merger_8m": ("merger", 1 << 23, 16384)}
+    for name, (kind, nn, m) in samples.items() if accuracy else ():
+        pos_np, mass_np = inputs.make(kind, nn)
+        P, M = torch.from_numpy(pos_np).to(dev), torch.from_numpy(mass_np).to(dev)
+        tree = orr.orr_eval_forces(P, M, eps=inputs.EPS, theta=inputs.THETA, leaf_cap=inputs.LEAF_CAP).acc
+        idx = np.arange(nn) if m is None else np.sort(np.random.default_rng(20260811).choice(nn, m, replace=False))
+        ti = torch.from_numpy(idx.astype(np.int64)).to(dev)
+        ref = orr.orr_direct_forces_fp64_targets(P, M, ti, eps=inputs.EPS)
+        d32 = orr.orr_direct_forces_targets(P, M, ti, eps=inputs.EPS)
+        torch.cuda.synchronize()
+        err[name] = {"targets": int(len(idx)), "tree_theta_0.5": summary(tree[ti], ref),
+                     "direct_fp32": summary(d32, ref)}
+        del P, M, tree, ref, d32, ti
+        torch.cuda.empty_cache()
+    out["error_vs_fp64_direct"] = err or None
     return out
 
 

@@ -325,6 +325,33 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
 orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, float eps, float *acc,
                              void *hip_stream);
 
+/* The all-pairs float32 direct sum of orr_direct_forces for selected targets
+ * only, the accuracy reference at sizes where the whole O(n^2) sum costs too
+ * much (the performance page's "Accuracy" measures the tree against a direct
+ * sum): acc[t] ([n_targets][3]) = the sum over j = 0..n-1 in index order for
+ * the particle with caller index targets[t], bit for bit what
+ * orr_direct_forces gives that particle. targets: DEVICE int64 [n_targets],
+ * caller indices; an index outside [0, n) yields NaN in its row (the
+ * device cannot report it without a synchronisation) and reads nothing.
+ * O(n n_targets) work. Errors: ORR_ERR_INVALID_ARG (null pointer),
+ * ORR_ERR_RANGE (n, n_targets < 0 or > ORR_MAX_N, eps as orr_tree_walk),
+ * ORR_ERR_HIP. */
+orr_status orr_direct_forces_targets(const float *pos, const float *mass, int64_t n, float eps, const int64_t *targets,
+                                     int64_t n_targets, float *acc, void *hip_stream);
+
+/* The accuracy reference of the performance page ("Accuracy": the same
+ * softened force law summed with compensation in double precision), for
+ * selected targets: acc[t] ([n_targets][3], DEVICE double) = sum over every
+ * other particle j != i, in index order, of m_j d (r2 sqrt(r2))^-1 with
+ * d = x_j - x_i and r2 = dx*dx + dy*dy + dz*dz + eps^2 in IEEE double
+ * operations, each component summed with Neumaier's compensation, for the
+ * caller index i = targets[t] (DEVICE int64; outside [0, n): NaN, nothing
+ * read). The self term is left out, so eps = 0 is allowed. O(n n_targets)
+ * work. Errors: ORR_ERR_INVALID_ARG (null pointer), ORR_ERR_RANGE (n,
+ * n_targets < 0 or > ORR_MAX_N, eps negative or not finite), ORR_ERR_HIP. */
+orr_status orr_direct_forces_fp64_targets(const float *pos, const float *mass, int64_t n, double eps,
+                                          const int64_t *targets, int64_t n_targets, double *acc, void *hip_stream);
+
 /* Self-check of the walk's inverse square root. For eps >= 2^-48 the walk
  * evaluates RN(1/RN(sqrt(r2))) with a shorter instruction sequence valid for
  * r2 >= 2^-96 (every r2 >= eps^2 there); this enqueues a comparison of that

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "orr.h")
 def declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(orr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(orr_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_binding_names():
@@ -153,3 +153,26 @@ def test_noalloc_limit_and_argument_errors():
                                      None) == orr.ORR_ERR_RANGE
     assert L.orr_eval_forces_noalloc(1, 1, 100, 0.05, 0.5, 32, 2, None, None, None, None, None,
                                      None) == orr.ORR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1, 100, 0.05, 1, 10, 1), orr.ORR_ERR_INVALID_ARG), ((1, 1, 100, 0.05, None, 10, 1), orr.ORR_ERR_INVALID_ARG),
+    ((1, 1, 100, 0.05, 1, 10, None), orr.ORR_ERR_INVALID_ARG), ((1, 1, 0, 0.05, 1, 10, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 100, 0.05, 1, -1, 1), orr.ORR_ERR_RANGE), ((1, 1, 100, 1e-20, 1, 10, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 100, 0.05, 1, 0, 1), orr.ORR_OK)])
+def test_direct_targets_argument_errors(args, status):
+    """Checked before any device work; zero targets is a no-op."""
+    L = orr.lib()
+    pos, mass, n, eps, targets, m, acc = args
+    assert L.orr_direct_forces_targets(pos, mass, n, eps, targets, m, acc, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1, 100, 0.05, 1, 10, 1), orr.ORR_ERR_INVALID_ARG), ((1, 1, 100, 0.05, None, 10, 1), orr.ORR_ERR_INVALID_ARG),
+    ((1, 1, 0, 0.05, 1, 10, 1), orr.ORR_ERR_RANGE), ((1, 1, 100, -1.0, 1, 10, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 100, float("nan"), 1, 10, 1), orr.ORR_ERR_RANGE), ((1, 1, 100, 0.05, 1, -2, 1), orr.ORR_ERR_RANGE),
+    ((1, 1, 100, 0.0, 1, 0, 1), orr.ORR_OK)])
+def test_direct_fp64_targets_argument_errors(args, status):
+    L = orr.lib()
+    pos, mass, n, eps, targets, m, acc = args
+    assert L.orr_direct_forces_fp64_targets(pos, mass, n, eps, targets, m, acc, None) == status

@@ -83,3 +83,51 @@ def test_direct_equals_theta_zero_walk_on_gpu():
     d = orr.orr_direct_forces(P, M, eps=EPS)
     torch.cuda.synchronize()
     assert torch.equal(w.acc.view(torch.int32), d.view(torch.int32))
+
+
+def test_direct_targets_equal_oracle_and_whole_sum():
+    """orr_direct_forces_targets gives, for each listed caller index, the
+    bits of the oracle's float32 direct sum and of orr_direct_forces'
+    row; repeated indices repeat the row; indices outside [0, n) get NaN."""
+    print("[case] direct targets", flush=True)
+    pos, mass = inputs.make("merger", 3001)
+    n = len(mass)
+    rng = np.random.default_rng(11)
+    idx = np.concatenate([rng.choice(n, 300, replace=False), [0, n - 1, 5, 5]]).astype(np.int64)
+    P, M = to_dev(pos, mass)
+    a = orr.orr_direct_forces_targets(P, M, torch.from_numpy(idx).cuda(), eps=EPS)
+    whole = orr.orr_direct_forces(P, M, eps=EPS)
+    torch.cuda.synchronize()
+    a = a.cpu().numpy()
+    assert same_bits(a, oracle.direct_fp32(pos, mass, EPS, idx))
+    assert same_bits(a, whole.cpu().numpy()[idx])
+    bad = orr.orr_direct_forces_targets(P, M, torch.tensor([-1, n, 7, 2**40], dtype=torch.int64).cuda(), eps=EPS)
+    torch.cuda.synchronize()
+    bad = bad.cpu().numpy()
+    assert np.isnan(bad[[0, 1, 3]]).all()
+    assert same_bits(bad[2:3], oracle.direct_fp32(pos, mass, EPS, np.array([7])))
+
+
+def test_direct_fp64_targets_equal_oracle():
+    """The GPU float64 compensated reference (orr_direct_forces_fp64_targets)
+    and the oracle's (oracle.direct_fp64) sum the same IEEE double terms in
+    the same order with the same compensation, and both sides' double square
+    roots and divisions are correctly rounded: bit for bit; an index outside
+    [0, n) gets NaN."""
+    print("[case] direct fp64 targets", flush=True)
+    pos, mass = inputs.make("plummer", 5000)
+    n = len(mass)
+    p64 = pos.astype(np.float64)
+    central = int(np.argmin(np.linalg.norm(p64, axis=1)))
+    idx = np.concatenate([np.random.default_rng(12).choice(n, 200, replace=False), [0, n - 1, central]])
+    idx = idx.astype(np.int64)
+    P, M = to_dev(pos, mass)
+    a = orr.orr_direct_forces_fp64_targets(P, M, torch.from_numpy(idx).cuda(), eps=EPS)
+    torch.cuda.synchronize()
+    a = a.cpu().numpy()
+    ref = oracle.direct_fp64(pos, mass, EPS, idx)
+    print(f"[fp64] rows bit-identical: {int(np.all(a == ref, axis=1).sum())} of {len(idx)}", flush=True)
+    assert np.array_equal(a.view(np.uint64), ref.view(np.uint64))
+    bad = orr.orr_direct_forces_fp64_targets(P, M, torch.tensor([-1, n], dtype=torch.int64).cuda(), eps=EPS)
+    torch.cuda.synchronize()
+    assert np.isnan(bad.cpu().numpy()).all()
