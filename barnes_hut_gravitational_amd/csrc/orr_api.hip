@@ -36,7 +36,31 @@ orr_status hip_fail(hipError_t e, const char *where) {
     return fail(ORR_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+// Fault injection, for tests of the error paths on any machine: when the
+// environment variable ORR_FAULT_INJECT names a site, that site reports a
+// failure instead of calling HIP (or allocating). Sites: "events" (timing
+// events), "cube", "sort", "build", "moments", "walk" (every walk launch),
+// "sync" (reading the device parameters back), "scratch" (the
+// allocation-free entry's set-up), "direct", "alloc" (the host tree handle).
+bool injected(const char *site) {
+    const char *v = std::getenv("ORR_FAULT_INJECT");
+    return v && std::strcmp(v, site) == 0;
+}
+
+hipError_t maybe_fault(const char *site) { return injected(site) ? hipErrorLaunchFailure : hipSuccess; }
+
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The int a C caller passed for an enum argument, read from the argument's
+// bytes: any int may arrive there, and loading a value outside the enum's
+// range through the enum type itself would be undefined in C++.
+template <class E>
+int enum_bits(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
 
 }  // namespace
 
@@ -158,6 +182,7 @@ struct PhaseTimer {
         on = enable;
         s = stream;
         if (!on) return hipSuccess;
+        if (injected("events")) return hipErrorOutOfMemory;
         for (auto &e : ev) {
             hipError_t r = hipEventCreate(&e);
             if (r != hipSuccess) return r;
@@ -181,18 +206,23 @@ struct PhaseTimer {
 orr_status build_into(const float *pos, const float *mass, const Workspace &ws, hipStream_t s, PhaseTimer &tm) {
     hipError_t e;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_cube(pos, mass, ws, s)) != hipSuccess) return hip_fail(e, "root cube");
-    if ((e = launch_keys_and_sort(pos, mass, ws, s, tm.on ? tm.ev[tm.k++] : nullptr)) != hipSuccess)
+    if ((e = maybe_fault("cube")) != hipSuccess || (e = launch_cube(pos, mass, ws, s)) != hipSuccess)
+        return hip_fail(e, "root cube");
+    if ((e = maybe_fault("sort")) != hipSuccess ||
+        (e = launch_keys_and_sort(pos, mass, ws, s, tm.on ? tm.ev[tm.k++] : nullptr)) != hipSuccess)
         return hip_fail(e, "keys / radix sort");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_build(ws, s)) != hipSuccess) return hip_fail(e, "tree build");
+    if ((e = maybe_fault("build")) != hipSuccess || (e = launch_build(ws, s)) != hipSuccess)
+        return hip_fail(e, "tree build");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_moments(ws, s)) != hipSuccess) return hip_fail(e, "moments");
+    if ((e = maybe_fault("moments")) != hipSuccess || (e = launch_moments(ws, s)) != hipSuccess)
+        return hip_fail(e, "moments");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return ORR_OK;
 }
 
 orr_status read_params(const orr_tree *t, DevParams *out) {
+    if (injected("sync")) return hip_fail(hipErrorIllegalAddress, "hipMemcpyAsync (injected)");
     hipError_t e = hipMemcpyAsync(out, t->ws.prm, sizeof(DevParams), hipMemcpyDeviceToHost, t->stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
     if ((e = hipStreamSynchronize(t->stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -206,7 +236,7 @@ orr_status read_params(const orr_tree *t, DevParams *out) {
 #define ORR_GUARD_END                                                       \
     }                                                                       \
     catch (const std::bad_alloc &) {                                        \
-        return fail(ORR_ERR_INVALID_ARG, "host allocation failed");         \
+        return fail(ORR_ERR_HOST_MEMORY, "host allocation failed");         \
     }                                                                       \
     catch (...) {                                                           \
         return fail(ORR_ERR_INVALID_ARG, "unexpected C++ exception");      \
@@ -217,19 +247,20 @@ extern "C" {
 int orr_abi_version(void) { return ORR_ABI_VERSION; }
 
 const char *orr_status_string(orr_status s) {
-    switch (s) {
+    switch (enum_bits(s)) {
         case ORR_OK: return "ok";
         case ORR_ERR_INVALID_ARG: return "invalid argument";
         case ORR_ERR_RANGE: return "argument out of range";
         case ORR_ERR_NONFINITE: return "non-finite or negative input";
         case ORR_ERR_HIP: return "HIP runtime error";
         case ORR_ERR_WORKSPACE: return "workspace too small";
+        case ORR_ERR_HOST_MEMORY: return "host allocation failed";
     }
     return "unknown status";
 }
 
 const char *orr_traversal_name(orr_traversal t) {
-    switch (t) {
+    switch (enum_bits(t)) {
         case ORR_TRAVERSAL_INDEPENDENT: return "independent";
         case ORR_TRAVERSAL_COHERENT: return "coherent";
     }
@@ -251,6 +282,7 @@ orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_
     *out = nullptr;
     orr_status st = check_build_args(pos, mass, n, leaf_cap, workspace, workspace_bytes);
     if (st != ORR_OK) return st;
+    if (injected("alloc")) throw std::bad_alloc();
     orr_tree *t = new orr_tree;
     carve_workspace(workspace, n, leaf_cap, &t->ws);
     t->stream = static_cast<hipStream_t>(hip_stream);
@@ -271,14 +303,16 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
     ORR_GUARD_BEGIN
     g_last_error.clear();
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
-    orr_status st = check_walk_args(eps, theta, (int)traversal);
+    orr_status st = check_walk_args(eps, theta, enum_bits(traversal));
     if (st != ORR_OK) return st;
     PhaseTimer tm;
     hipError_t e = tm.init(timings != nullptr, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = launch_walk(tree->ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent, eps * eps,
-                    theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk(tree->ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
+                        eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "walk");
     if (!timings) return ORR_OK;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -299,8 +333,10 @@ orr_status orr_tree_walk_min_advance(const orr_tree *tree, float eps, float thet
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
     orr_status st = check_walk_args(eps, theta, ORR_TRAVERSAL_COHERENT);
     if (st != ORR_OK) return st;
-    hipError_t e = launch_walk(tree->ws, kWalkCoherentMin, eps * eps, theta * theta, acc, visits_own, visits_stepped,
-                               n_pp, n_pc, tree->stream);
+    hipError_t e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk(tree->ws, kWalkCoherentMin, eps * eps, theta * theta, acc, visits_own, visits_stepped,
+                        n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "min-advance walk");
     return ORR_OK;
     ORR_GUARD_END
@@ -316,8 +352,10 @@ static orr_status walk_grouped_entry(const orr_tree *tree, float eps, float thet
     if (st != ORR_OK) return st;
     if (group_width < 1 || group_width > 64 || (group_width & (group_width - 1)) != 0)
         return fail(ORR_ERR_RANGE, "group_width %d is not a power of two in [1, 64]", group_width);
-    hipError_t e = launch_walk_grouped(tree->ws, group_width, descend, eps * eps, theta * theta, acc, visits_own,
-                                       visits_stepped, n_pp, n_pc, tree->stream);
+    hipError_t e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk_grouped(tree->ws, group_width, descend, eps * eps, theta * theta, acc, visits_own,
+                                visits_stepped, n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, descend ? "descend-together walk" : "grouped walk");
     return ORR_OK;
     ORR_GUARD_END
@@ -347,8 +385,10 @@ orr_status orr_tree_walk_width(const orr_tree *tree, float eps, float theta, int
     if ((uint64_t)tree->ws.max_nodes * sizeof(NodeRec) > 0xffffffffull)
         return fail(ORR_ERR_RANGE, "n = %lld is too large for the width walks (node array beyond 4 GiB)",
                     (long long)tree->ws.n);
-    hipError_t e = launch_walk_width(tree->ws, width, eps * eps, theta * theta, acc, visits_own, visits_stepped,
-                                     n_pp, n_pc, tree->stream);
+    hipError_t e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk_width(tree->ws, width, eps * eps, theta * theta, acc, visits_own, visits_stepped,
+                              n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "width walk");
     return ORR_OK;
     ORR_GUARD_END
@@ -360,7 +400,7 @@ orr_status orr_tree_walk_range(const orr_tree *tree, float eps, float theta, orr
     ORR_GUARD_BEGIN
     g_last_error.clear();
     if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
-    orr_status st = check_walk_args(eps, theta, (int)traversal);
+    orr_status st = check_walk_args(eps, theta, enum_bits(traversal));
     if (st != ORR_OK) return st;
     const Workspace &ws = tree->ws;
     if (first < 0 || count < 0 || first > ws.n || count > ws.n - first)
@@ -371,11 +411,13 @@ orr_status orr_tree_walk_range(const orr_tree *tree, float eps, float theta, orr
         return fail(ORR_ERR_RANGE, "targets [%lld, %lld + %lld) are not whole waves of 64", (long long)first,
                     (long long)first, (long long)count);
     hipError_t e;
-    const bool coherent = traversal == ORR_TRAVERSAL_COHERENT;
+    const bool coherent = enum_bits(traversal) == ORR_TRAVERSAL_COHERENT;
     if (coherent && (e = launch_range_schedule(ws, first / 64, ceil_div(count, 64), tree->stream)) != hipSuccess)
         return hip_fail(e, "range schedule");
-    e = launch_walk_range(ws, coherent ? kWalkCoherent : kWalkIndependent, WalkRange{first, count, ws.range_order},
-                          eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk_range(ws, coherent ? kWalkCoherent : kWalkIndependent, WalkRange{first, count, ws.range_order},
+                              eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "range walk");
     return ORR_OK;
     ORR_GUARD_END
@@ -415,7 +457,7 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     g_last_error.clear();
     orr_status st = check_build_args(pos, mass, n, leaf_cap, workspace, workspace_bytes);
     if (st != ORR_OK) return st;
-    if ((st = check_walk_args(eps, theta, (int)traversal)) != ORR_OK) return st;
+    if ((st = check_walk_args(eps, theta, enum_bits(traversal))) != ORR_OK) return st;
     orr_tree t;
     carve_workspace(workspace, n, leaf_cap, &t.ws);
     t.stream = static_cast<hipStream_t>(hip_stream);
@@ -423,8 +465,10 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     hipError_t e = tm.init(timings != nullptr, t.stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((st = build_into(pos, mass, t.ws, t.stream, tm)) != ORR_OK) return st;
-    e = launch_walk(t.ws, traversal == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent, eps * eps,
-                    theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, t.stream);
+    e = maybe_fault("walk");
+    if (e == hipSuccess)
+        e = launch_walk(t.ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
+                        eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, t.stream);
     if (e != hipSuccess) return hip_fail(e, "walk");
     if (!timings) return ORR_OK;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -482,9 +526,10 @@ void *g_scratch_ptr[kMaxDevices] = {};
 // device (with that device current) and kept.
 orr_status scratch_for_current_device(void **out) {
     int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = injected("scratch") ? hipErrorNoDevice : hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (dev < 0 || dev >= kMaxDevices) return fail(ORR_ERR_HIP, "device %d is beyond the %d supported", dev, kMaxDevices);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ORR_ERR_HIP, "device %d is beyond the %d supported", dev, kMaxDevices);
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
         void *ptr = nullptr;
@@ -515,7 +560,7 @@ orr_status orr_eval_forces_noalloc(const float *pos, const float *mass, int64_t 
                     "n = %lld at leaf_cap %d needs %zu bytes of workspace; the allocation-free entry holds %zu",
                     (long long)n, leaf_cap, need, (size_t)ORR_NOALLOC_SCRATCH_BYTES);
     if (!pos || !mass) return fail(ORR_ERR_INVALID_ARG, "pos and mass must not be NULL");
-    if ((st = check_walk_args(eps, theta, (int)traversal)) != ORR_OK) return st;
+    if ((st = check_walk_args(eps, theta, enum_bits(traversal))) != ORR_OK) return st;
     void *ws = nullptr;
     if ((st = scratch_for_current_device(&ws)) != ORR_OK) return st;
     // the evaluation without timings enqueues kernels only (no allocation,
@@ -608,7 +653,9 @@ orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, flo
     if (!pos || !mass || !acc) return fail(ORR_ERR_INVALID_ARG, "pos, mass and acc must not be NULL");
     if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
     if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
-    hipError_t e = launch_direct(pos, mass, n, eps * eps, nullptr, n, acc, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = maybe_fault("direct");
+    if (e == hipSuccess)
+        e = launch_direct(pos, mass, n, eps * eps, nullptr, n, acc, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "direct sum");
     return ORR_OK;
     ORR_GUARD_END
@@ -625,8 +672,10 @@ orr_status orr_direct_forces_targets(const float *pos, const float *mass, int64_
         return fail(ORR_ERR_RANGE, "n_targets = %lld is outside [0, %lld]", (long long)n_targets, ORR_MAX_N);
     if (check_eps(eps) != ORR_OK) return ORR_ERR_RANGE;
     if (n_targets == 0) return ORR_OK;
-    hipError_t e = launch_direct(pos, mass, n, eps * eps, targets, n_targets, acc,
-                                 static_cast<hipStream_t>(hip_stream));
+    hipError_t e = maybe_fault("direct");
+    if (e == hipSuccess)
+        e = launch_direct(pos, mass, n, eps * eps, targets, n_targets, acc,
+                          static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "direct sum over targets");
     return ORR_OK;
     ORR_GUARD_END
@@ -644,8 +693,10 @@ orr_status orr_direct_forces_fp64_targets(const float *pos, const float *mass, i
     if (!(std::isfinite(eps) && eps >= 0.0))
         return fail(ORR_ERR_RANGE, "eps must be finite and >= 0 (got %g)", eps);
     if (n_targets == 0) return ORR_OK;
-    hipError_t e = launch_direct_fp64(pos, mass, n, eps, targets, n_targets, acc,
-                                      static_cast<hipStream_t>(hip_stream));
+    hipError_t e = maybe_fault("direct");
+    if (e == hipSuccess)
+        e = launch_direct_fp64(pos, mass, n, eps, targets, n_targets, acc,
+                               static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "float64 direct sum over targets");
     return ORR_OK;
     ORR_GUARD_END

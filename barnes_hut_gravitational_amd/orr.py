@@ -16,7 +16,8 @@ import torch  # loaded before liborr so both share one HIP runtime
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liborr.so")
 
-ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_ERR_WORKSPACE = range(6)
+(ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_ERR_WORKSPACE,
+ ORR_ERR_HOST_MEMORY) = range(7)
 TRAVERSALS = {"independent": 0, "coherent": 1}
 NOALLOC_SCRATCH_BYTES = 144 << 20  # ORR_NOALLOC_SCRATCH_BYTES of include/orr.h
 EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_last_error",

@@ -58,6 +58,11 @@
  *     crosses the ABI. On error, orr_last_error() gives a thread-local
  *     message; outputs are then unspecified. Argument checks happen before any
  *     device work.
+ *   - Fault injection (tests of the error paths): when the environment
+ *     variable ORR_FAULT_INJECT names a site ("events", "cube", "sort",
+ *     "build", "moments", "walk", "sync", "scratch", "direct", "alloc"), the
+ *     entry points report a failure there (ORR_ERR_HIP, or
+ *     ORR_ERR_HOST_MEMORY for "alloc") instead of calling HIP or allocating.
  *   - Inputs whose positions or masses are non-finite, whose masses are
  *     negative, or whose extent overflows float32 are detected on the device
  *     while the tree is built; the evaluation still runs to completion on a
@@ -86,7 +91,8 @@ typedef enum {
     ORR_ERR_RANGE = 2,       /* n, leaf_cap, eps or theta out of range */
     ORR_ERR_NONFINITE = 3,   /* non-finite input found on the device */
     ORR_ERR_HIP = 4,         /* a HIP runtime call failed */
-    ORR_ERR_WORKSPACE = 5    /* workspace smaller than orr_workspace_bytes */
+    ORR_ERR_WORKSPACE = 5,   /* workspace smaller than orr_workspace_bytes */
+    ORR_ERR_HOST_MEMORY = 6  /* a host allocation (the tree handle) failed */
 } orr_status;
 
 /* Which walk the device runs (enum TreeTraversal of the solver page). */

@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liborr_oracle.so")
+# ORR_ORACLE_LIB: another build of the same source (the sanitizer test)
+_LIB_PATH = os.environ.get("ORR_ORACLE_LIB") or os.path.join(_HERE, "liborr_oracle.so")
 _lib = None
 
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
