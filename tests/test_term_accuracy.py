@@ -1,0 +1,81 @@
+"""Why the walk keeps the exactly rounded term (RN(1/RN(sqrt(r2))) and
+unfused sums) instead of a reciprocal-square-root instruction and fused
+multiply-adds: on the Plummer sphere of 1,048,576 particles, the 2,000
+targets with the smallest |a| are re-summed term by term in their walk's
+order (tests/term_variants.c) with
+
+- the exact sequence: must give the oracle's accelerations bit for bit (so
+  the terms and their order are right);
+- inv = RN(1/sqrt(r2)) (a correctly rounded reciprocal square root), the
+  sums unfused;
+- that with fused multiply-adds in r2 and in a += f d.
+
+Both cheaper variants leave the 1e-5 bar on maximum relative per-particle
+error (the benchmark spec's accuracy bar; the variants reach 1.22e-5 and
+1.29e-5 at one target near the centre, where |a| is about 2 % of the
+median), while the exact sequence meets it with zero error. CPU only."""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from barnes_hut_gravitational_amd import inputs
+
+pytestmark = pytest.mark.slow
+HERE = os.path.dirname(os.path.abspath(__file__))
+BAR = 1e-5
+
+
+@pytest.fixture(scope="module")
+def variants(tmp_path_factory):
+    so = str(tmp_path_factory.mktemp("term") / "term_variants.so")
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-mfpmath=sse",
+                    os.path.join(HERE, "term_variants.c"), "-o", so, "-lm"], check=True)
+    L = ctypes.CDLL(so)
+    fp = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+    for f in ("sum_exact", "sum_rsqrt", "sum_rsqrt_fma"):
+        getattr(L, f).argtypes = [fp, ctypes.c_int64, ctypes.c_float, fp]
+        getattr(L, f).restype = None
+    return L
+
+
+def walk_terms(t, i, eps, theta):
+    """(m, dx, dy, dz) of every term of sorted target i, in walk order."""
+    nodes, act = oracle.walk_trace(t, eps, theta, i)
+    xi = t.xs[i, :3]
+    parts = []
+    for nd, a in zip(nodes, act):
+        if a == 0:  # accepted cell: its monopole
+            g = t.geom[nd]
+            parts.append(np.array([[g[3], g[0] - xi[0], g[1] - xi[1], g[2] - xi[2]]], np.float32))
+        elif a == 1:  # opened leaf: its particles in sorted order
+            b, c = int(t.begin[nd]), int(t.count[nd])
+            p = t.xs[b:b + c]
+            parts.append(np.stack([p[:, 3], p[:, 0] - xi[0], p[:, 1] - xi[1], p[:, 2] - xi[2]], 1).astype(np.float32))
+    return np.ascontiguousarray(np.concatenate(parts))
+
+
+def test_cheaper_term_arithmetic_misses_the_bar_at_1m(variants):
+    eps, theta = inputs.EPS, inputs.THETA
+    pos, mass = inputs.make_config("plummer_1m")
+    t = oracle.build_tree(pos, mass, inputs.LEAF_CAP)
+    acc, _, _, _ = oracle.walk(t, eps, theta)
+    mag = np.linalg.norm(acc.astype(np.float64), axis=1)
+    sel = np.argsort(mag)[:2000]
+    eps2 = np.float32(eps) * np.float32(eps)
+    worst = {"sum_rsqrt": 0.0, "sum_rsqrt_fma": 0.0}
+    out = np.zeros(3, np.float32)
+    for i in sel:
+        terms = walk_terms(t, int(i), eps, theta)
+        variants.sum_exact(terms, len(terms), eps2, out)
+        assert np.array_equal(out.view(np.uint32), acc[i].view(np.uint32)), i
+        for k in worst:
+            getattr(variants, k)(terms, len(terms), eps2, out)
+            worst[k] = max(worst[k], float(np.linalg.norm(out.astype(np.float64) - acc[i]) / mag[i]))
+    print(f"max relative error over the 2,000 smallest |a|: {worst}")
+    assert worst["sum_rsqrt"] > BAR and worst["sum_rsqrt_fma"] > BAR
+    assert worst["sum_rsqrt"] < 10 * BAR and worst["sum_rsqrt_fma"] < 10 * BAR
