@@ -58,5 +58,35 @@ def build(jobs: int = 8, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+def resources(src: str = "walk.hip") -> list:
+    """Per-kernel resources the compiler gives one source's gfx950 code:
+    (kernel, VGPRs, SGPRs, LDS bytes, scratch bytes per lane, VGPR spills),
+    from the code object metadata of a device-only assembly build."""
+    import re
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as d:
+        asm = os.path.join(d, "k.s")
+        cmd = [HIPCC, *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        text = open(asm).read()
+    meta = text[text.index("amdhsa.kernels:"):]
+    out = []
+    for blk in meta.split("  - .agpr_count")[1:]:
+        def field(k):
+            return re.search(r"\." + k + r":\s+(\S+)", blk).group(1)
+        out.append((field("name"), int(field("vgpr_count")), int(field("sgpr_count")),
+                    int(field("group_segment_fixed_size")), int(field("private_segment_fixed_size")),
+                    int(field("vgpr_spill_count"))))
+    return out
+
+
 if __name__ == "__main__":
-    print(build())
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        for src in sys.argv[2:] or ["walk.hip"]:
+            for name, v, sg, lds, scratch, spill in resources(src):
+                print(f"{src}\t{name}\tvgpr {v}\tsgpr {sg}\tlds {lds}\tscratch {scratch}\tvgpr_spill {spill}")
+    else:
+        print(build())

@@ -167,8 +167,11 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
 
 // Eight waves per SIMD (at most 64 VGPRs): the occupancy the walk's issue
 // rate needs; without the bound the unrolled leaf sums take more registers.
+// The split variants run only on grids that fill at most half the wave
+// slots, so they take the registers they need (at least 4 waves per SIMD)
+// instead of spilling 30 of them to scratch.
 template <bool kOff32, bool kMin, uint32_t kSplit>
-__global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_walk_coherent(const float4 *__restrict__ xs,
+__global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(kSplit == 1 ? 8 : 4, 8))) void k_walk_coherent(const float4 *__restrict__ xs,
                                                               const NodeRec *__restrict__ nodes,
                                                               const DevParams *__restrict__ prm,
                                                               const uint32_t *__restrict__ perm, uint32_t n,
