@@ -646,6 +646,22 @@ orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t
     ORR_GUARD_END
 }
 
+orr_status orr_tree_export_schedule(const orr_tree *tree, uint32_t *wave_cost, uint32_t *order) {
+    ORR_GUARD_BEGIN
+    g_last_error.clear();
+    if (!tree) return fail(ORR_ERR_INVALID_ARG, "tree must not be NULL");
+    const Workspace &ws = tree->ws;
+    hipError_t e;
+    if (wave_cost && (e = hipMemcpyAsync(wave_cost, ws.wave_cost, sizeof(uint32_t) * (size_t)ws.n_waves,
+                                         hipMemcpyDeviceToDevice, tree->stream)) != hipSuccess)
+        return hip_fail(e, "export wave costs");
+    if (order && (e = hipMemcpyAsync(order, ws.wave_order, sizeof(uint32_t) * (size_t)schedule_slots(ws.n_waves),
+                                     hipMemcpyDeviceToDevice, tree->stream)) != hipSuccess)
+        return hip_fail(e, "export schedule");
+    return ORR_OK;
+    ORR_GUARD_END
+}
+
 orr_status orr_direct_forces(const float *pos, const float *mass, int64_t n, float eps, float *acc,
                              void *hip_stream) {
     ORR_GUARD_BEGIN

@@ -23,6 +23,8 @@ namespace orr {
 constexpr int kWaveOrderThreads = kWaveCostBins / 2;
 constexpr uint32_t kScheduleRegions = 64;
 constexpr uint32_t kContiguousSlack = 5;  // percent
+// Waves at the end of a long list that run longest first (see wave_order_list).
+constexpr uint32_t kScheduleTail = 1024;
 // Slots of the schedule buffer for n_waves waves: the 8 lists and their lengths.
 inline int64_t schedule_slots(int64_t n_waves) {
     return (int64_t)kScheduleRegions * ((n_waves + kScheduleRegions - 1) / kScheduleRegions) + 8;
@@ -38,9 +40,15 @@ static_assert(64 * kMaxLevel + 32 * kMaxLevel < kWaveCostBins, "wave cost range"
 // holds them when the eighths carry nearly equal work, else regions dealt in
 // a snake over their total cost (ranks 0..7 to lists 0..7, ranks 8..15 to
 // lists 7..0, ...), which evens the work out. List x is stored at
-// order[x L .. x L + len_x) with L = R kScheduleRegions / 8, its waves in
-// decreasing cost (longest first); len_x at order[8 L + x]. Equal costs keep
-// the LDS atomics' order, in which neighbouring waves stay together.
+// order[x L .. x L + len_x) with L = R kScheduleRegions / 8; len_x at
+// order[8 L + x]. A list of at most 2 kScheduleTail waves (two rounds of an
+// XCD's wave slots or fewer) runs in decreasing cost (longest first). A
+// longer one runs many rounds, and there the waves that run together should
+// be neighbours, which share nodes and leaves in the XCD's L2: its
+// kScheduleTail cheapest waves (whole cost bins, so at least that many) end the
+// list, longest first, and the others run before them in the list's own
+// order (increasing wave index within each region). Equal costs in the tail
+// keep the LDS atomics' order, in which neighbouring waves stay together.
 constexpr int kOrderCached = 16;  // costs per thread held in registers (list positions t + 1024 i)
 constexpr int kRegionUnroll = 4;  // loads in flight per region in the region sums
 
@@ -69,6 +77,8 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
     __shared__ uint32_t rcost[kScheduleRegions];
     __shared__ uint32_t myreg[kPerList];
     __shared__ uint32_t wsum[kWaves];
+    __shared__ uint32_t head_at[kOrderCached * kWaves];  // head positions of a chunk's (i, wave) groups
+    __shared__ uint32_t tail_bin, head_len;
     const uint32_t t = threadIdx.x, lane = t & 63u, wv = t >> 6;
     const uint32_t R = (n_waves + kScheduleRegions - 1u) / kScheduleRegions;
     const uint32_t Rm = R > 1u ? 0xffffffffu / R + 1u : 0u;
@@ -148,11 +158,53 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
         for (int i = 0; i < kOrderCached; i++)
             if (c[i] < kBins) atomicAdd(&bins[kBins - 1u - c[i]], 1u);
     };
+    // Places a chunk: a wave of bin b < tail_bin goes to the head, at its
+    // rank among the head's waves in list order (position base + 1024 i +
+    // 64 v + lane: ranks from the ballots of the chunk's (i, v) groups, scanned
+    // in that order by wave 0, plus the head waves of earlier chunks); any
+    // other wave to its bin's next place.
     auto place_chunk = [&](uint32_t base, const uint32_t(&c)[kOrderCached]) {
+        const uint32_t tb = tail_bin;
+        uint64_t head[kOrderCached];
 #pragma unroll
-        for (int i = 0; i < kOrderCached; i++)
-            if (c[i] < kBins)
-                order[atomicAdd(&bins[kBins - 1u - c[i]], 1u)] = wave_at(base + t + (uint32_t)i * kWaveOrderThreads);
+        for (int i = 0; i < kOrderCached; i++) {
+            head[i] = __builtin_amdgcn_ballot_w64(c[i] < kBins && kBins - 1u - c[i] < tb);
+            if (lane == 0u) head_at[i * kWaves + wv] = (uint32_t)__builtin_popcountll(head[i]);
+        }
+        __syncthreads();
+        if (wv == 0u) {
+            static_assert(kOrderCached * kWaves == 4u * 64u, "four groups per lane");
+            uint32_t g[4], sum = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                g[k] = head_at[4u * lane + k];
+                sum += g[k];
+            }
+            uint32_t inc = sum;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(inc, o, 64);
+                if (lane >= (uint32_t)o) inc += y;
+            }
+            uint32_t at = head_len + inc - sum;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                head_at[4u * lane + k] = at;
+                at += g[k];
+            }
+            if (lane == 63u) head_len = at;
+        }
+        __syncthreads();
+        const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int i = 0; i < kOrderCached; i++) {
+            if (c[i] >= kBins) continue;
+            const uint32_t w = wave_at(base + t + (uint32_t)i * kWaveOrderThreads);
+            if ((head[i] >> lane) & 1ull)
+                order[x * L + head_at[i * kWaves + wv] + (uint32_t)__builtin_popcountll(head[i] & below)] = w;
+            else
+                order[atomicAdd(&bins[kBins - 1u - c[i]], 1u)] = w;
+        }
+        __syncthreads();  // head_at is rewritten by the next chunk
     };
     load_chunk(0u, cb);
     count_chunk(cb);
@@ -176,6 +228,20 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
     for (uint32_t v = 0; v < wv; v++) before += wsum[v];
     bins[2u * t] = before;
     bins[2u * t + 1u] = before + c0;
+    // The tail: the bins from the one holding decreasing-cost position
+    // len - kScheduleTail on (none of them in a list of at most 2 kScheduleTail).
+    {
+        uint32_t len = 0;
+        for (uint32_t k = 0; k < kPerList; k++) len += min(R, n_waves - min(n_waves, myreg[k] * R));
+        const uint32_t h = len > 2u * kScheduleTail ? len - kScheduleTail : 0u;
+        const uint32_t s0 = before - x * L, s1 = s0 + c0;  // list positions of bins 2t and 2t + 1
+        if (t == 0u) {
+            head_len = 0u;
+            if (h == 0u) tail_bin = 0u;
+        }
+        if (h != 0u && c0 != 0u && s0 <= h && h < s1) tail_bin = 2u * t;
+        if (h != 0u && c1 != 0u && s1 <= h && h < s1 + c1) tail_bin = 2u * t + 1u;
+    }
     __syncthreads();
     place_chunk(0u, cb);
     for (uint32_t base = kChunk; base < L; base += kChunk) {

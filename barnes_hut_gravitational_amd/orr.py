@@ -24,8 +24,8 @@ EXPORTED = ("orr_abi_version", "orr_status_string", "orr_traversal_name", "orr_l
             "orr_workspace_bytes", "orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped",
             "orr_tree_walk_descend", "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
             "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check", "orr_tree_info_get",
-            "orr_tree_check", "orr_tree_export", "orr_direct_forces", "orr_direct_forces_targets",
-            "orr_direct_forces_fp64_targets", "orr_selftest_inv_sqrt", "orr_tree_free")
+            "orr_tree_check", "orr_tree_export", "orr_tree_export_schedule", "orr_direct_forces",
+            "orr_direct_forces_targets", "orr_direct_forces_fp64_targets", "orr_selftest_inv_sqrt", "orr_tree_free")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.orr_tree_info_get.argtypes = [_vp, ctypes.POINTER(TreeInfo)]
         L.orr_tree_check.argtypes = [_vp]
         L.orr_tree_export.argtypes = [_vp] * 9
+        L.orr_tree_export_schedule.argtypes = [_vp] * 3
         L.orr_direct_forces.argtypes = [_vp, _vp, i64, f32, _vp, _vp]
         L.orr_direct_forces_targets.argtypes = [_vp, _vp, i64, f32, _vp, i64, _vp, _vp]
         L.orr_direct_forces_fp64_targets.argtypes = [_vp, _vp, i64, ctypes.c_double, _vp, i64, _vp, _vp]
@@ -93,7 +94,8 @@ def lib() -> ctypes.CDLL:
         for name in ("orr_build_tree", "orr_tree_walk", "orr_tree_walk_grouped", "orr_tree_walk_descend",
                      "orr_tree_walk_min_advance", "orr_tree_walk_width", "orr_tree_walk_range",
                      "orr_tree_shard_bounds", "orr_eval_forces", "orr_eval_forces_noalloc", "orr_workspace_check",
-                     "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_direct_forces",
+                     "orr_tree_info_get", "orr_tree_check", "orr_tree_export", "orr_tree_export_schedule",
+                     "orr_direct_forces",
                      "orr_direct_forces_targets", "orr_direct_forces_fp64_targets", "orr_selftest_inv_sqrt"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -337,6 +339,14 @@ class Tree:
         _check(lib().orr_tree_export(self._h, *[_ptr(out[k]) for k in
                                                 ("keys_sorted", "perm", "level", "begin", "count", "escape",
                                                  "geom", "s2")]))
+        return out
+
+    def export_schedule(self) -> dict:
+        """The coherent walk's schedule: wave costs and the eight XCD lists."""
+        nw = (self.n + 63) // 64
+        out = {"wave_cost": torch.empty(nw, dtype=torch.int32, device=self.device),
+               "order": torch.empty(64 * ((nw + 63) // 64) + 8, dtype=torch.int32, device=self.device)}
+        _check(lib().orr_tree_export_schedule(self._h, _ptr(out["wave_cost"]), _ptr(out["order"])))
         return out
 
     def __del__(self):

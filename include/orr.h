@@ -319,6 +319,19 @@ orr_status orr_tree_check(const orr_tree *tree);
 orr_status orr_tree_export(const orr_tree *tree, uint64_t *keys_sorted, uint32_t *perm, uint8_t *level,
                            uint32_t *begin, uint32_t *count, uint32_t *escape, float *geom, float *s2);
 
+/* Enqueue device-to-device copies of the coherent walk's schedule, which the
+ * tree build computes and which decides only when each target wave runs, never
+ * what it computes (the orrery solver page, "The mitigation": waves of 64
+ * consecutive sorted targets). wave_cost [n_waves] (n_waves = ceil(n / 64),
+ * uint32): a wave's estimated run time, its targets' summed leaf level plus 32
+ * times the levels between its deepest leaf and the smallest cell holding all
+ * its targets. order [64 ceil(n_waves / 64) + 8] (uint32): eight lists of
+ * waves, one per XCD, list x at order[x L ..], L = 8 ceil(n_waves / 64), its
+ * length at order[8 L + x]; entries past a list's length are unspecified.
+ * Either pointer may be NULL. Errors: ORR_ERR_INVALID_ARG (NULL tree),
+ * ORR_ERR_HIP. */
+orr_status orr_tree_export_schedule(const orr_tree *tree, uint32_t *wave_cost, uint32_t *order);
+
 /* All-pairs float32 direct sum, the reference the tree is measured against
  * (the direct solver of the orrery performance page, "Against the two solvers
  * it has to beat"): for every particle i, acc[i] = sum over j = 0..n-1 in

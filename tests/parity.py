@@ -70,3 +70,29 @@ def check_acc_bitwise(r: orr.Result, ref_acc: np.ndarray, rows=None):
     sel = slice(None) if rows is None else rows
     assert np.isfinite(ref_acc).all(), "non-finite reference acceleration"
     assert np.array_equal(r.acc.cpu().numpy()[sel].view(np.uint32), ref_acc.view(np.uint32))
+
+
+def host_wave_cost(ex, n):
+    """The coherent walk's per-wave cost estimate recomputed on the host from an
+    exported tree (Tree.export()): for each wave of 64 consecutive sorted
+    targets, the summed level of its targets' leaves plus 32 times the levels
+    between its deepest leaf and the smallest cell holding all its targets
+    (whole 3-bit digits of the common prefix of its first and last key)."""
+    keys = ex["keys_sorted"].cpu().numpy().view(np.uint64)
+    level = ex["level"].cpu().numpy().astype(np.int64)
+    begin, count, escape = (u32(ex[k_]).astype(np.int64) for k_ in ("begin", "count", "escape"))
+    leaf = escape == np.arange(len(escape)) + 1
+    lvl = np.repeat(level[leaf], count[leaf])  # leaves in preorder cover the sorted targets in order
+    assert len(lvl) == n and np.array_equal(begin[leaf], np.concatenate([[0], np.cumsum(count[leaf])[:-1]]))
+    nw = (n + 63) // 64
+    pad = np.full(64 * nw, -1, np.int64)
+    pad[:n] = lvl
+    pad = pad.reshape(nw, 64)
+    depth_sum = np.where(pad >= 0, pad, 0).sum(axis=1)
+    deepest = pad.max(axis=1)
+    first_key = keys[0::64].astype(np.uint64)
+    last_key = keys[np.minimum(np.arange(nw) * 64 + 63, n - 1)]
+    x = first_key ^ last_key
+    bl = np.array([int(v).bit_length() for v in x.tolist()], np.int64)
+    enclosing = np.where(x == 0, 21, (64 - bl - 1) // 3)
+    return depth_sum + 32 * np.maximum(0, deepest - enclosing)

@@ -16,7 +16,7 @@ import torch
 import oracle
 from barnes_hut_gravitational_amd import inputs, orr
 
-from parity import to_dev, u32
+from parity import host_wave_cost, to_dev, u32
 
 pytestmark = pytest.mark.gpu
 EPS, THETA = inputs.EPS, inputs.THETA
@@ -44,24 +44,8 @@ def as_u32(r):
 def expected_bounds(ex, n, cap, k):
     """The split rule of orr_tree_shard_bounds over the cost estimate,
     recomputed from the exported tree."""
-    keys = ex["keys_sorted"].cpu().numpy().view(np.uint64)
-    level = ex["level"].cpu().numpy().astype(np.int64)
-    begin, count, escape = (u32(ex[k_]).astype(np.int64) for k_ in ("begin", "count", "escape"))
-    leaf = escape == np.arange(len(escape)) + 1
-    lvl = np.repeat(level[leaf], count[leaf])  # leaves in preorder cover the sorted targets in order
-    assert len(lvl) == n and np.array_equal(begin[leaf], np.concatenate([[0], np.cumsum(count[leaf])[:-1]]))
-    nw = (n + 63) // 64
-    pad = np.full(64 * nw, -1, np.int64)
-    pad[:n] = lvl
-    pad = pad.reshape(nw, 64)
-    depth_sum = np.where(pad >= 0, pad, 0).sum(axis=1)
-    deepest = pad.max(axis=1)
-    first_key = keys[0::64].astype(np.uint64)
-    last_key = keys[np.minimum(np.arange(nw) * 64 + 63, n - 1)]
-    x = first_key ^ last_key
-    bl = np.array([int(v).bit_length() for v in x.tolist()], np.int64)
-    enclosing = np.where(x == 0, 21, (64 - bl - 1) // 3)
-    cost = depth_sum + 32 * np.maximum(0, deepest - enclosing)
+    cost = host_wave_cost(ex, n)
+    nw = len(cost)
     total = int(cost.sum())
     pre = np.concatenate([[0], np.cumsum(cost)])
     b = [0]
