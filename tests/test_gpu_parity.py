@@ -108,6 +108,25 @@ def test_degenerate_inputs():
     run_full_case(pos * np.float32(1e30), mass, 32, EPS, 0.5)
 
 
+@pytest.mark.parametrize("n", [16384, 16385])
+def test_sort_tile_edges(n):
+    """The sort's 4,096-key tiles: 16,384 keys fill four tiles, 16,385 leave a
+    last tile of one key. The oracle's tree and walk for Plummer, for heavy
+    duplicates on a lattice (long runs of equal keys across tiles, so
+    stability decides the order), for a single point, and for a signed-zero
+    minimum (the corner must be +0)."""
+    pos, mass = inputs.make("plummer", n)
+    run_full_case(pos, mass, 32, EPS, 0.5)
+    rng = np.random.default_rng(5)
+    lat = rng.integers(0, 4, (n, 3)).astype(np.float32)
+    run_full_case(lat, np.full(n, 1 / n, np.float32), 8, EPS, 0.5)
+    run_full_case(np.full((n, 3), -1.5, np.float32), np.full(n, 1 / n, np.float32), 32, EPS, 0.5)
+    z = rng.uniform(0, 1, (n, 3)).astype(np.float32)
+    z[::3, 1] = np.float32(-0.0)
+    z[1::3, 1] = np.float32(0.0)
+    run_full_case(z, np.full(n, 1 / n, np.float32), 32, EPS, 0.5)
+
+
 @pytest.mark.parametrize("name", ["plummer_16k", "plummer_131k", "uniform_262k"])
 def test_configs_full(name):
     pos, mass = inputs.make_config(name)
@@ -144,8 +163,12 @@ def test_configs_large_every_target(name):
     print(f"[{name}] timings {r.timings}", flush=True)
 
 
-def test_nonfinite_input_reported():
-    pos, mass = inputs.make("plummer", 1000)
+@pytest.mark.parametrize("n", [1000, 20000])
+def test_nonfinite_input_reported(n):
+    """Non-finite positions and masses and negative masses are flagged, with
+    the particle at block 0 of 4 (1,000 particles) or of 79 (20,000) blocks
+    of the cube and key kernels."""
+    pos, mass = inputs.make("plummer", n)
     for bad_pos, bad_mass in ((np.nan, None), (np.inf, None), (None, -1.0), (None, np.nan)):
         p, m = pos.copy(), mass.copy()
         if bad_pos is not None:
