@@ -25,6 +25,9 @@
 // wave the 64 targets 64 w .. 64 w + 63); outputs go straight to the
 // caller's order through perm (the scatter step of the performance page's
 // "Where one evaluation goes" table).
+#include <cstdlib>
+#include <cstring>
+
 #include "orr_internal.h"
 #include "term.h"
 #include "schedule.h"
@@ -290,7 +293,9 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
     const uint32_t nb = (uint32_t)ws.max_nodes;
     const uint32_t end = (uint32_t)(rg.first + rg.count);  // targets [first, end) are walked
     if (mode != kWalkIndependent) {
-        const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull;
+        const char *force = std::getenv("ORR_WALK_NODE_OFFSETS");  // "64": the large-tree path at any size
+        const bool off32 = (uint64_t)ws.max_nodes * sizeof(NodeRec) <= 0xffffffffull &&
+                           !(force && std::strcmp(force, "64") == 0);
         const int64_t nw = ceil_div(rg.count, (int64_t)64);
         // 8 XCD lists of up to L target waves each (scheduled_target)
         const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(nw, (int64_t)kScheduleRegions);

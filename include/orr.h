@@ -63,6 +63,12 @@
  *     "build", "moments", "walk", "sync", "scratch", "direct", "alloc"), the
  *     entry points report a failure there (ORR_ERR_HIP, or
  *     ORR_ERR_HOST_MEMORY for "alloc") instead of calling HIP or allocating.
+ *   - Node addressing (tests of the large-tree path): the coherent walk
+ *     kernel addresses the node records by 32-bit byte offsets when the workspace's
+ *     node bound (orr_workspace_bytes) fits in 4 GiB, about 82 million
+ *     particles at leaf capacity 32, and by 64-bit indices above. Setting the
+ *     environment variable ORR_WALK_NODE_OFFSETS to "64" makes every launch of
+ *     it take the 64-bit path; results are the same bit for bit.
  *   - Inputs whose positions or masses are non-finite, whose masses are
  *     negative, or whose extent overflows float32 are detected on the device
  *     while the tree is built; the evaluation still runs to completion on a

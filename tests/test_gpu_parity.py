@@ -108,6 +108,17 @@ def test_degenerate_inputs():
     run_full_case(pos * np.float32(1e30), mass, 32, EPS, 0.5)
 
 
+@pytest.mark.parametrize("kind,n,cap,theta", [("plummer", 4097, 32, 0.5), ("merger", 5000, 16, 0.7),
+                                               ("plummer", 131072, 32, 0.5)])
+def test_64bit_node_offsets(kind, n, cap, theta, monkeypatch):
+    """The coherent walk's large-tree path (node records by 64-bit index,
+    taken on its own above about 82 million particles), forced at sizes the
+    oracle finishes in seconds."""
+    monkeypatch.setenv("ORR_WALK_NODE_OFFSETS", "64")
+    pos, mass = inputs.make(kind, n)
+    run_full_case(pos, mass, cap, EPS, theta)
+
+
 @pytest.mark.parametrize("n", [16384, 16385])
 def test_sort_tile_edges(n):
     """The sort's 4,096-key tiles: 16,384 keys fill four tiles, 16,385 leave a
