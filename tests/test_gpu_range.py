@@ -93,8 +93,11 @@ def test_ranges_reproduce_the_walk(kind, n, cap, k, traversal):
     check_ranges(pos, mass, cap, k, traversal)
 
 
-@pytest.mark.parametrize("name,k", [("plummer_131k", 8), ("merger_8m", 8)])
+@pytest.mark.parametrize("name,k", [("plummer_131k", 8), ("merger_8m", 8), ("merger_8m", 2)])
 def test_ranges_configs(name, k):
+    """Eight ranges of the 8M merger give each range's schedule lists of at
+    most 2,048 waves (longest first); two ranges give lists of about 8,192
+    waves, which run their head in list order and their tail longest first."""
     pos, mass = inputs.make_config(name)
     check_ranges(pos, mass, inputs.LEAF_CAP, k, "coherent", against_oracle=False)
 
