@@ -27,6 +27,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+# Libraries the host code links: roctx, for the phase ranges that rocprofv3
+# --marker-trace shows.
+LINK_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def _compile(src: str, extra=(), build_dir=BUILD) -> str:
@@ -50,7 +53,7 @@ def build(jobs: int = 8, extra_flags=(), out: str = LIB) -> str:
     with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
         objs = list(ex.map(lambda src: _compile(src, extra_flags, build_dir), SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LINK_LIBS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")

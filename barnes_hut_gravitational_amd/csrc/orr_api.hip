@@ -11,6 +11,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "orr.h"
 #include "orr_internal.h"
 #include "schedule.h"
@@ -201,22 +203,40 @@ struct PhaseTimer {
     }
 };
 
+// A roctx range around the host-side enqueue of one phase (rocprofv3
+// --marker-trace shows it beside the phase's kernels); popped on every return.
+struct Range {
+    explicit Range(const char *name) { roctxRangePushA(name); }
+    ~Range() { roctxRangePop(); }
+    Range(const Range &) = delete;
+    Range &operator=(const Range &) = delete;
+};
+
 // Phase marks: 0 start, 1 after cube and keys, 2 after sort and gather, 3
 // after topology, 4 after moments, 5 after the walk.
 orr_status build_into(const float *pos, const float *mass, const Workspace &ws, hipStream_t s, PhaseTimer &tm) {
     hipError_t e;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = maybe_fault("cube")) != hipSuccess || (e = launch_cube(pos, mass, ws, s)) != hipSuccess)
-        return hip_fail(e, "root cube");
-    if ((e = maybe_fault("sort")) != hipSuccess ||
-        (e = launch_keys_and_sort(pos, mass, ws, s, tm.on ? tm.ev[tm.k++] : nullptr)) != hipSuccess)
-        return hip_fail(e, "keys / radix sort");
+    {
+        Range r("orr: cube, keys, sort and gather");
+        if ((e = maybe_fault("cube")) != hipSuccess || (e = launch_cube(pos, mass, ws, s)) != hipSuccess)
+            return hip_fail(e, "root cube");
+        if ((e = maybe_fault("sort")) != hipSuccess ||
+            (e = launch_keys_and_sort(pos, mass, ws, s, tm.on ? tm.ev[tm.k++] : nullptr)) != hipSuccess)
+            return hip_fail(e, "keys / radix sort");
+    }
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = maybe_fault("build")) != hipSuccess || (e = launch_build(ws, s)) != hipSuccess)
-        return hip_fail(e, "tree build");
+    {
+        Range r("orr: tree topology");
+        if ((e = maybe_fault("build")) != hipSuccess || (e = launch_build(ws, s)) != hipSuccess)
+            return hip_fail(e, "tree build");
+    }
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = maybe_fault("moments")) != hipSuccess || (e = launch_moments(ws, s)) != hipSuccess)
-        return hip_fail(e, "moments");
+    {
+        Range r("orr: moments and walk schedule");
+        if ((e = maybe_fault("moments")) != hipSuccess || (e = launch_moments(ws, s)) != hipSuccess)
+            return hip_fail(e, "moments");
+    }
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     return ORR_OK;
 }
@@ -309,10 +329,13 @@ orr_status orr_tree_walk(const orr_tree *tree, float eps, float theta, orr_trave
     hipError_t e = tm.init(timings != nullptr, tree->stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = maybe_fault("walk");
-    if (e == hipSuccess)
-        e = launch_walk(tree->ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
-                        eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    {
+        Range r("orr: walk");
+        e = maybe_fault("walk");
+        if (e == hipSuccess)
+            e = launch_walk(tree->ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
+                            eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, tree->stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "walk");
     if (!timings) return ORR_OK;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -465,10 +488,13 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     hipError_t e = tm.init(timings != nullptr, t.stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((st = build_into(pos, mass, t.ws, t.stream, tm)) != ORR_OK) return st;
-    e = maybe_fault("walk");
-    if (e == hipSuccess)
-        e = launch_walk(t.ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
-                        eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, t.stream);
+    {
+        Range r("orr: walk");
+        e = maybe_fault("walk");
+        if (e == hipSuccess)
+            e = launch_walk(t.ws, enum_bits(traversal) == ORR_TRAVERSAL_COHERENT ? kWalkCoherent : kWalkIndependent,
+                            eps * eps, theta * theta, acc, visits_own, visits_stepped, n_pp, n_pc, t.stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "walk");
     if (!timings) return ORR_OK;
     if ((e = tm.mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");

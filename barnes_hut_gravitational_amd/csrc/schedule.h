@@ -107,6 +107,10 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
         }
     }
     for (uint32_t b = t; b < kBins; b += kWaveOrderThreads) bins[b] = 0u;
+    if (t == 0u) {
+        tail_bin = 0u;  // no head unless the bin holding position len - kScheduleTail says otherwise
+        head_len = 0u;
+    }
     __syncthreads();
     if (wv == 0u) {
         // Contiguous lists (list x = regions 8x .. 8x + 7) when their estimated
@@ -235,10 +239,6 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
         for (uint32_t k = 0; k < kPerList; k++) len += min(R, n_waves - min(n_waves, myreg[k] * R));
         const uint32_t h = len > 2u * kScheduleTail ? len - kScheduleTail : 0u;
         const uint32_t s0 = before - x * L, s1 = s0 + c0;  // list positions of bins 2t and 2t + 1
-        if (t == 0u) {
-            head_len = 0u;
-            if (h == 0u) tail_bin = 0u;
-        }
         if (h != 0u && c0 != 0u && s0 <= h && h < s1) tail_bin = 2u * t;
         if (h != 0u && c1 != 0u && s1 <= h && h < s1 + c1) tail_bin = 2u * t + 1u;
     }

@@ -49,7 +49,47 @@ def parse():
                     help="skip the one-GPU share leg (range walks of the 8M merger split 8 ways)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--csv-dir", default=None,
+                    help="also write scaling.csv (the Plummer sweep) and divergence.csv (every workload, "
+                         "both traversals) into this directory")
     return ap.parse_args()
+
+
+SCALING_COLUMNS = ("n", "n_nodes", "eval_ms_median", "eval_ms_iqr", "walk_ms_median", "eval_ms_per_n_log2n",
+                   "cells_per_particle", "visits_own_per_particle", "visits_stepped_per_particle")
+DIVERGENCE_COLUMNS = ("workload", "n", "n_nodes", "eval_ms_median", "eval_ms_iqr", "coherent_walk_ms",
+                      "independent_walk_ms", "coherent_speedup_walk", "visits_own_per_particle",
+                      "visits_stepped_per_particle", "redundancy", "interactions", "interactions_per_s_walk")
+
+
+def write_csvs(csv_dir, scaling, configs):
+    """The benchmark's two tables as CSV, one row per size or workload (the
+    scaling and divergence files of the orrery performance page, "Scaling,
+    and where it stops" and "The divergence mitigation")."""
+    import csv
+    os.makedirs(csv_dir, exist_ok=True)
+    written = []
+    if scaling:
+        path = os.path.join(csv_dir, "scaling.csv")
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(SCALING_COLUMNS)
+            for n, row in sorted(scaling.items(), key=lambda kv: int(kv[0])):
+                w.writerow([int(n)] + [row[c] for c in SCALING_COLUMNS[1:]])
+        written.append(path)
+    if configs:
+        path = os.path.join(csv_dir, "divergence.csv")
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(DIVERGENCE_COLUMNS)
+            for name, row in configs.items():
+                w.writerow([name, row["n"], row["n_nodes"], row["eval_ms_median"], row["eval_ms_iqr"],
+                            row["walk_ms_median"]["coherent"], row["walk_ms_median"]["independent"],
+                            row["coherent_speedup_walk"], row["visits_own_per_particle"],
+                            row["visits_stepped_per_particle"], row["redundancy"], row["interactions"],
+                            row["interactions_per_s_walk"]])
+        written.append(path)
+    return written
 
 
 def percentile(v, q):
@@ -601,6 +641,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pos_np, mass_np, args.cpu_trials)
+    if args.csv_dir:
+        for path in write_csvs(args.csv_dir, scaling, configs):
+            print(f"wrote {path}", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

@@ -65,7 +65,7 @@ def test_abi_host_code_under_asan_and_ubsan(tmp_path):
     # objects with host-side sanitizers; device code is built as in the product
     objs = [build_lib._compile(src, host_san, str(tmp_path)) for src in build_lib.SOURCES]
     link = [clang + "++", "-shared", "-fPIC", *objs, "-o", out, "-fsanitize=address,undefined", "-shared-libasan",
-            "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+            "-L/opt/rocm/lib", "-lamdhip64", *build_lib.LINK_LIBS]
     # the objects' device code needs nothing more: it is embedded as built
     subprocess.run(link, check=True, capture_output=True, text=True)
     rt = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
