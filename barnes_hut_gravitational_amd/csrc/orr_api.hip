@@ -68,7 +68,7 @@ int enum_bits(const E &e) {
 
 size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     const int64_t nb = max_nodes_for(n, leaf_cap);
-    const int64_t n_tiles = ceil_div(n, kTile);
+    const int64_t n_tiles = ceil_div(n, sort_tile_keys(n));
     const int64_t n_scan_tiles = ceil_div(n + 1, 256);
     char *p = static_cast<char *>(base);
     size_t off = 0;

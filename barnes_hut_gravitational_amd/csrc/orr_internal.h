@@ -14,13 +14,13 @@ constexpr int kMaxLevel = 21;            // 21 bits per axis, 63-bit keys
 constexpr uint32_t kQMax = 2097151u;     // 2^21 - 1
 constexpr uint32_t kNoParent = 0xffffffffu;
 
-// Sort tiles: 512 threads x kTileItems keys.
-#ifndef ORR_SORT_ITEMS
-#define ORR_SORT_ITEMS 8
-#endif
+// Sort tiles: 512 threads x 2, 4 or 8 keys. Small inputs take small tiles:
+// a pass over few tiles is bound by each tile's latency, which shrinks with
+// the keys per thread, while large inputs gain from the fewer tiles (and
+// shorter look-back) of large ones.
 constexpr int kTileThreads = 512;
-constexpr int kTileItems = ORR_SORT_ITEMS;
-constexpr int kTile = kTileThreads * kTileItems;
+inline int sort_tile_items(int64_t n) { return n <= 32768 ? 2 : n <= 262144 ? 4 : 8; }
+inline int64_t sort_tile_keys(int64_t n) { return (int64_t)kTileThreads * sort_tile_items(n); }
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kRadixPasses = 8;          // 64 / 8; bit 63 is always zero

@@ -12,8 +12,8 @@
 //   * k_morton_hist computes every key once and the 8 digit histograms of all
 //     keys; k_digit_offsets turns them into the first output slot of each
 //     digit in each pass.
-//   * k_onesweep, one launch per pass: a tile of 4096 keys (512 threads x 8)
-//     takes a ticket (its position in the output), counts its digits and
+//   * k_onesweep, one launch per pass: a tile of 512 threads x 2, 4 or 8 keys
+//     (by the input's size, sort_tile_items) takes a ticket (its position in the output), counts its digits and
 //     publishes the counts at once, ranks its keys stably inside each wave
 //     (lanes with the same digit found with 8 ballots), and then adds the
 //     counts of the tiles before it by decoupled look-back: walking back over
@@ -268,14 +268,15 @@ __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restri
 // w owns elements [kTile t + w kTile/W, + kTile/W), lane l of round r element
 // w kTile/W + 64 r + l, so (w, r, l) order is input order. The tile is reordered by digit in LDS and
 // written out in that order, so consecutive threads store consecutive slots.
-template <bool kGather>
+// kItems keys per thread: kTile = kTileThreads kItems.
+template <int kItems, bool kGather>
 __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__restrict__ keys_in,
                                                   const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
                                                   const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
                                                   DevParams *prm, uint64_t *__restrict__ keys_out,
                                                   uint32_t *__restrict__ vals_out, const float4 *__restrict__ xs0,
                                                   float4 *__restrict__ xs) {
-    constexpr int kWaves = kTileThreads / 64;
+    constexpr int kWaves = kTileThreads / 64, kTile = kTileThreads * kItems;
     static_assert(kWaves * kRadixBins * 4 <= kTile * 8, "counts fit in the key buffer");
     __shared__ uint64_t s_keys[kTile];  // first the per-wave digit counts, then the tile's keys by digit
     __shared__ uint32_t s_vals[kTile];
@@ -296,20 +297,20 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
     const uint32_t tile_n = (uint32_t)min<uint64_t>(kTile, n - t0);
     const uint64_t base = t0 + (uint64_t)w * (kTile / kWaves);
 
-    uint64_t key[kTileItems];
-    uint32_t val[kTileItems], rank[kTileItems];
-    for (int r = 0; r < kTileItems; r++) {
+    uint64_t key[kItems];
+    uint32_t val[kItems], rank[kItems];
+    for (int r = 0; r < kItems; r++) {
         const uint64_t e = base + (uint64_t)r * 64 + lane;
         key[r] = e < n ? keys_in[e] : 0ull;
         val[r] = e < n ? vals_in[e] : 0u;
     }
     // The tile's digit counts first, published at once, so that later tiles
     // can add them while this one ranks its keys.
-    for (int r = 0; r < kTileItems; r++)
+    for (int r = 0; r < kItems; r++)
         if (base + (uint64_t)r * 64 + lane < n) atomicAdd(&s_hist[(uint32_t)(key[r] >> shift) & (kRadixBins - 1)], 1u);
     __syncthreads();
     if (threadIdx.x < kRadixBins) lb_publish(lb_words + threadIdx.x, tile, kRadixBins, s_hist[threadIdx.x]);
-    for (int r = 0; r < kTileItems; r++) {
+    for (int r = 0; r < kItems; r++) {
         const bool valid = base + (uint64_t)r * 64 + lane < n;
         const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
         uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
@@ -351,13 +352,13 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         }
     }
     __syncthreads();
-    uint32_t slot[kTileItems];
-    for (int r = 0; r < kTileItems; r++) {
+    uint32_t slot[kItems];
+    for (int r = 0; r < kItems; r++) {
         const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
         slot[r] = s_cnt[w][d] + rank[r];
     }
     __syncthreads();
-    for (int r = 0; r < kTileItems; r++) {
+    for (int r = 0; r < kItems; r++) {
         if (base + (uint64_t)r * 64 + lane < n) {
             s_keys[slot[r]] = key[r];
             s_vals[slot[r]] = val[r];
@@ -381,7 +382,7 @@ uint32_t morton_hist_blocks(int64_t n) { return (uint32_t)std::min<int64_t>(kSor
 hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Workspace &ws, hipStream_t s,
                                 hipEvent_t after_keys) {
     const uint32_t n = (uint32_t)ws.n;
-    const uint32_t nt = (uint32_t)ws.n_tiles;
+    const uint32_t nt = (uint32_t)ws.n_tiles;  // tiles of sort_tile_keys(n) keys
     const uint32_t hb = morton_hist_blocks(ws.n);
     const int cube_parts = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));  // as launch_cube
     // msum (at least n float4) holds the particles in input order until the
@@ -393,15 +394,22 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
         hipError_t e = hipEventRecord(after_keys, s);
         if (e != hipSuccess) return e;
     }
+    const int items = sort_tile_items(ws.n);
     for (int pass = 0; pass < kRadixPasses; pass++) {
         const int src = pass & 1, dst = src ^ 1;
         uint64_t *words = ws.lb_words + (uint64_t)pass * nt * kRadixBins;
-        if (pass + 1 < kRadixPasses)
-            k_onesweep<false><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
-                                                 ws.keys[dst], ws.vals[dst], nullptr, nullptr);
+        const bool last = pass + 1 == kRadixPasses;
+#define ORR_ONESWEEP(ITEMS, GATHER)                                                                              \
+    k_onesweep<ITEMS, GATHER><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, \
+                                                          ws.prm, ws.keys[dst], ws.vals[dst],                      \
+                                                          GATHER ? ws.msum : nullptr, GATHER ? ws.xs : nullptr)
+        if (items == 2)
+            last ? ORR_ONESWEEP(2, true) : ORR_ONESWEEP(2, false);
+        else if (items == 4)
+            last ? ORR_ONESWEEP(4, true) : ORR_ONESWEEP(4, false);
         else
-            k_onesweep<true><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm,
-                                                ws.keys[dst], ws.vals[dst], ws.msum, ws.xs);
+            last ? ORR_ONESWEEP(8, true) : ORR_ONESWEEP(8, false);
+#undef ORR_ONESWEEP
     }
     return hipGetLastError();
 }

@@ -119,18 +119,22 @@ def test_64bit_node_offsets(kind, n, cap, theta, monkeypatch):
     run_full_case(pos, mass, cap, EPS, theta)
 
 
-@pytest.mark.parametrize("n", [16384, 16385])
+@pytest.mark.parametrize("n", [16384, 16385, 32768, 32769, 262144, 262145])
 def test_sort_tile_edges(n):
-    """The sort's 4,096-key tiles: 16,384 keys fill four tiles, 16,385 leave a
-    last tile of one key. The oracle's tree and walk for Plummer, for heavy
-    duplicates on a lattice (long runs of equal keys across tiles, so
-    stability decides the order), for a single point, and for a signed-zero
+    """The sort's tiles hold 1,024 keys up to 32,768 particles, 2,048 up to
+    262,144 and 4,096 above: each size here fills its tiles exactly or leaves a
+    last tile of one key, and the three limits switch tile sizes. The
+    oracle's tree and walk for Plummer and for heavy duplicates on a lattice
+    (long runs of equal keys across tiles, so stability decides the order);
+    up to 32,769 particles also for a single point and for a signed-zero
     minimum (the corner must be +0)."""
     pos, mass = inputs.make("plummer", n)
     run_full_case(pos, mass, 32, EPS, 0.5)
     rng = np.random.default_rng(5)
     lat = rng.integers(0, 4, (n, 3)).astype(np.float32)
     run_full_case(lat, np.full(n, 1 / n, np.float32), 8, EPS, 0.5)
+    if n > 32769:
+        return
     run_full_case(np.full((n, 3), -1.5, np.float32), np.full(n, 1 / n, np.float32), 32, EPS, 0.5)
     z = rng.uniform(0, 1, (n, 3)).astype(np.float32)
     z[::3, 1] = np.float32(-0.0)
