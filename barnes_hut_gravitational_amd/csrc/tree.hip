@@ -533,7 +533,11 @@ hipError_t launch_build(const Workspace &ws, hipStream_t s) {
 }
 
 hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
-    const unsigned blocks = (unsigned)std::min<int64_t>(1024, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 2));
+    // Far more work-groups than the cut subtrees a tree of n particles usually
+    // has (the host does not know their number): each reduces its subtrees
+    // level by level with a barrier per level, so subtrees that share a
+    // work-group add up, and a work-group past the list exits at once.
+    const unsigned blocks = (unsigned)std::min<int64_t>(4096, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 64));
     k_moments_cut<<<blocks, 256, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.cut_list, ws.prm, (uint32_t)ws.max_nodes,
                                          ws.msum);
     k_moments_top<<<9, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum,
