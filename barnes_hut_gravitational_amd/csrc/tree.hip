@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__
                                                     uint32_t *__restrict__ tile_sum,
                                                     uint32_t *__restrict__ wave_cost) {
     __shared__ uint64_t sk[256 + 2 * 256];
-    __shared__ signed char sw[256 + 256];
+    __shared__ signed char sw[2][256 + 256];
     __shared__ uint32_t s_wsum[4];
     const int64_t B = (int64_t)blockIdx.x * 256;
     const int64_t wbeg = B - (int64_t)cap;
@@ -78,14 +78,28 @@ __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__
         const int64_t s = wbeg + t;
         signed char v = -1;
         if (s >= 0 && s + (int64_t)cap < (int64_t)n) v = (signed char)lcp_digits(sk[t], sk[t + cap]);
-        sw[t] = v;
+        sw[0][t] = v;
     }
     __syncthreads();
+    // A particle's leaf depth needs the largest of cap + 1 consecutive window
+    // values; maxima over 2^k of them come by doubling (level k: sw[k & 1][t]
+    // = max of level-0 values [t, t + 2^k)), and the window is two
+    // overlapping ones of the largest width that fits. Fewer LDS reads than
+    // a scan of cap + 1 values per particle.
+    const int W = (int)cap + 1;
+    const int kmax = 31 - __clz(W);
+    for (int k = 1; k <= kmax; k++) {
+        const int half = 1 << (k - 1), cnt = 256 + (int)cap - (1 << k) + 1;
+        const signed char *src = sw[(k - 1) & 1];
+        signed char *dst = sw[k & 1];
+        for (int t = threadIdx.x; t < cnt; t += 256) dst[t] = max(src[t], src[t + half]);
+        __syncthreads();
+    }
     const int64_t i = B + threadIdx.x;
     uint32_t nst = 0, depth = 0;
     if (i < (int64_t)n) {
-        int m = -1;
-        for (int t = threadIdx.x; t <= threadIdx.x + (int)cap; t++) m = max(m, (int)sw[t]);
+        const signed char *mk = sw[kmax & 1];
+        const int m = max((int)mk[threadIdx.x], (int)mk[threadIdx.x + W - (1 << kmax)]);
         const int D = min(m + 1, kMaxLevel);
         const int first = (i == 0) ? 0 : lcp_digits(sk[threadIdx.x + cap - 1], sk[threadIdx.x + cap]) + 1;
         info[i] = (uint32_t)first | ((uint32_t)D << 8);
