@@ -138,31 +138,47 @@ __global__ __launch_bounds__(256) void k_tree_count(const uint64_t *__restrict__
 }
 
 // One block: exclusive scan of the tile sums in place; the total is n_nodes.
+// Wave w takes a contiguous chunk of the tiles (a multiple of 64 of them):
+// its sum, read 64 consecutive sums at a time; the 16 wave sums give each
+// chunk's offset; then each wave scans its chunk 64 sums at a time (256
+// loaded together), carrying the running total. One block barrier in all.
 __global__ __launch_bounds__(1024) void k_tile_scan(uint32_t *__restrict__ tile_sum, uint32_t n_tiles,
                                                     DevParams *__restrict__ prm) {
     __shared__ uint32_t s_wsum[16];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t carry = 0;
-    for (uint32_t c0 = 0; c0 < n_tiles; c0 += 1024) {
-        const uint32_t k = c0 + threadIdx.x;
-        const uint32_t v = k < n_tiles ? tile_sum[k] : 0u;
-        uint32_t inc = v;
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t t = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += t;
-        }
-        if (lane == 63) s_wsum[w] = inc;
-        __syncthreads();
-        uint32_t woff = 0, tot = 0;
-        for (int q = 0; q < 16; q++) {
-            if (q < w) woff += s_wsum[q];
-            tot += s_wsum[q];
-        }
-        if (k < n_tiles) tile_sum[k] = carry + woff + inc - v;
-        carry += tot;
-        __syncthreads();
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint32_t chunk = ((n_tiles + 15u) / 16u + 63u) / 64u * 64u;
+    const uint32_t b = min(w * chunk, n_tiles), e = min(b + chunk, n_tiles);
+    uint32_t part = 0;
+#pragma unroll 4
+    for (uint32_t k = b + lane; k < e; k += 64u) part += tile_sum[k];
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == 0u) s_wsum[w] = part;
+    __syncthreads();
+    uint32_t carry = 0, tot = 0;
+    for (uint32_t q = 0; q < 16u; q++) {
+        if (q < w) carry += s_wsum[q];
+        tot += s_wsum[q];
     }
-    if (threadIdx.x == 0) prm->n_nodes = carry;
+    for (uint32_t k0 = b; k0 < e; k0 += 4u * 64u) {  // four groups of 64 sums loaded together
+        uint32_t v[4];
+#pragma unroll
+        for (uint32_t g = 0; g < 4u; g++) {
+            const uint32_t k = k0 + 64u * g + lane;
+            v[g] = k < e ? tile_sum[k] : 0u;
+        }
+#pragma unroll
+        for (uint32_t g = 0; g < 4u; g++) {
+            const uint32_t k = k0 + 64u * g + lane;
+            uint32_t inc = v[g];
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = __shfl_up(inc, o, 64);
+                if (lane >= (uint32_t)o) inc += t;
+            }
+            if (k < e) tile_sum[k] = carry + inc - v[g];
+            carry += __shfl(inc, 63, 64);
+        }
+    }
+    if (threadIdx.x == 0) prm->n_nodes = tot;
 }
 
 // First j > start whose key differs from pre in its top bits (key >> sh), or
