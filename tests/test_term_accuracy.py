@@ -10,8 +10,8 @@ order (tests/term_variants.c) with
   sums unfused;
 - that with fused multiply-adds in r2 and in a += f d.
 
-Both cheaper variants leave the 1e-5 bar on maximum relative per-particle
-error (the benchmark spec's accuracy bar; the variants reach 1.22e-5 and
+Both cheaper variants leave the accuracy bar of 1e-5 on the maximum
+relative per-particle error of the accelerations (they reach 1.22e-5 and
 1.29e-5 at one target near the centre, where |a| is about 2 % of the
 median), while the exact sequence meets it with zero error. CPU only."""
 
