@@ -178,6 +178,24 @@ def test_configs_large_every_target(name):
     print(f"[{name}] timings {r.timings}", flush=True)
 
 
+@pytest.mark.parametrize("kind,n", [("plummer", 1000003), ("uniform", 300007), ("merger", 2000001)])
+def test_ragged_large_every_target(kind, n):
+    """Sizes that are not powers of two at full scale: a last sort tile, a
+    last target wave and a last schedule region that are partly empty. The
+    tree bit for bit, and every target's acceleration, counts and wave union
+    against the oracle's whole evaluation."""
+    pos, mass = inputs.make(kind, n)
+    print(f"[case] ragged {kind} n={n}", flush=True)
+    ref = oracle.evaluate(pos, mass, EPS, THETA, inputs.LEAF_CAP)
+    P, M = to_dev(pos, mass)
+    r = orr.orr_eval_forces(P, M, eps=EPS, theta=THETA, leaf_cap=inputs.LEAF_CAP, traversal="coherent",
+                            timings=True)
+    check_walk(r, ref, "coherent")
+    check_acc_bitwise(r, ref.acc)
+    tree = orr.Tree(P, M, inputs.LEAF_CAP)
+    check_tree(tree, ref.tree)
+
+
 @pytest.mark.parametrize("n", [1000, 20000])
 def test_nonfinite_input_reported(n):
     """Non-finite positions and masses and negative masses are flagged, with
