@@ -84,7 +84,7 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws) {
     for (int k = 0; k < 2; k++) w.vals[k] = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
     w.hist_part = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kSortHistBlocks * kRadixPasses * kRadixBins));
     w.digit_offs = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * kRadixPasses * kRadixBins));
-    w.n_lb_words = (int64_t)kRadixPasses * n_tiles * kRadixBins;
+    w.n_lb_words = (int64_t)kFullPasses * n_tiles * kRadixBins;
     w.lb_words = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * w.n_lb_words));
     w.xs = reinterpret_cast<float4 *>(take(sizeof(float4) * n));
     w.info = reinterpret_cast<uint32_t *>(take(sizeof(uint32_t) * n));
@@ -502,7 +502,7 @@ orr_status orr_eval_forces(const float *pos, const float *mass, int64_t n, float
     if ((st = read_params(&t, &prm)) != ORR_OK) return st;
     timings->cube_keys_ms = tm.ms(0, 1);
     timings->sort_ms = tm.ms(1, 2);
-    timings->gather_ms = 0.0f;  // fused into the last sort pass
+    timings->gather_ms = 0.0f;  // done by the sort's run fix-up, inside sort_ms
     timings->build_ms = tm.ms(2, 3);
     timings->moments_ms = tm.ms(3, 4);
     timings->walk_ms = tm.ms(4, 5);

@@ -23,7 +23,17 @@ inline int sort_tile_items(int64_t n) { return n <= 32768 ? 2 : n <= 262144 ? 4 
 inline int64_t sort_tile_keys(int64_t n) { return (int64_t)kTileThreads * sort_tile_items(n); }
 constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kRadixPasses = 8;          // 64 / 8; bit 63 is always zero
+// The main sort orders the keys by their high 32 bits (bits 31..62) in 4
+// passes; runs of equal high bits are then ordered by the low 31 bits in
+// place (k_sort_fix). A run longer than kFixMaxRun sends the whole array
+// through the fallback: the 8 passes of the full key.
+constexpr int kRadixPasses = 4;
+constexpr int kSortLowBits = 31;
+constexpr int kFullPasses = 8;           // 64 / 8; bit 63 is always zero
+constexpr int kFixThreads = 512;         // positions per block of the run fix-up
+constexpr int kFixHalo = 64;             // window margin: runs up to 64 are finished per thread
+constexpr int kFixMaxRun = 4096;         // longest run finished by one work-group
+constexpr int kFallbackBlocks = 512;     // persistent blocks of the fallback sort
 
 constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube reduction
 
@@ -37,7 +47,7 @@ struct DevParams {
     float side;
     float scale;          // 2^21 / side
     uint32_t bad_input;   // bit 0: non-finite position/mass, negative mass or overflowing extent;
-                          // bit 1: a look-back wait gave up (never expected)
+                          // bit 1: a look-back or phase wait of the sort gave up (never expected)
     uint32_t n_nodes;
     uint32_t n_leaves;    // filled by the info kernels only
     uint32_t depth;
@@ -45,7 +55,10 @@ struct DevParams {
     uint32_t sort_ticket[kRadixPasses];  // tile tickets of the one-sweep passes
     uint32_t n_cut;                      // entries of the cut-node list
     uint32_t n_top;                      // entries of the above-the-cut list
-    uint32_t pad[12];
+    uint32_t sort_fallback;              // set by k_sort_fix: a run is too long, re-sort by the full key
+    uint32_t fb_ticket;                  // work tickets of the fallback sort
+    uint32_t fb_done[1 + kFullPasses];   // finished tiles of the fallback's histogram phase and passes
+    uint32_t pad[5];
 };
 static_assert(sizeof(DevParams) == 128, "DevParams layout");
 
@@ -61,11 +74,13 @@ static_assert(sizeof(NodeRec) == 32, "NodeRec layout");
 struct Workspace {
     DevParams *prm;
     float *cube_part;      // [kCubeBlocks][8]
-    uint64_t *keys[2];     // [n] radix ping-pong; sorted keys end in keys[0]
+    uint64_t *keys[2];     // [n] radix ping-pong: the passes start and end in keys[1], the
+                           // run fix-up writes the sorted keys to keys[0]
     uint32_t *vals[2];     // [n] payload: original index; perm ends in vals[0]
-    uint32_t *hist_part;   // [kSortHistBlocks][kRadixPasses][kRadixBins] digit counts per block
+    uint32_t *hist_part;   // [kSortHistBlocks][kRadixPasses][kRadixBins] digit counts per block;
+                           // after the digit offsets, [kFullPasses][kRadixBins] counts of the fallback
     uint32_t *digit_offs;  // [kRadixPasses][kRadixBins] first output slot of each digit
-    uint64_t *lb_words;    // look-back words of the sort's passes
+    uint64_t *lb_words;    // look-back words of the sort's passes (room for the fallback's 8)
     int64_t n_lb_words;
     float4 *xs;            // [n] sorted (x, y, z, m)
     uint32_t *info;        // [n] first level started | leaf depth << 8
@@ -102,8 +117,10 @@ size_t carve_workspace(void *base, int64_t n, int32_t leaf_cap, Workspace *ws);
 
 // ---- launch wrappers (each returns hipGetLastError() of its launches) ----
 hipError_t launch_cube(const float *pos, const float *mass, const Workspace &ws, hipStream_t s);
-// Keys, digit histograms, the 8 sort passes and the gather; after_keys (may be
-// null) is recorded between the key pass and the first sort pass.
+// Keys, digit histograms, the 4 high-bit passes, the run fix-up with the
+// gather, and the fallback (which returns at once unless the fix-up asked for
+// it); after_keys (may be null) is recorded between the key pass and the
+// first sort pass.
 hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Workspace &ws, hipStream_t s,
                                 hipEvent_t after_keys);
 hipError_t launch_build(const Workspace &ws, hipStream_t s);

@@ -1,30 +1,46 @@
-// Morton keys with their digit histograms, and the stable one-sweep LSD radix
-// sort of (key, index) with the gather into tree order fused into its last
-// pass.
+// Morton keys with their digit histograms, and the stable sort of
+// (key, index) into tree order with the gather of the particles.
 //
 // The orrery performance page ("Where one evaluation goes", "The largest
 // row") measures the host Morton sort as the largest single cost of an
 // evaluation and names a device radix sort as the first thing to do; here it
-// runs on the GPU. Equal keys keep ascending original index because every
-// pass is stable and the payload starts as the identity.
+// runs on the GPU. The result is the stable sort by key: equal keys keep
+// ascending original index.
 //
-// Pass structure (8 passes of 8-bit digits, bit 63 is always zero):
-//   * k_morton_hist computes every key once and the 8 digit histograms of all
-//     keys; k_digit_offsets turns them into the first output slot of each
-//     digit in each pass.
+// Structure. A 63-bit key splits into its high 32 bits H (bits 31..62) and
+// its low 31 bits. Sorting by H alone takes 4 one-sweep LSD passes of 8-bit
+// digits instead of 8; what remains is to order each run of equal H by the
+// low bits, and in Morton order such runs are short: a run is a cell 2^-10
+// of the root side or smaller, and on the Plummer, uniform and merger inputs
+// runs average 1.0 to 1.5 keys and never exceed 30.
+//   * k_morton_hist computes every key once and the 4 digit histograms of H;
+//     k_digit_offsets turns them into the first output slot of each digit.
 //   * k_onesweep, one launch per pass: a tile of 512 threads x 2, 4 or 8 keys
-//     (by the input's size, sort_tile_items) takes a ticket (its position in the output), counts its digits and
-//     publishes the counts at once, ranks its keys stably inside each wave
-//     (lanes with the same digit found with 8 ballots), and then adds the
-//     counts of the tiles before it by decoupled look-back: walking back over
-//     predecessors' published words, four per step, until one carries an
-//     inclusive prefix. Publishing before the ranking lets the successors'
-//     walks find the counts sooner. Tickets are taken in the order
-//     blocks start, so every predecessor is running or done and publishes its
-//     counts without waiting on anyone; each wait is nevertheless bounded and
-//     reports an error. The tile is then reordered by digit in LDS and
-//     written out in that order: each digit's run of the tile lands in one
-//     contiguous stretch of the output, stored by consecutive threads.
+//     (by the input's size, sort_tile_items) takes a ticket (its position in
+//     the output), counts its digits and publishes the counts at once, ranks
+//     its keys stably inside each wave (lanes with the same digit found with
+//     8 ballots), and then adds the counts of the tiles before it by
+//     decoupled look-back: walking back over predecessors' published words,
+//     four per step, until one carries an inclusive prefix. Tickets are taken
+//     in the order blocks start, so every predecessor is running or done and
+//     publishes its counts without waiting on anyone; each wait is
+//     nevertheless bounded and reports an error. The tile is then reordered
+//     by digit in LDS and written out in that order.
+//   * k_sort_fix finishes the runs and gathers the particles: each thread
+//     takes one position, finds its run from a window of keys in LDS (64
+//     positions either side) and, for a run of at most 64, places its own
+//     element at the run's start plus its stable rank by the low bits. A run
+//     of 65 to 4,096 is sorted by the work-group holding its first position
+//     (a bitonic sort in LDS of (low bits, position), unique values). A
+//     longer run - more than 4,096 particles in one cell of the H grid - sets
+//     a flag.
+//   * k_sort_fallback, always launched, returns at once unless that flag is
+//     set; then its persistent blocks redo the sort by the full key: 8 passes
+//     of the same tiles over the H-sorted keys, driven by one ticket counter
+//     (a histogram phase, then the passes in order), each phase waiting for
+//     the one before it with a bounded wait. Since equal keys have equal H,
+//     they are in index order in the H-sorted array, and a stable sort of it
+//     by the full key is the sort by (key, index).
 #include "orr_internal.h"
 
 namespace orr {
@@ -153,13 +169,13 @@ __device__ __forceinline__ void cube_from_partials(const float *__restrict__ par
     if (side == 0.0f) side = 1.0f;
 }
 
-// Keys and the identity payload; each block's 8 digit histograms to
-// part[block][pass][digit]; zeroes the look-back words of the build; copies
-// every particle as one float4 (x, y, z, m) in input order to xs0, which the
-// last pass gathers from (one aligned load per particle instead of a 12-byte
-// and a 4-byte one). Each
-// block first forms the root cube from the partials; block 0 also stores it
-// in prm with the input flag and resets the build's device counters.
+// Keys and the identity payload; each block's 4 digit histograms of the high
+// bits to part[block][pass][digit]; zeroes the look-back words of the 4
+// passes; copies every particle as one float4 (x, y, z, m) in input order to
+// xs0, which the gather reads from (one aligned load per particle instead of
+// a 12-byte and a 4-byte one). Each block first forms the root cube from the
+// partials; block 0 also stores it in prm with the input flag and resets the
+// build's device counters.
 __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ pos, const float *__restrict__ mass,
                                                      float4 *__restrict__ xs0, uint32_t n,
                                                      const float *__restrict__ cube_part, int cube_parts,
@@ -188,6 +204,9 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
                 for (int q = 0; q < kRadixPasses; q++) prm->sort_ticket[q] = 0;
                 prm->n_cut = 0;
                 prm->n_top = 0;
+                prm->sort_fallback = 0;
+                prm->fb_ticket = 0;
+                for (int q = 0; q <= kFullPasses; q++) prm->fb_done[q] = 0;
             }
         }
     }
@@ -200,8 +219,9 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
         keys[i] = key;
         idx[i] = i;
         xs0[i] = make_float4(x, y, z, m);
+        const uint32_t hi = (uint32_t)(key >> kSortLowBits);
         for (int p = 0; p < kRadixPasses; p++)
-            atomicAdd(&h[p * kRadixBins + ((uint32_t)(key >> (p * kRadixBits)) & (kRadixBins - 1))], 1u);
+            atomicAdd(&h[p * kRadixBins + ((hi >> (p * kRadixBits)) & (kRadixBins - 1))], 1u);
     };
     uint32_t i = blockIdx.x * 256u + threadIdx.x;
     for (; i + 3u * stride < n; i += 4u * stride) {  // four particles' loads in flight
@@ -264,18 +284,21 @@ __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restri
     }
 }
 
-// One pass over a tile of kTile keys. With W = kTileThreads / 64 waves, wave
-// w owns elements [kTile t + w kTile/W, + kTile/W), lane l of round r element
-// w kTile/W + 64 r + l, so (w, r, l) order is input order. The tile is reordered by digit in LDS and
-// written out in that order, so consecutive threads store consecutive slots.
-// kItems keys per thread: kTile = kTileThreads kItems.
-template <int kItems, bool kGather>
-__global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__restrict__ keys_in,
-                                                  const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
-                                                  const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
-                                                  DevParams *prm, uint64_t *__restrict__ keys_out,
-                                                  uint32_t *__restrict__ vals_out, const float4 *__restrict__ xs0,
-                                                  float4 *__restrict__ xs) {
+// One stable pass over one tile of kTile = kTileThreads kItems keys, by digit
+// (key >> shift) & 255. The tile is `tile`, or, with a ticket counter, the
+// next ticket. digit_base[d]: the first output slot of digit d over all
+// tiles; words: this pass's look-back words, [tile][digit]. With W =
+// kTileThreads / 64 waves, wave w owns elements [kTile t + w kTile/W, +
+// kTile/W), lane l of round r element w kTile/W + 64 r + l, so (w, r, l)
+// order is input order. The tile is reordered by digit in LDS and written
+// out in that order, so consecutive threads store consecutive slots; with
+// xs given, each output slot o also receives xs[o] = xs0[value].
+template <int kItems>
+__device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
+                                           uint32_t n, int shift, const uint32_t *digit_base, uint64_t *words,
+                                           uint32_t *ticket, uint32_t tile_arg, uint32_t *err,
+                                           uint64_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
+                                           const float4 *__restrict__ xs0, float4 *__restrict__ xs) {
     constexpr int kWaves = kTileThreads / 64, kTile = kTileThreads * kItems;
     static_assert(kWaves * kRadixBins * 4 <= kTile * 8, "counts fit in the key buffer");
     __shared__ uint64_t s_keys[kTile];  // first the per-wave digit counts, then the tile's keys by digit
@@ -287,12 +310,11 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
     uint32_t(*s_cnt)[kRadixBins] = reinterpret_cast<uint32_t(*)[kRadixBins]>(s_keys);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int shift = pass * kRadixBits;
     for (int k = threadIdx.x; k < kWaves * kRadixBins; k += kTileThreads) (&s_cnt[0][0])[k] = 0;
     if (threadIdx.x < kRadixBins) s_hist[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s_tile = atomicAdd(&prm->sort_ticket[pass], 1u);
+    if (threadIdx.x == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : tile_arg;
     __syncthreads();
-    const uint32_t tile = s_tile;
+    const uint32_t tile = __builtin_amdgcn_readfirstlane(s_tile);
     const uint64_t t0 = (uint64_t)tile * kTile;
     const uint32_t tile_n = (uint32_t)min<uint64_t>(kTile, n - t0);
     const uint64_t base = t0 + (uint64_t)w * (kTile / kWaves);
@@ -309,7 +331,7 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
     for (int r = 0; r < kItems; r++)
         if (base + (uint64_t)r * 64 + lane < n) atomicAdd(&s_hist[(uint32_t)(key[r] >> shift) & (kRadixBins - 1)], 1u);
     __syncthreads();
-    if (threadIdx.x < kRadixBins) lb_publish(lb_words + threadIdx.x, tile, kRadixBins, s_hist[threadIdx.x]);
+    if (threadIdx.x < kRadixBins) lb_publish(words + threadIdx.x, tile, kRadixBins, s_hist[threadIdx.x]);
     for (int r = 0; r < kItems; r++) {
         const bool valid = base + (uint64_t)r * 64 + lane < n;
         const uint32_t d = (uint32_t)(key[r] >> shift) & (kRadixBins - 1);
@@ -342,8 +364,8 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         const int d = threadIdx.x;
         uint32_t local = inc - tot;
         for (int k = 0; k < w; k++) local += s_wsum[k];
-        const uint32_t excl = lb_resolve(lb_words + d, tile, kRadixBins, tot, &prm->bad_input);
-        s_delta[d] = digit_offs[pass * kRadixBins + d] + excl - local;
+        const uint32_t excl = lb_resolve(words + d, tile, kRadixBins, tot, err);
+        s_delta[d] = digit_base[d] + excl - local;
         uint32_t run = local;
         for (int k = 0; k < kWaves; k++) {  // in place: column d is this thread's alone
             const uint32_t c = s_cnt[k][d];
@@ -369,9 +391,267 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
         const uint64_t k = s_keys[j];
         const uint32_t v = s_vals[j];
         const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
-        keys_out[o] = k;
-        vals_out[o] = v;
-        if (kGather) xs[o] = xs0[v];
+        if (o < n) {  // always, unless a look-back wait gave up (flagged): then never a stray store
+            keys_out[o] = k;
+            vals_out[o] = v;
+            if (xs && v < n) xs[o] = xs0[v];
+        }
+    }
+}
+
+// One pass of the high-bit sort: digit `pass` of H, one tile per block.
+template <int kItems>
+__global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__restrict__ keys_in,
+                                                           const uint32_t *__restrict__ vals_in, uint32_t n, int pass,
+                                                           const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
+                                                           DevParams *prm, uint64_t *__restrict__ keys_out,
+                                                           uint32_t *__restrict__ vals_out) {
+    sweep_tile<kItems>(keys_in, vals_in, n, kSortLowBits + pass * kRadixBits, digit_offs + pass * kRadixBins,
+                              lb_words, &prm->sort_ticket[pass], 0u, &prm->bad_input, keys_out, vals_out, nullptr,
+                              nullptr);
+}
+
+// Finishes the runs of equal high bits and gathers the particles. Input: the
+// H-sorted keys and values; output: the sorted keys, values and particles.
+// Block b owns positions [b B, b B + B), B = kFixThreads, and holds the keys
+// of [b B - 64, b B + B + 64) in LDS with one bit per position that starts a
+// run (a position whose H differs from its predecessor's; also the window's
+// first slot and every position outside [1, n)). A thread at window slot q
+// looks for its run's start in q's bit word and the one before (at least the
+// 64 slots up to q) and for the next run's start in q's word and the one
+// after (at least 64 slots past q). Finding both, its run [s, e) is exact;
+// missing either, the run is longer than 64. Runs of 65 to kFixMaxRun keys are sorted by the block
+// holding their first position; longer ones set prm->sort_fallback and are
+// left to the fallback. Block 0 also clears the fallback's digit counts.
+__global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__restrict__ keys_in,
+                                                          const uint32_t *__restrict__ vals_in, uint32_t n,
+                                                          const float4 *__restrict__ xs0,
+                                                          uint64_t *__restrict__ keys_out,
+                                                          uint32_t *__restrict__ vals_out, float4 *__restrict__ xs,
+                                                          DevParams *__restrict__ prm, uint32_t *__restrict__ fb_hist) {
+    constexpr int kWin = kFixThreads + 2 * kFixHalo;
+    constexpr int kWords = kWin / 64;
+    constexpr int kMaxLong = kFixThreads / (kFixHalo + 1) + 1;  // long runs starting in one block
+    static_assert(kWin % 64 == 0 && kWin <= kFixMaxRun, "window layout");
+    __shared__ uint64_t s_buf[kFixMaxRun];  // the window's keys, then one long run's (low bits, position)
+    __shared__ uint64_t s_head[kWords];
+    __shared__ uint32_t s_long[kMaxLong];
+    __shared__ uint32_t s_nlong, s_end;
+    const int t = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kFixThreads;
+    const int64_t p = t0 + t;
+    const bool mine = p < n;
+    const uint32_t v = mine ? vals_in[p] : 0u;  // issued early: the gather waits on it
+    if (t == 0) s_nlong = 0;
+    if (blockIdx.x == 0)
+        for (int k = t; k < kFullPasses * kRadixBins; k += kFixThreads) fb_hist[k] = 0;
+    for (int q = t; q < kWin; q += kFixThreads) {
+        const int64_t g = t0 - kFixHalo + q;
+        s_buf[q] = g >= 0 && g < n ? keys_in[g] : 0ull;
+    }
+    __syncthreads();
+    for (int q = t; q < kWin; q += kFixThreads) {  // whole waves: kWin - kFixThreads is a multiple of 64
+        const int64_t g = t0 - kFixHalo + q;
+        const bool head =
+            q == 0 || g <= 0 || g >= n || (s_buf[q] >> kSortLowBits) != (s_buf[q - 1] >> kSortLowBits);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(head);
+        if ((q & 63) == 0) s_head[q >> 6] = m;
+    }
+    __syncthreads();
+    if (mine) {
+        const int q = kFixHalo + t, k = q >> 6;
+        const uint64_t le = (2ull << (q & 63)) - 1;  // bits 0 .. q & 63
+        // Run start: the last start at or before q, in this word or the one before.
+        int s = -1;
+        if (const uint64_t m = s_head[k] & le) s = 64 * k + 63 - __clzll(m);
+        else if (const uint64_t m = s_head[k - 1]) s = 64 * (k - 1) + 63 - __clzll(m);
+        // Run end: the first start after q, in this word or the next.
+        int e = -1;
+        if (const uint64_t m = s_head[k] & ~le) e = 64 * k + __ffsll((long long)m) - 1;
+        else if (const uint64_t m = s_head[k + 1]) e = 64 * (k + 1) + __ffsll((long long)m) - 1;
+        if (s >= 0 && e >= 0 && e - s <= kFixHalo) {
+            const uint64_t key = s_buf[q];
+            uint32_t rank = 0;
+            for (int i = s; i < e; i++) {
+                const uint64_t o = s_buf[i];
+                rank += (o < key) | ((o == key) & (i < q));
+            }
+            const int64_t out = t0 - kFixHalo + s + rank;
+            keys_out[out] = key;
+            vals_out[out] = v;
+            xs[out] = xs0[v];
+        } else if (s == q) {
+            s_long[atomicAdd(&s_nlong, 1u)] = (uint32_t)p;
+        }
+    }
+    __syncthreads();
+    // Loop bounds around barriers are read from LDS with readfirstlane: the
+    // same for every thread, and known to the compiler to be uniform, so the
+    // loops stay uniform control flow.
+    const uint32_t nlong = __builtin_amdgcn_readfirstlane(s_nlong);
+    for (uint32_t r = 0; r < nlong; r++) {
+        const uint32_t S = __builtin_amdgcn_readfirstlane(s_long[r]);
+        const uint64_t hs = keys_in[S] >> kSortLowBits;
+        if (t == 0) s_end = ~0u;
+        __syncthreads();
+        // The run's end: the first position in (S, S + kFixMaxRun] past the
+        // array or with other high bits.
+        uint32_t end = ~0u;
+        for (uint32_t c = S + 1; end == ~0u && c <= S + kFixMaxRun; c += kFixThreads) {
+            const uint32_t j = c + t;
+            if (j <= S + kFixMaxRun && (j >= n || (keys_in[j] >> kSortLowBits) != hs)) atomicMin(&s_end, j);
+            __syncthreads();
+            end = __builtin_amdgcn_readfirstlane(s_end);
+            __syncthreads();
+        }
+        if (end == ~0u) {  // longer than kFixMaxRun
+            if (t == 0) atomicOr(&prm->sort_fallback, 1u);
+            continue;
+        }
+        const uint32_t len = end - S;
+        uint32_t np = 128;
+        while (np < len) np <<= 1;
+        for (uint32_t i = t; i < np; i += kFixThreads)
+            s_buf[i] = i < len ? ((keys_in[S + i] & 0x7fffffffull) << 12) | i : ~0ull;
+        __syncthreads();
+        for (uint32_t k = 2; k <= np; k <<= 1) {
+            for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+                for (uint32_t i = t; i < np; i += kFixThreads) {
+                    const uint32_t l = i ^ j;
+                    if (l > i) {
+                        const uint64_t a = s_buf[i], b = s_buf[l];
+                        if ((a > b) == ((i & k) == 0)) {
+                            s_buf[i] = b;
+                            s_buf[l] = a;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (uint32_t i = t; i < len; i += kFixThreads) {
+            const uint32_t src = S + (uint32_t)(s_buf[i] & 0xfffu);
+            const uint32_t w = vals_in[src];
+            keys_out[S + i] = keys_in[src];
+            vals_out[S + i] = w;
+            xs[S + i] = xs0[w];
+        }
+        __syncthreads();  // s_buf and s_end are reused by the next run
+    }
+}
+
+// Bounded wait for a phase counter of the fallback to reach `target`.
+__device__ __forceinline__ void wait_count(const uint32_t *c, uint32_t target, uint32_t *err) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++spins > kSpinLimit) {
+            atomicOr(err, 2u);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// The fallback: the stable sort of the H-sorted keys by the full key, run
+// only when k_sort_fix set prm->sort_fallback. Work is handed out by one
+// ticket counter: tickets [0, nt) are the histogram phase (the 8 digit counts
+// of each tile, and the tile's look-back words cleared), then nt tickets per
+// pass for the 8 passes in order. A block takes the next ticket only after
+// finishing its current one, so the holders of all earlier tickets are
+// running or done; a tile of phase f waits until all nt tiles of phase f - 1
+// are done (release after a tile, acquire before one). Passes alternate
+// between the H-sorted array (a) and scratch (s); the last writes the output
+// and gathers the particles.
+template <int kItems>
+__global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a, uint32_t *vals_a, uint64_t *keys_s,
+                                                                uint32_t *vals_s, uint64_t *keys_out,
+                                                                uint32_t *vals_out, uint32_t n, uint32_t nt,
+                                                                uint32_t *fb_hist, uint64_t *lb_words, DevParams *prm,
+                                                                const float4 *__restrict__ xs0, float4 *xs) {
+    constexpr int kTile = kTileThreads * kItems;
+    if (prm->sort_fallback == 0) return;
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_base[kRadixBins];
+    __shared__ uint32_t s_wsum[kRadixBins / 64];
+    __shared__ uint32_t s_h[kFullPasses * kRadixBins];
+    const uint32_t total = (1u + kFullPasses) * nt;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // Thread 0 takes the tickets; the loop is entered and left on the same
+    // uniform value (readfirstlane after a barrier), and thread 0's work at
+    // the end of an iteration is followed by a barrier, so every barrier in
+    // the loop stays in uniform control flow.
+    if (threadIdx.x == 0) s_ticket = atomicAdd(&prm->fb_ticket, 1u);
+    __syncthreads();
+    uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    while (ticket < total) {
+        const uint32_t phase = ticket / nt, tile = ticket % nt;
+        if (phase > 0) {
+            // Acquire by thread 0, passed on to the work-group by the barrier
+            // (its waves share one CU and its L1).
+            if (threadIdx.x == 0) {
+                wait_count(&prm->fb_done[phase - 1], nt, &prm->bad_input);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+        }
+        if (phase == 0) {
+            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) s_h[k] = 0;
+            __syncthreads();
+            const uint64_t t0 = (uint64_t)tile * kTile;
+            for (uint64_t e = t0 + threadIdx.x; e < n && e < t0 + kTile; e += kTileThreads) {
+                const uint64_t key = keys_a[e];
+                for (int q = 0; q < kFullPasses; q++)
+                    atomicAdd(&s_h[q * kRadixBins + ((uint32_t)(key >> (q * kRadixBits)) & (kRadixBins - 1))], 1u);
+            }
+            __syncthreads();
+            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads)
+                if (s_h[k]) atomicAdd(&fb_hist[k], s_h[k]);
+            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) {
+                const int q = k / kRadixBins, d = k % kRadixBins;
+                lb_store(lb_words + ((uint64_t)q * nt + tile) * kRadixBins + d, 0ull);
+            }
+        } else {
+            const int pass = (int)phase - 1;
+            // First output slot of each digit: the exclusive scan of the counts.
+            uint32_t c = 0, inc = 0;
+            if (threadIdx.x < kRadixBins) {
+                c = __hip_atomic_load(&fb_hist[pass * kRadixBins + threadIdx.x], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                inc = c;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t u = __shfl_up(inc, o, 64);
+                    if (lane >= o) inc += u;
+                }
+                if (lane == 63) s_wsum[w] = inc;
+            }
+            __syncthreads();
+            if (threadIdx.x < kRadixBins) {
+                uint32_t off = inc - c;
+                for (int k = 0; k < w; k++) off += s_wsum[k];
+                s_base[threadIdx.x] = off;
+            }
+            __syncthreads();
+            uint64_t *words = lb_words + (uint64_t)pass * nt * kRadixBins;
+            const int shift = pass * kRadixBits;
+            const bool from_a = (pass & 1) == 0;
+            const uint64_t *ki = from_a ? keys_a : keys_s;
+            const uint32_t *vi = from_a ? vals_a : vals_s;
+            const bool last = pass == kFullPasses - 1;
+            sweep_tile<kItems>(ki, vi, n, shift, s_base, words, nullptr, tile, &prm->bad_input,
+                               last ? keys_out : from_a ? keys_s : keys_a, last ? vals_out : from_a ? vals_s : vals_a,
+                               last ? xs0 : nullptr, last ? xs : nullptr);
+        }
+        // One release per tile, by thread 0: each wave first waits until its
+        // own stores have reached the L2 (the barrier alone does not wait for
+        // them), so thread 0's L2 write-back covers the whole tile.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __hip_atomic_fetch_add(&prm->fb_done[phase], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            s_ticket = atomicAdd(&prm->fb_ticket, 1u);
+        }
+        __syncthreads();
+        ticket = __builtin_amdgcn_readfirstlane(s_ticket);
     }
 }
 
@@ -386,31 +666,46 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
     const uint32_t hb = morton_hist_blocks(ws.n);
     const int cube_parts = (int)std::min<int64_t>(kCubeBlocks, ceil_div(ws.n, 256));  // as launch_cube
     // msum (at least n float4) holds the particles in input order until the
-    // moments need it: the last pass gathers one aligned float4 per particle.
-    k_morton_hist<<<hb, 256, 0, s>>>(pos, mass, ws.msum, n, ws.cube_part, cube_parts, ws.prm, ws.keys[0], ws.vals[0],
-                                     ws.hist_part, ws.lb_words, (uint64_t)ws.n_lb_words);
+    // moments need it: the gather reads one aligned float4 per particle.
+    k_morton_hist<<<hb, 256, 0, s>>>(pos, mass, ws.msum, n, ws.cube_part, cube_parts, ws.prm, ws.keys[1], ws.vals[1],
+                                     ws.hist_part, ws.lb_words, (uint64_t)kRadixPasses * nt * kRadixBins);
     k_digit_offsets<<<kRadixPasses, 1024, 0, s>>>(ws.hist_part, hb, ws.digit_offs);
     if (after_keys) {
         hipError_t e = hipEventRecord(after_keys, s);
         if (e != hipSuccess) return e;
     }
     const int items = sort_tile_items(ws.n);
-    for (int pass = 0; pass < kRadixPasses; pass++) {
-        const int src = pass & 1, dst = src ^ 1;
+    for (int pass = 0; pass < kRadixPasses; pass++) {  // keys[1] -> keys[0] -> ... -> keys[1]
+        const int src = (pass & 1) ^ 1, dst = src ^ 1;
         uint64_t *words = ws.lb_words + (uint64_t)pass * nt * kRadixBins;
-        const bool last = pass + 1 == kRadixPasses;
-#define ORR_ONESWEEP(ITEMS, GATHER)                                                                              \
-    k_onesweep<ITEMS, GATHER><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, \
-                                                          ws.prm, ws.keys[dst], ws.vals[dst],                      \
-                                                          GATHER ? ws.msum : nullptr, GATHER ? ws.xs : nullptr)
+#define ORR_ONESWEEP(ITEMS)                                                                                      \
+    k_onesweep<ITEMS><<<nt, kTileThreads, 0, s>>>(ws.keys[src], ws.vals[src], n, pass, ws.digit_offs, words, ws.prm, \
+                                                  ws.keys[dst], ws.vals[dst])
         if (items == 2)
-            last ? ORR_ONESWEEP(2, true) : ORR_ONESWEEP(2, false);
+            ORR_ONESWEEP(2);
         else if (items == 4)
-            last ? ORR_ONESWEEP(4, true) : ORR_ONESWEEP(4, false);
+            ORR_ONESWEEP(4);
         else
-            last ? ORR_ONESWEEP(8, true) : ORR_ONESWEEP(8, false);
+            ORR_ONESWEEP(8);
 #undef ORR_ONESWEEP
     }
+    k_sort_fix<<<(uint32_t)ceil_div(ws.n, kFixThreads), kFixThreads, 0, s>>>(
+        ws.keys[1], ws.vals[1], n, ws.msum, ws.keys[0], ws.vals[0], ws.xs, ws.prm, ws.hist_part);
+    // The fallback's ping-pong scratch: the node records, not written before
+    // the build (32 bytes per node, at least n nodes; 12 bytes per key used).
+    uint64_t *keys_s = reinterpret_cast<uint64_t *>(ws.nodes);
+    uint32_t *vals_s = reinterpret_cast<uint32_t *>(keys_s + ws.n);
+#define ORR_FALLBACK(ITEMS)                                                                                       \
+    k_sort_fallback<ITEMS><<<kFallbackBlocks, kTileThreads, 0, s>>>(ws.keys[1], ws.vals[1], keys_s, vals_s,        \
+                                                                    ws.keys[0], ws.vals[0], n, nt, ws.hist_part,  \
+                                                                    ws.lb_words, ws.prm, ws.msum, ws.xs)
+    if (items == 2)
+        ORR_FALLBACK(2);
+    else if (items == 4)
+        ORR_FALLBACK(4);
+    else
+        ORR_FALLBACK(8);
+#undef ORR_FALLBACK
     return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ typedef struct orr_tree orr_tree; /* host handle; device data lives in the works
 typedef struct {
     float cube_keys_ms; /* root cube and Morton keys */
     float sort_ms;      /* radix sort of (key, index) */
-    float gather_ms;    /* particles into sorted order: done by the sort's last pass, so 0 (in sort_ms) */
+    float gather_ms;    /* particles into sorted order: done inside the sort (its run fix-up), so 0 (in sort_ms) */
     float build_ms;     /* topology and escape indices (node staging included) */
     float moments_ms;   /* monopole moments */
     float walk_ms;      /* the traversal, scatter to caller order included */

@@ -142,6 +142,58 @@ def test_sort_tile_edges(n):
     run_full_case(z, np.full(n, 1 / n, np.float32), 32, EPS, 0.5)
 
 
+def clustered(n_clusters, per, side, seed, outlier=False):
+    """n_clusters cubes of edge `side` at random centres in [0.1, 0.9]^3, `per`
+    uniform particles each, plus optionally one particle at (3, 3, 3). The
+    sort orders keys by their high 32 bits first (a grid of cells 2^-10 to
+    2^-11 of the root side) and then each run of equal high bits by the low
+    bits: a cube of edge 1e-5 lies in one or a few such cells, so it makes
+    runs of up to `per` keys whose low bits mostly differ."""
+    rng = np.random.default_rng(seed)
+    c = rng.uniform(0.1, 0.9, (n_clusters, 1, 3))
+    pos = (c + rng.uniform(0, side, (n_clusters, per, 3))).reshape(-1, 3)
+    if outlier:
+        pos = np.vstack([pos, [[3.0, 3.0, 3.0]]])
+    pos = pos.astype(np.float32)
+    return pos, np.full(len(pos), 1 / len(pos), np.float32)
+
+
+def high_runs(keys):
+    """Lengths of the runs of equal high 32 key bits in sorted keys."""
+    h = keys >> np.uint64(31)
+    starts = np.flatnonzero(np.r_[True, h[1:] != h[:-1]])
+    return np.diff(np.r_[starts, len(h)])
+
+
+@pytest.mark.parametrize("n_clusters,per,outlier", [(40, 1500, False), (12, 64, False), (9, 65, False),
+                                                    (1, 4096, True), (1, 4097, True), (1, 20000, True),
+                                                    (3, 30000, False)])
+def test_sort_clustered_runs(n_clusters, per, outlier):
+    """Runs of equal high key bits of every length class: up to 64 (one
+    thread each), 65 to 4,096 (one work-group each), and longer (the full-key
+    fallback), at the class limits 64 / 65 and 4,096 / 4,097, with the
+    oracle's tree and both walks. The run lengths actually produced are
+    printed and their classes asserted."""
+    pos, mass = clustered(n_clusters, per, 1e-5, 11 + per, outlier)
+    ref, _ = run_full_case(pos, mass, 32, EPS, 0.5)
+    runs = high_runs(ref.tree.keys_sorted)
+    print(f"[runs] max {runs.max()} over 64: {(runs > 64).sum()} over 4096: {(runs > 4096).sum()}", flush=True)
+    assert runs.max() > 64 or per <= 64
+
+
+@pytest.mark.parametrize("n", [1 << 20, 2_000_003])
+def test_sort_fallback_large(n):
+    """One cluster of n - 1 particles and one far particle: a single run of
+    about n keys, sorted by the fallback over hundreds of tiles; the tree
+    against the oracle's, bit for bit."""
+    pos, mass = clustered(1, n - 1, 1e-5, 3, outlier=True)
+    print(f"[case] fallback n={n}", flush=True)
+    ot = oracle.build_tree(pos, mass, 32)
+    assert high_runs(ot.keys_sorted).max() > 4096
+    P, M = to_dev(pos, mass)
+    check_tree(orr.Tree(P, M, 32), ot)
+
+
 @pytest.mark.parametrize("name", ["plummer_16k", "plummer_131k", "uniform_262k"])
 def test_configs_full(name):
     pos, mass = inputs.make_config(name)
