@@ -59,9 +59,6 @@ __device__ __forceinline__ void lb_store(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-#ifndef ORR_LB_WIN
-#define ORR_LB_WIN 4
-#endif
 // Publishes a tile's value for one digit: inclusive for tile 0, else an
 // aggregate that successors can add while the tile works on.
 __device__ __forceinline__ void lb_publish(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine) {
@@ -69,23 +66,26 @@ __device__ __forceinline__ void lb_publish(uint64_t *words, uint32_t tile, uint3
 }
 
 // Exclusive prefix over earlier tiles of one value, after lb_publish: walks
-// back over the predecessors' words, ORR_LB_WIN at a time, adding aggregates
-// until an inclusive value, then publishes its own inclusive value. Sets
-// *err on a wait that never ends.
+// back over the predecessors' words, kWin at a time, adding aggregates until
+// an inclusive value, then publishes its own inclusive value. Sets *err on a
+// wait that never ends. A window of 4 suits tiles that start in dispatch
+// order (their predecessors are mostly resolved); tiles released together
+// find only aggregates and walk back far, and take a wider window.
+template <int kWin>
 __device__ __forceinline__ uint32_t lb_resolve(uint64_t *words, uint32_t tile, uint32_t stride, uint32_t mine,
                                                uint32_t *err) {
     if (tile == 0) return 0;
     uint32_t excl = 0, spins = 0;
     int64_t t = (int64_t)tile - 1;
     while (true) {
-        uint64_t v[ORR_LB_WIN];
+        uint64_t v[kWin];
 #pragma unroll
-        for (int k = 0; k < ORR_LB_WIN; k++)
+        for (int k = 0; k < kWin; k++)
             v[k] = t - k >= 0 ? lb_load(words + (uint64_t)(t - k) * stride) : kStInclusive;
         int used = 0;
         bool done = false;
 #pragma unroll
-        for (int k = 0; k < ORR_LB_WIN; k++) {
+        for (int k = 0; k < kWin; k++) {
             if (done || used < k) continue;
             const uint64_t st = v[k] & ~0xffffffffull;
             if (st == kStInclusive) {
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restri
 // order is input order. The tile is reordered by digit in LDS and written
 // out in that order, so consecutive threads store consecutive slots; with
 // xs given, each output slot o also receives xs[o] = xs0[value].
-template <int kItems>
+template <int kItems, int kLbWin>
 __device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
                                            uint32_t n, int shift, const uint32_t *digit_base, uint64_t *words,
                                            uint32_t *ticket, uint32_t tile_arg, uint32_t *err,
@@ -364,7 +364,7 @@ __device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in,
         const int d = threadIdx.x;
         uint32_t local = inc - tot;
         for (int k = 0; k < w; k++) local += s_wsum[k];
-        const uint32_t excl = lb_resolve(words + d, tile, kRadixBins, tot, err);
+        const uint32_t excl = lb_resolve<kLbWin>(words + d, tile, kRadixBins, tot, err);
         s_delta[d] = digit_base[d] + excl - local;
         uint32_t run = local;
         for (int k = 0; k < kWaves; k++) {  // in place: column d is this thread's alone
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
                                                            const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
                                                            DevParams *prm, uint64_t *__restrict__ keys_out,
                                                            uint32_t *__restrict__ vals_out) {
-    sweep_tile<kItems>(keys_in, vals_in, n, kSortLowBits + pass * kRadixBits, digit_offs + pass * kRadixBins,
+    sweep_tile<kItems, 4>(keys_in, vals_in, n, kSortLowBits + pass * kRadixBits, digit_offs + pass * kRadixBins,
                               lb_words, &prm->sort_ticket[pass], 0u, &prm->bad_input, keys_out, vals_out, nullptr,
                               nullptr);
 }
@@ -597,11 +597,25 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a
         if (phase == 0) {
             for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) s_h[k] = 0;
             __syncthreads();
+            // Lanes with equal digits add their count once (clustered keys
+            // share their high digits, and one LDS address per wave would
+            // serialise 64 adds).
             const uint64_t t0 = (uint64_t)tile * kTile;
-            for (uint64_t e = t0 + threadIdx.x; e < n && e < t0 + kTile; e += kTileThreads) {
-                const uint64_t key = keys_a[e];
-                for (int q = 0; q < kFullPasses; q++)
-                    atomicAdd(&s_h[q * kRadixBins + ((uint32_t)(key >> (q * kRadixBits)) & (kRadixBins - 1))], 1u);
+            const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+            for (uint32_t r = 0; r < kItems; r++) {
+                const uint64_t e = t0 + r * kTileThreads + threadIdx.x;
+                const bool valid = e < n;
+                const uint64_t key = valid ? keys_a[e] : 0ull;
+                const uint64_t live = __builtin_amdgcn_ballot_w64(valid);
+                for (int q = 0; q < kFullPasses; q++) {
+                    const uint32_t d = (uint32_t)(key >> (q * kRadixBits)) & (kRadixBins - 1);
+                    uint64_t peers = live;
+                    for (int b = 0; b < kRadixBits; b++) {
+                        const uint64_t m = __builtin_amdgcn_ballot_w64((d >> b) & 1u);
+                        peers &= ((d >> b) & 1u) ? m : ~m;
+                    }
+                    if (valid && (peers & lt) == 0ull) atomicAdd(&s_h[q * kRadixBins + d], (uint32_t)__popcll(peers));
+                }
             }
             __syncthreads();
             for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads)
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a
             const uint64_t *ki = from_a ? keys_a : keys_s;
             const uint32_t *vi = from_a ? vals_a : vals_s;
             const bool last = pass == kFullPasses - 1;
-            sweep_tile<kItems>(ki, vi, n, shift, s_base, words, nullptr, tile, &prm->bad_input,
+            sweep_tile<kItems, 16>(ki, vi, n, shift, s_base, words, nullptr, tile, &prm->bad_input,
                                last ? keys_out : from_a ? keys_s : keys_a, last ? vals_out : from_a ? vals_s : vals_a,
                                last ? xs0 : nullptr, last ? xs : nullptr);
         }
