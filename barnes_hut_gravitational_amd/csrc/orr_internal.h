@@ -25,19 +25,28 @@ constexpr int kRadixBits = 8;
 constexpr int kRadixBins = 1 << kRadixBits;
 // The main sort orders the keys by their high 32 bits (bits 31..62) in 4
 // passes; runs of equal high bits are then ordered by the low 31 bits in
-// place (k_sort_fix). A run longer than kFixMaxRun sends the whole array
-// through the fallback: the 8 passes of the full key.
+// place (k_sort_fix). Runs longer than kFixMaxRun go to the fallback, which
+// sorts their elements together by (rank of the run, low 31 bits) when there
+// are at most kMaxLongRuns of them, and the whole array by the full key
+// otherwise.
 constexpr int kRadixPasses = 4;
 constexpr int kSortLowBits = 31;
 constexpr int kFullPasses = 8;           // 64 / 8; bit 63 is always zero
+constexpr int kRunPasses = 5;            // digits of (run rank < 64) << 31 | low bits
 constexpr int kFixThreads = 512;         // positions per block of the run fix-up
 constexpr int kFixHalo = 64;             // window margin: runs up to 64 are finished per thread
 constexpr int kFixMaxRun = 4096;         // longest run finished by one work-group
+constexpr int kMaxLongRuns = 64;         // longer runs the fallback sorts by themselves
 constexpr int kFallbackBlocks = 512;     // persistent blocks of the fallback sort
+// The fallback's scratch in hist_part (free after k_digit_offsets): digit
+// counts, then the list of long runs (first position, end) as uint2.
+constexpr int kFbHistWords = kFullPasses * kRadixBins;
+constexpr int kFbListWords = 2 * kMaxLongRuns;
 
 constexpr int kCubeBlocks = 256;         // partial blocks of the root-cube reduction
 
 constexpr int kSortHistBlocks = 256;     // blocks of the key + histogram pass
+static_assert(kFbHistWords + kFbListWords <= kSortHistBlocks * kRadixPasses * kRadixBins, "fallback scratch fits");
 constexpr uint32_t kCutParticles = 4096; // subtrees of at most this many particles get one workgroup
 constexpr int kWaveCostBins = 2048;      // bins of the walk schedule's wave cost
 
@@ -55,10 +64,13 @@ struct DevParams {
     uint32_t sort_ticket[kRadixPasses];  // tile tickets of the one-sweep passes
     uint32_t n_cut;                      // entries of the cut-node list
     uint32_t n_top;                      // entries of the above-the-cut list
-    uint32_t sort_fallback;              // set by k_sort_fix: a run is too long, re-sort by the full key
+    uint32_t sort_fallback;              // set by k_sort_fix: some run is longer than kFixMaxRun
+    uint32_t n_long;                     // such runs (listed up to kMaxLongRuns)
     uint32_t fb_ticket;                  // work tickets of the fallback sort
-    uint32_t fb_done[1 + kFullPasses];   // finished tiles of the fallback's histogram phase and passes
-    uint32_t pad[5];
+    uint32_t fb_hist_done;               // finished tiles of the fallback's histogram phase
+    uint32_t fb_plan;                    // bit q: the fallback's digit q is not the same for all keys
+    uint32_t fb_done[1 + kFullPasses];   // phase 0 (nt once the plan is set) and finished tiles per pass
+    uint32_t pad[2];
 };
 static_assert(sizeof(DevParams) == 128, "DevParams layout");
 
@@ -78,7 +90,7 @@ struct Workspace {
                            // run fix-up writes the sorted keys to keys[0]
     uint32_t *vals[2];     // [n] payload: original index; perm ends in vals[0]
     uint32_t *hist_part;   // [kSortHistBlocks][kRadixPasses][kRadixBins] digit counts per block;
-                           // after the digit offsets, [kFullPasses][kRadixBins] counts of the fallback
+                           // after the digit offsets, the fallback's counts and list of long runs
     uint32_t *digit_offs;  // [kRadixPasses][kRadixBins] first output slot of each digit
     uint64_t *lb_words;    // look-back words of the sort's passes (room for the fallback's 8)
     int64_t n_lb_words;

@@ -32,15 +32,20 @@
 //     element at the run's start plus its stable rank by the low bits. A run
 //     of 65 to 4,096 is sorted by the work-group holding its first position
 //     (a bitonic sort in LDS of (low bits, position), unique values). A
-//     longer run - more than 4,096 particles in one cell of the H grid - sets
-//     a flag.
-//   * k_sort_fallback, always launched, returns at once unless that flag is
-//     set; then its persistent blocks redo the sort by the full key: 8 passes
-//     of the same tiles over the H-sorted keys, driven by one ticket counter
-//     (a histogram phase, then the passes in order), each phase waiting for
-//     the one before it with a bounded wait. Since equal keys have equal H,
-//     they are in index order in the H-sorted array, and a stable sort of it
-//     by the full key is the sort by (key, index).
+//     longer run - more than 4,096 particles in one cell of the H grid - is
+//     measured by a 512-way search for its end (H only grows along the
+//     array) and listed.
+//   * k_sort_fallback, always launched, returns at once unless some run was
+//     listed. Its persistent blocks then sort the listed runs' elements
+//     together, as one virtual array (the runs in position order), by
+//     (rank of the run, low 31 bits): LSD passes of the same tiles, driven
+//     by one ticket counter (a histogram phase, then the passes in order,
+//     each phase waiting for the one before it with a bounded wait). Digits
+//     that are the same for every element are skipped. With more than 64
+//     such runs the virtual array is the whole H-sorted array and the key
+//     the full key: equal keys have equal H, so they are in index order
+//     there, and a stable sort of it by the full key is the sort by
+//     (key, index).
 #include "orr_internal.h"
 
 namespace orr {
@@ -205,7 +210,10 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
                 prm->n_cut = 0;
                 prm->n_top = 0;
                 prm->sort_fallback = 0;
+                prm->n_long = 0;
                 prm->fb_ticket = 0;
+                prm->fb_hist_done = 0;
+                prm->fb_plan = 0;
                 for (int q = 0; q <= kFullPasses; q++) prm->fb_done[q] = 0;
             }
         }
@@ -284,21 +292,40 @@ __global__ __launch_bounds__(1024) void k_digit_offsets(const uint32_t *__restri
     }
 }
 
+// Plain arrays in and out (the high-bit passes, and the fallback's
+// scratch).
+struct ArrayIO {
+    const uint64_t *ki;
+    const uint32_t *vi;
+    uint64_t *ko;
+    uint32_t *vo;
+    __device__ __forceinline__ void load(uint64_t e, uint64_t &k, uint32_t &v) const {
+        k = ki[e];
+        v = vi[e];
+    }
+    __device__ __forceinline__ void store(uint64_t o, uint64_t k, uint32_t v) const {
+        ko[o] = k;
+        vo[o] = v;
+    }
+    __device__ __forceinline__ bool gathers() const { return false; }
+    __device__ __forceinline__ float4 fetch(uint32_t) const { return float4{}; }
+    __device__ __forceinline__ void store_with(uint64_t o, uint64_t k, uint32_t v, float4) const { store(o, k, v); }
+};
+
 // One stable pass over one tile of kTile = kTileThreads kItems keys, by digit
-// (key >> shift) & 255. The tile is `tile`, or, with a ticket counter, the
-// next ticket. digit_base[d]: the first output slot of digit d over all
-// tiles; words: this pass's look-back words, [tile][digit]. With W =
-// kTileThreads / 64 waves, wave w owns elements [kTile t + w kTile/W, +
-// kTile/W), lane l of round r element w kTile/W + 64 r + l, so (w, r, l)
-// order is input order. The tile is reordered by digit in LDS and written
-// out in that order, so consecutive threads store consecutive slots; with
-// xs given, each output slot o also receives xs[o] = xs0[value].
-template <int kItems, int kLbWin>
-__device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in, const uint32_t *__restrict__ vals_in,
-                                           uint32_t n, int shift, const uint32_t *digit_base, uint64_t *words,
-                                           uint32_t *ticket, uint32_t tile_arg, uint32_t *err,
-                                           uint64_t *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
-                                           const float4 *__restrict__ xs0, float4 *__restrict__ xs) {
+// (key >> shift) & 255, reading through io.load and writing through
+// io.store. The tile is `tile`, or, with a ticket counter, the next ticket.
+// digit_base[d]: the first output slot of digit d over all tiles; words:
+// this pass's look-back words, [tile][digit]. With W = kTileThreads / 64
+// waves, wave w owns elements [kTile t + w kTile/W, + kTile/W), lane l of
+// round r element w kTile/W + 64 r + l, so (w, r, l) order is input order.
+// The tile is reordered by digit in LDS and written out in that order, so
+// consecutive threads store consecutive slots. An IO that also gathers a
+// particle per element (io.gathers()) has each thread fetch all of its
+// particles before it stores any, so that the random reads overlap.
+template <int kItems, int kLbWin, class IO>
+__device__ __forceinline__ void sweep_tile(const IO &io, uint32_t n, int shift, const uint32_t *digit_base,
+                                           uint64_t *words, uint32_t *ticket, uint32_t tile_arg, uint32_t *err) {
     constexpr int kWaves = kTileThreads / 64, kTile = kTileThreads * kItems;
     static_assert(kWaves * kRadixBins * 4 <= kTile * 8, "counts fit in the key buffer");
     __shared__ uint64_t s_keys[kTile];  // first the per-wave digit counts, then the tile's keys by digit
@@ -323,8 +350,9 @@ __device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in,
     uint32_t val[kItems], rank[kItems];
     for (int r = 0; r < kItems; r++) {
         const uint64_t e = base + (uint64_t)r * 64 + lane;
-        key[r] = e < n ? keys_in[e] : 0ull;
-        val[r] = e < n ? vals_in[e] : 0u;
+        key[r] = 0ull;
+        val[r] = 0u;
+        if (e < n) io.load(e, key[r], val[r]);
     }
     // The tile's digit counts first, published at once, so that later tiles
     // can add them while this one ranks its keys.
@@ -387,15 +415,27 @@ __device__ __forceinline__ void sweep_tile(const uint64_t *__restrict__ keys_in,
         }
     }
     __syncthreads();
+    if (io.gathers()) {
+        float4 g[kItems];
+        for (int r = 0; r < kItems; r++) {
+            const uint32_t j = threadIdx.x + r * kTileThreads;
+            g[r] = j < tile_n ? io.fetch(s_vals[j]) : float4{};
+        }
+        for (int r = 0; r < kItems; r++) {
+            const uint32_t j = threadIdx.x + r * kTileThreads;
+            if (j < tile_n) {
+                const uint64_t k = s_keys[j];
+                const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
+                if (o < n) io.store_with(o, k, s_vals[j], g[r]);
+            }
+        }
+        return;
+    }
     for (uint32_t j = threadIdx.x; j < tile_n; j += kTileThreads) {
         const uint64_t k = s_keys[j];
         const uint32_t v = s_vals[j];
         const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
-        if (o < n) {  // always, unless a look-back wait gave up (flagged): then never a stray store
-            keys_out[o] = k;
-            vals_out[o] = v;
-            if (xs && v < n) xs[o] = xs0[v];
-        }
+        if (o < n) io.store(o, k, v);  // always, unless a look-back wait gave up (flagged)
     }
 }
 
@@ -406,9 +446,9 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
                                                            const uint32_t *__restrict__ digit_offs, uint64_t *lb_words,
                                                            DevParams *prm, uint64_t *__restrict__ keys_out,
                                                            uint32_t *__restrict__ vals_out) {
-    sweep_tile<kItems, 4>(keys_in, vals_in, n, kSortLowBits + pass * kRadixBits, digit_offs + pass * kRadixBins,
-                              lb_words, &prm->sort_ticket[pass], 0u, &prm->bad_input, keys_out, vals_out, nullptr,
-                              nullptr);
+    const ArrayIO io{keys_in, vals_in, keys_out, vals_out};
+    sweep_tile<kItems, 4>(io, n, kSortLowBits + pass * kRadixBits, digit_offs + pass * kRadixBins, lb_words,
+                          &prm->sort_ticket[pass], 0u, &prm->bad_input);
 }
 
 // Finishes the runs of equal high bits and gathers the particles. Input: the
@@ -420,15 +460,17 @@ __global__ __launch_bounds__(kTileThreads) void k_onesweep(const uint64_t *__res
 // looks for its run's start in q's bit word and the one before (at least the
 // 64 slots up to q) and for the next run's start in q's word and the one
 // after (at least 64 slots past q). Finding both, its run [s, e) is exact;
-// missing either, the run is longer than 64. Runs of 65 to kFixMaxRun keys are sorted by the block
-// holding their first position; longer ones set prm->sort_fallback and are
-// left to the fallback. Block 0 also clears the fallback's digit counts.
+// missing either, the run is longer than 64. Runs of 65 to kFixMaxRun keys
+// are sorted by the block holding their first position; a longer one is
+// measured and listed (first position, end) for the fallback, up to
+// kMaxLongRuns of them. Block 0 also clears the fallback's digit counts.
 __global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__restrict__ keys_in,
                                                           const uint32_t *__restrict__ vals_in, uint32_t n,
                                                           const float4 *__restrict__ xs0,
                                                           uint64_t *__restrict__ keys_out,
                                                           uint32_t *__restrict__ vals_out, float4 *__restrict__ xs,
-                                                          DevParams *__restrict__ prm, uint32_t *__restrict__ fb_hist) {
+                                                          DevParams *__restrict__ prm, uint32_t *__restrict__ fb_hist,
+                                                          uint2 *__restrict__ long_runs) {
     constexpr int kWin = kFixThreads + 2 * kFixHalo;
     constexpr int kWords = kWin / 64;
     constexpr int kMaxLong = kFixThreads / (kFixHalo + 1) + 1;  // long runs starting in one block
@@ -444,7 +486,7 @@ __global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__rest
     const uint32_t v = mine ? vals_in[p] : 0u;  // issued early: the gather waits on it
     if (t == 0) s_nlong = 0;
     if (blockIdx.x == 0)
-        for (int k = t; k < kFullPasses * kRadixBins; k += kFixThreads) fb_hist[k] = 0;
+        for (int k = t; k < kFbHistWords; k += kFixThreads) fb_hist[k] = 0;
     for (int q = t; q < kWin; q += kFixThreads) {
         const int64_t g = t0 - kFixHalo + q;
         s_buf[q] = g >= 0 && g < n ? keys_in[g] : 0ull;
@@ -504,8 +546,34 @@ __global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__rest
             end = __builtin_amdgcn_readfirstlane(s_end);
             __syncthreads();
         }
-        if (end == ~0u) {  // longer than kFixMaxRun
-            if (t == 0) atomicOr(&prm->sort_fallback, 1u);
+        if (end == ~0u) {
+            // Longer than kFixMaxRun. H only grows along the array, so the end
+            // is the first position with greater H: a 512-way search, each
+            // round narrowing [lo, hi] (the end lies in it, H = hs below lo)
+            // to one sample interval.
+            uint32_t lo = S + kFixMaxRun + 1, hi = n;
+            while (lo < hi) {
+                const uint32_t step = (hi - lo + kFixThreads - 1) / kFixThreads;
+                if (t == 0) s_end = ~0u;
+                __syncthreads();
+                const uint64_t j = (uint64_t)lo + (uint64_t)t * step;
+                if (j < hi && (keys_in[j] >> kSortLowBits) != hs) atomicMin(&s_end, (uint32_t)j);
+                __syncthreads();
+                const uint32_t f = __builtin_amdgcn_readfirstlane(s_end);
+                __syncthreads();  // s_end is reset in the next round
+                if (f == ~0u) {
+                    const uint32_t last = lo + step * min<uint32_t>(kFixThreads - 1, (hi - 1 - lo) / step);
+                    lo = last + 1;
+                } else {
+                    lo = f - lo >= step ? f - step + 1 : lo;
+                    hi = f;
+                }
+            }
+            if (t == 0) {
+                const uint32_t i = atomicAdd(&prm->n_long, 1u);
+                if (i < kMaxLongRuns) long_runs[i] = make_uint2(S, lo);
+                atomicOr(&prm->sort_fallback, 1u);
+            }
             continue;
         }
         const uint32_t len = end - S;
@@ -552,30 +620,152 @@ __device__ __forceinline__ void wait_count(const uint32_t *c, uint32_t target, u
     }
 }
 
-// The fallback: the stable sort of the H-sorted keys by the full key, run
-// only when k_sort_fix set prm->sort_fallback. Work is handed out by one
-// ticket counter: tickets [0, nt) are the histogram phase (the 8 digit counts
-// of each tile, and the tile's look-back words cleared), then nt tickets per
-// pass for the 8 passes in order. A block takes the next ticket only after
-// finishing its current one, so the holders of all earlier tickets are
-// running or done; a tile of phase f waits until all nt tiles of phase f - 1
-// are done (release after a tile, acquire before one). Passes alternate
-// between the H-sorted array (a) and scratch (s); the last writes the output
-// and gathers the particles.
+// The fallback's virtual array: the listed runs in position order, run r at
+// virtual positions [vb[r], vb[r + 1]), physical [s[r], s[r] + vb[r + 1] -
+// vb[r]), all of whose keys have high bits h[r]. Its key is (r << 31) | low
+// bits. In full mode it is the whole array with the full key (one "run").
+struct RunTable {
+    uint32_t s[kMaxLongRuns], vb[kMaxLongRuns + 1], h[kMaxLongRuns];
+    uint32_t nr;
+    uint32_t full;
+};
+
+// Reads the virtual array from the H-sorted input (src_a) or a plain
+// scratch array; writes a plain scratch array or the output at the physical
+// positions with the particles gathered (dst_out).
+struct FallbackIO {
+    const RunTable *tb;
+    bool src_a, dst_out;
+    const uint64_t *ki;
+    const uint32_t *vi;
+    uint64_t *ko;
+    uint32_t *vo;
+    const float4 *xs0;
+    float4 *xs;
+    uint32_t n;  // particles: gathered indices are checked against it
+    __device__ __forceinline__ uint32_t run_of(uint64_t e) const {  // last r with vb[r] <= e
+        uint32_t lo = 0, hi = tb->nr - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (tb->vb[mid] <= e) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+    __device__ __forceinline__ void load(uint64_t e, uint64_t &k, uint32_t &v) const {
+        if (!src_a) {
+            k = ki[e];
+            v = vi[e];
+        } else if (tb->full) {
+            k = ki[e];
+            v = vi[e];
+        } else {
+            const uint32_t r = run_of(e);
+            const uint64_t ph = tb->s[r] + (e - tb->vb[r]);
+            k = ((uint64_t)r << kSortLowBits) | (ki[ph] & 0x7fffffffull);
+            v = vi[ph];
+        }
+    }
+    __device__ __forceinline__ void store(uint64_t o, uint64_t k, uint32_t v) const {
+        if (!dst_out) {
+            ko[o] = k;
+            vo[o] = v;
+            return;
+        }
+        uint64_t ph = o;
+        if (!tb->full) {
+            const uint32_t r = (uint32_t)(k >> kSortLowBits);
+            ph = tb->s[r] + (o - tb->vb[r]);
+            k = ((uint64_t)tb->h[r] << kSortLowBits) | (k & 0x7fffffffull);
+        }
+        ko[ph] = k;
+        vo[ph] = v;
+        if (v < n) xs[ph] = xs0[v];
+    }
+    __device__ __forceinline__ bool gathers() const { return dst_out; }
+    __device__ __forceinline__ float4 fetch(uint32_t v) const { return v < n ? xs0[v] : float4{}; }
+    __device__ __forceinline__ void store_with(uint64_t o, uint64_t k, uint32_t v, float4 g) const {
+        if (!dst_out) {
+            ko[o] = k;
+            vo[o] = v;
+            return;
+        }
+        uint64_t ph = o;
+        if (!tb->full) {
+            const uint32_t r = (uint32_t)(k >> kSortLowBits);
+            ph = tb->s[r] + (o - tb->vb[r]);
+            k = ((uint64_t)tb->h[r] << kSortLowBits) | (k & 0x7fffffffull);
+        }
+        ko[ph] = k;
+        vo[ph] = v;
+        xs[ph] = g;
+    }
+};
+
+// The fallback, run only when k_sort_fix listed a run longer than
+// kFixMaxRun (prm->sort_fallback). Work is handed out by one ticket counter:
+// tickets [0, nt) are the histogram phase (the digit counts of each tile of
+// the virtual array, and the tile's look-back words cleared), then nt
+// tickets per pass slot. A block takes the next ticket only after finishing
+// its current one, so the holders of all earlier tickets are running or
+// done. The histogram tile that finishes last sets the plan (the digits that
+// differ between keys) and then marks phase 0 done; a tile of slot j waits
+// for the plan, skips when fewer than j digits differ, and otherwise waits
+// until all nt tiles of slot j - 1 are done (release after a tile, acquire
+// before one). Slot j sorts by the j-th differing digit, from the input
+// (slot 1) or scratch x / y, to y / x or, for the last slot, the output;
+// with no differing digit slot 1 copies the input to the output.
 template <int kItems>
-__global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a, uint32_t *vals_a, uint64_t *keys_s,
-                                                                uint32_t *vals_s, uint64_t *keys_out,
-                                                                uint32_t *vals_out, uint32_t n, uint32_t nt,
-                                                                uint32_t *fb_hist, uint64_t *lb_words, DevParams *prm,
-                                                                const float4 *__restrict__ xs0, float4 *xs) {
+__global__ __launch_bounds__(kTileThreads) void k_sort_fallback(const uint64_t *keys_a, const uint32_t *vals_a,
+                                                                uint64_t *keys_x, uint32_t *vals_x, uint64_t *keys_y,
+                                                                uint32_t *vals_y, uint64_t *keys_out,
+                                                                uint32_t *vals_out, uint32_t n, uint32_t *fb_hist,
+                                                                const uint2 *long_runs, uint64_t *lb_words,
+                                                                DevParams *prm, const float4 *__restrict__ xs0,
+                                                                float4 *xs) {
     constexpr int kTile = kTileThreads * kItems;
-    if (prm->sort_fallback == 0) return;
-    __shared__ uint32_t s_ticket;
+    // Values that steer loops around barriers are read with readfirstlane:
+    // prm is written by this kernel, so its loads are vector loads, which the
+    // compiler cannot prove uniform.
+    if (__builtin_amdgcn_readfirstlane(prm->sort_fallback) == 0) return;
+    __shared__ RunTable tb;
+    __shared__ uint32_t s_ticket, s_flag;
     __shared__ uint32_t s_base[kRadixBins];
     __shared__ uint32_t s_wsum[kRadixBins / 64];
     __shared__ uint32_t s_h[kFullPasses * kRadixBins];
-    const uint32_t total = (1u + kFullPasses) * nt;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // The run table: the listed runs ranked by first position.
+    const uint32_t n_long = __builtin_amdgcn_readfirstlane(prm->n_long);
+    const bool full = n_long > (uint32_t)kMaxLongRuns;
+    if (threadIdx.x == 0) {
+        tb.full = full;
+        tb.nr = full ? 1u : n_long;
+    }
+    if (full) {
+        if (threadIdx.x == 0) {
+            tb.s[0] = 0;
+            tb.vb[0] = 0;
+            tb.vb[1] = n;
+            tb.h[0] = 0;
+        }
+    } else if (threadIdx.x < n_long) {
+        const uint2 me = long_runs[threadIdx.x];
+        uint32_t rank = 0;
+        for (uint32_t q = 0; q < n_long; q++) rank += long_runs[q].x < me.x;
+        tb.s[rank] = me.x;
+        tb.vb[rank + 1] = me.y - me.x;  // lengths for now
+        tb.h[rank] = (uint32_t)(keys_a[me.x] >> kSortLowBits);
+    }
+    __syncthreads();
+    if (!full && threadIdx.x == 0) {
+        tb.vb[0] = 0;
+        for (uint32_t r = 0; r < n_long; r++) tb.vb[r + 1] += tb.vb[r];
+    }
+    __syncthreads();
+    const uint32_t m = __builtin_amdgcn_readfirstlane(tb.vb[tb.nr]);
+    const int nd = __builtin_amdgcn_readfirstlane(full ? kFullPasses : kRunPasses);
+    const uint32_t nt = __builtin_amdgcn_readfirstlane((m + kTile - 1) / kTile);
+    const uint32_t total = __builtin_amdgcn_readfirstlane((1u + (uint32_t)nd) * nt);
     // Thread 0 takes the tickets; the loop is entered and left on the same
     // uniform value (readfirstlane after a barrier), and thread 0's work at
     // the end of an iteration is followed by a barrier, so every barrier in
@@ -585,75 +775,126 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a
     uint32_t ticket = __builtin_amdgcn_readfirstlane(s_ticket);
     while (ticket < total) {
         const uint32_t phase = ticket / nt, tile = ticket % nt;
-        if (phase > 0) {
-            // Acquire by thread 0, passed on to the work-group by the barrier
-            // (its waves share one CU and its L1).
-            if (threadIdx.x == 0) {
-                wait_count(&prm->fb_done[phase - 1], nt, &prm->bad_input);
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            }
-            __syncthreads();
-        }
+        bool counted = false;  // phase 0 marks itself done through the plan
         if (phase == 0) {
-            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) s_h[k] = 0;
-            __syncthreads();
             // Lanes with equal digits add their count once (clustered keys
             // share their high digits, and one LDS address per wave would
             // serialise 64 adds).
+            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) s_h[k] = 0;
+            __syncthreads();
+            const FallbackIO io{&tb, true, false, keys_a, vals_a, nullptr, nullptr, nullptr, nullptr, n};
             const uint64_t t0 = (uint64_t)tile * kTile;
             const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
             for (uint32_t r = 0; r < kItems; r++) {
                 const uint64_t e = t0 + r * kTileThreads + threadIdx.x;
-                const bool valid = e < n;
-                const uint64_t key = valid ? keys_a[e] : 0ull;
+                const bool valid = e < m;
+                uint64_t key = 0ull;
+                uint32_t val = 0u;
+                if (valid) io.load(e, key, val);
                 const uint64_t live = __builtin_amdgcn_ballot_w64(valid);
-                for (int q = 0; q < kFullPasses; q++) {
+                for (int q = 0; q < nd; q++) {
                     const uint32_t d = (uint32_t)(key >> (q * kRadixBits)) & (kRadixBins - 1);
                     uint64_t peers = live;
                     for (int b = 0; b < kRadixBits; b++) {
-                        const uint64_t m = __builtin_amdgcn_ballot_w64((d >> b) & 1u);
-                        peers &= ((d >> b) & 1u) ? m : ~m;
+                        const uint64_t mk = __builtin_amdgcn_ballot_w64((d >> b) & 1u);
+                        peers &= ((d >> b) & 1u) ? mk : ~mk;
                     }
                     if (valid && (peers & lt) == 0ull) atomicAdd(&s_h[q * kRadixBins + d], (uint32_t)__popcll(peers));
                 }
             }
             __syncthreads();
-            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads)
+            for (int k = threadIdx.x; k < nd * kRadixBins; k += kTileThreads)
                 if (s_h[k]) atomicAdd(&fb_hist[k], s_h[k]);
-            for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) {
+            for (int k = threadIdx.x; k < nd * kRadixBins; k += kTileThreads) {
                 const int q = k / kRadixBins, d = k % kRadixBins;
                 lb_store(lb_words + ((uint64_t)q * nt + tile) * kRadixBins + d, 0ull);
             }
-        } else {
-            const int pass = (int)phase - 1;
-            // First output slot of each digit: the exclusive scan of the counts.
-            uint32_t c = 0, inc = 0;
-            if (threadIdx.x < kRadixBins) {
-                c = __hip_atomic_load(&fb_hist[pass * kRadixBins + threadIdx.x], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                inc = c;
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t u = __shfl_up(inc, o, 64);
-                    if (lane >= o) inc += u;
+            // The last histogram tile sets the plan, then marks phase 0 done.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const uint32_t prev =
+                    __hip_atomic_fetch_add(&prm->fb_hist_done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                s_flag = prev + 1 == nt;
+                if (s_flag) s_h[0] = 0;  // the plan's bits, gathered below
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(s_flag)) {
+                uint32_t varies = 0;
+                for (int k = threadIdx.x; k < nd * kRadixBins; k += kTileThreads) {
+                    const uint32_t c =
+                        __hip_atomic_load(&fb_hist[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (c != 0 && c != m) varies |= 1u << (k / kRadixBins);  // two or more digits occur
                 }
-                if (lane == 63) s_wsum[w] = inc;
+                __syncthreads();  // s_h[0] is cleared before any thread adds to it
+                if (varies) atomicOr(&s_h[0], varies);
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    __hip_atomic_store(&prm->fb_plan, s_h[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(&prm->fb_done[0], nt, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            counted = true;
+        } else {
+            if (threadIdx.x == 0) {
+                wait_count(&prm->fb_done[0], nt, &prm->bad_input);
+                s_flag = __hip_atomic_load(&prm->fb_plan, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
-            if (threadIdx.x < kRadixBins) {
-                uint32_t off = inc - c;
-                for (int k = 0; k < w; k++) off += s_wsum[k];
-                s_base[threadIdx.x] = off;
+            const uint32_t plan = __builtin_amdgcn_readfirstlane(s_flag);
+            const uint32_t slots = __popc(plan);
+            const uint32_t slot = phase;  // 1-based
+            if (slot <= max(slots, 1u)) {
+                // Acquire by thread 0 after the previous slot, passed on to the
+                // work-group by the barrier (its waves share one CU and its L1).
+                if (threadIdx.x == 0) {
+                    if (slot >= 2) wait_count(&prm->fb_done[slot - 1], nt, &prm->bad_input);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                }
+                __syncthreads();
+                const bool last = slot == max(slots, 1u);
+                const uint64_t *ki = slot == 1 ? keys_a : (slot & 1) ? keys_y : keys_x;
+                const uint32_t *vi = slot == 1 ? vals_a : (slot & 1) ? vals_y : vals_x;
+                uint64_t *ko = last ? keys_out : (slot & 1) ? keys_x : keys_y;
+                uint32_t *vo = last ? vals_out : (slot & 1) ? vals_x : vals_y;
+                const FallbackIO io{&tb, slot == 1, last, ki, vi, ko, vo, xs0, xs, n};
+                if (slots == 0) {
+                    // Every digit is the same: the input order is the sorted order.
+                    const uint64_t t0 = (uint64_t)tile * kTile;
+                    for (uint64_t e = t0 + threadIdx.x; e < m && e < t0 + kTile; e += kTileThreads) {
+                        uint64_t k;
+                        uint32_t v;
+                        io.load(e, k, v);
+                        io.store(e, k, v);
+                    }
+                } else {
+                    uint32_t q = 0;  // the slot-th differing digit
+                    for (uint32_t b = plan, j = 0; b; b &= b - 1)
+                        if (++j == slot) q = __ffs(b) - 1;
+                    // First output slot of each digit: the exclusive scan of the counts.
+                    uint32_t c = 0, inc = 0;
+                    if (threadIdx.x < kRadixBins) {
+                        c = __hip_atomic_load(&fb_hist[q * kRadixBins + threadIdx.x], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                        inc = c;
+                        for (int o = 1; o < 64; o <<= 1) {
+                            const uint32_t u = __shfl_up(inc, o, 64);
+                            if (lane >= o) inc += u;
+                        }
+                        if (lane == 63) s_wsum[w] = inc;
+                    }
+                    __syncthreads();
+                    if (threadIdx.x < kRadixBins) {
+                        uint32_t off = inc - c;
+                        for (int k = 0; k < w; k++) off += s_wsum[k];
+                        s_base[threadIdx.x] = off;
+                    }
+                    __syncthreads();
+                    sweep_tile<kItems, 16>(io, m, (int)q * kRadixBits, s_base,
+                                           lb_words + (uint64_t)(slot - 1) * nt * kRadixBins, nullptr, tile,
+                                           &prm->bad_input);
+                }
             }
-            __syncthreads();
-            uint64_t *words = lb_words + (uint64_t)pass * nt * kRadixBins;
-            const int shift = pass * kRadixBits;
-            const bool from_a = (pass & 1) == 0;
-            const uint64_t *ki = from_a ? keys_a : keys_s;
-            const uint32_t *vi = from_a ? vals_a : vals_s;
-            const bool last = pass == kFullPasses - 1;
-            sweep_tile<kItems, 16>(ki, vi, n, shift, s_base, words, nullptr, tile, &prm->bad_input,
-                               last ? keys_out : from_a ? keys_s : keys_a, last ? vals_out : from_a ? vals_s : vals_a,
-                               last ? xs0 : nullptr, last ? xs : nullptr);
         }
         // One release per tile, by thread 0: each wave first waits until its
         // own stores have reached the L2 (the barrier alone does not wait for
@@ -661,7 +902,8 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(uint64_t *keys_a
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) {
-            __hip_atomic_fetch_add(&prm->fb_done[phase], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (!counted)
+                __hip_atomic_fetch_add(&prm->fb_done[phase], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             s_ticket = atomicAdd(&prm->fb_ticket, 1u);
         }
         __syncthreads();
@@ -703,16 +945,20 @@ hipError_t launch_keys_and_sort(const float *pos, const float *mass, const Works
             ORR_ONESWEEP(8);
 #undef ORR_ONESWEEP
     }
+    uint2 *long_runs = reinterpret_cast<uint2 *>(ws.hist_part + kFbHistWords);
     k_sort_fix<<<(uint32_t)ceil_div(ws.n, kFixThreads), kFixThreads, 0, s>>>(
-        ws.keys[1], ws.vals[1], n, ws.msum, ws.keys[0], ws.vals[0], ws.xs, ws.prm, ws.hist_part);
+        ws.keys[1], ws.vals[1], n, ws.msum, ws.keys[0], ws.vals[0], ws.xs, ws.prm, ws.hist_part, long_runs);
     // The fallback's ping-pong scratch: the node records, not written before
-    // the build (32 bytes per node, at least n nodes; 12 bytes per key used).
-    uint64_t *keys_s = reinterpret_cast<uint64_t *>(ws.nodes);
-    uint32_t *vals_s = reinterpret_cast<uint32_t *>(keys_s + ws.n);
-#define ORR_FALLBACK(ITEMS)                                                                                       \
-    k_sort_fallback<ITEMS><<<kFallbackBlocks, kTileThreads, 0, s>>>(ws.keys[1], ws.vals[1], keys_s, vals_s,        \
-                                                                    ws.keys[0], ws.vals[0], n, nt, ws.hist_part,  \
-                                                                    ws.lb_words, ws.prm, ws.msum, ws.xs)
+    // the build (32 bytes per node, at least n nodes): x at byte 0, y at 16 n,
+    // 12 bytes per element each.
+    uint64_t *keys_x = reinterpret_cast<uint64_t *>(ws.nodes);
+    uint32_t *vals_x = reinterpret_cast<uint32_t *>(keys_x + ws.n);
+    uint64_t *keys_y = keys_x + 2 * ws.n;
+    uint32_t *vals_y = reinterpret_cast<uint32_t *>(keys_y + ws.n);
+#define ORR_FALLBACK(ITEMS)                                                                                         \
+    k_sort_fallback<ITEMS><<<kFallbackBlocks, kTileThreads, 0, s>>>(ws.keys[1], ws.vals[1], keys_x, vals_x, keys_y, \
+                                                                    vals_y, ws.keys[0], ws.vals[0], n, ws.hist_part, \
+                                                                    long_runs, ws.lb_words, ws.prm, ws.msum, ws.xs)
     if (items == 2)
         ORR_FALLBACK(2);
     else if (items == 4)

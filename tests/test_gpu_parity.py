@@ -165,20 +165,27 @@ def high_runs(keys):
     return np.diff(np.r_[starts, len(h)])
 
 
-@pytest.mark.parametrize("n_clusters,per,outlier", [(40, 1500, False), (12, 64, False), (9, 65, False),
-                                                    (1, 4096, True), (1, 4097, True), (1, 20000, True),
-                                                    (3, 30000, False)])
-def test_sort_clustered_runs(n_clusters, per, outlier):
+@pytest.mark.parametrize("n_clusters,per,side,outlier", [(40, 1500, 1e-5, False), (12, 64, 1e-5, False),
+                                                         (9, 65, 1e-5, False), (1, 4096, 1e-5, True),
+                                                         (1, 4097, 1e-5, True), (1, 20000, 1e-5, True),
+                                                         (3, 30000, 1e-5, False), (2, 9000, 0.0, True),
+                                                         (70, 5000, 1e-6, False)])
+def test_sort_clustered_runs(n_clusters, per, side, outlier):
     """Runs of equal high key bits of every length class: up to 64 (one
-    thread each), 65 to 4,096 (one work-group each), and longer (the full-key
+    thread each), 65 to 4,096 (one work-group each), and longer (the
     fallback), at the class limits 64 / 65 and 4,096 / 4,097, with the
-    oracle's tree and both walks. The run lengths actually produced are
-    printed and their classes asserted."""
-    pos, mass = clustered(n_clusters, per, 1e-5, 11 + per, outlier)
+    oracle's tree and both walks. Longer runs are sorted by their low bits as
+    one array when there are at most 64 of them (here 1, 2 and 3, the 2 of
+    them clusters of coincident points whose low bits are all equal) and the
+    whole array by the full key otherwise (here 70). The run lengths
+    actually produced are printed and their classes asserted."""
+    pos, mass = clustered(n_clusters, per, side, 11 + per, outlier)
     ref, _ = run_full_case(pos, mass, 32, EPS, 0.5)
     runs = high_runs(ref.tree.keys_sorted)
     print(f"[runs] max {runs.max()} over 64: {(runs > 64).sum()} over 4096: {(runs > 4096).sum()}", flush=True)
     assert runs.max() > 64 or per <= 64
+    if n_clusters == 70:
+        assert (runs > 4096).sum() > 64
 
 
 @pytest.mark.parametrize("n", [1 << 20, 2_000_003])
