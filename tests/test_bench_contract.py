@@ -1,5 +1,5 @@
 """CPU-side checks of the benchmark's command-line contract: more than one GPU
-is refused with a message (this build measures one GPU), and the JSON line's
+is refused with a message (the benchmark measures one GPU), and the JSON line's
 helpers behave. No GPU is touched."""
 
 import os
