@@ -10,9 +10,11 @@
 // Structure. A 63-bit key splits into its high 32 bits H (bits 31..62) and
 // its low 31 bits. Sorting by H alone takes 4 one-sweep LSD passes of 8-bit
 // digits instead of 8; what remains is to order each run of equal H by the
-// low bits, and in Morton order such runs are short: a run is a cell 2^-10
-// of the root side or smaller, and on the Plummer, uniform and merger inputs
-// runs average 1.0 to 1.5 keys and never exceed 30.
+// low bits, and in Morton order such runs are short: H holds the first 10
+// levels of the key and the x and y bits of the 11th, so a run lies in one
+// box of 2^-11 of the root side in x and y and 2^-10 in z, and on the
+// Plummer, uniform and merger inputs runs average 1.0 to 1.5 keys and never
+// exceed 30.
 //   * k_morton_hist computes every key once and the 4 digit histograms of H;
 //     k_digit_offsets turns them into the first output slot of each digit.
 //   * k_onesweep, one launch per pass: a tile of 512 threads x 2, 4 or 8 keys
@@ -32,7 +34,7 @@
 //     element at the run's start plus its stable rank by the low bits. A run
 //     of 65 to 4,096 is sorted by the work-group holding its first position
 //     (a bitonic sort in LDS of (low bits, position), unique values). A
-//     longer run - more than 4,096 particles in one cell of the H grid - is
+//     longer run - more than 4,096 particles in one such box - is
 //     measured by a 512-way search for its end (H only grows along the
 //     array) and listed.
 //   * k_sort_fallback, always launched, returns at once unless some run was
