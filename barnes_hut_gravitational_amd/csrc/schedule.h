@@ -260,7 +260,7 @@ __device__ __forceinline__ void wave_order_list(const uint32_t *__restrict__ cos
 // takes its target waves from that XCD's list of the schedule, in block order
 // (slot s of the XCD runs list entry s: targets 64 (wave0 + w) .. + 63 of the
 // schedule's wave w, whose waves start at wave0). With kSplit hardware waves
-// per target wave, consecutive hardware waves of a block share one slot and
+// per target wave, consecutive hardware waves of the XCD share one slot and
 // *part receives this wave's share (0 .. kSplit - 1). Slots past the list get
 // the first target past the schedule's waves, which no lane walks.
 template <uint32_t kSplit>
@@ -268,8 +268,11 @@ __device__ __forceinline__ uint32_t scheduled_target(const uint32_t *__restrict_
                                                      uint32_t wave0, uint32_t *part) {
     const uint32_t L = (kScheduleRegions / 8u) * ((n_waves + kScheduleRegions - 1u) / kScheduleRegions);
     const uint32_t x = blockIdx.x & 7u;
-    const uint32_t hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t s = (blockIdx.x >> 3) * (kWalkBlock / 64u / kSplit) + hw / kSplit;
+    // The hardware waves of XCD x in launch order; kSplit consecutive ones
+    // share one target wave (a work-group holds 4 waves; teams of 8 or 16
+    // span 2 or 4 work-groups, which need not run together).
+    const uint32_t hw = (blockIdx.x >> 3) * (kWalkBlock / 64u) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t s = hw / kSplit;
     *part = hw % kSplit;
     const uint32_t w = s < order[8u * L + x] ? min(order[x * L + s], n_waves) : n_waves;
     return (wave0 + w) * 64u + (threadIdx.x & 63u);

@@ -69,7 +69,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // same node sequence (the next node any lane wants is c + 1 if some lane
 // opened c and escape[c] otherwise); kMin exists to measure the cost of the
 // explicit reduction.
-// kSplit (1, 2, 4): the target wave's 64 walks are shared by kSplit
+// kSplit (1, 2, 4, 8, 16): the target wave's 64 walks are shared by kSplit
 // hardware waves. Each runs the whole traversal (node loads, opening tests of
 // all 64 lanes, advance), so all of them step through the same nodes, and
 // each adds the terms, accepted cells and opened leaves, of its own 64 /
@@ -88,7 +88,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t part,
                                               uint32_t n, uint32_t n_nodes, float eps2, float theta2,
                                               uint32_t s2_shift, const WalkOut &out, WalkLds &lds) {
-    static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4, "split");
+    static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4 || kSplit == 8 || kSplit == 16, "split");
     constexpr uint32_t kOwn = 64u / kSplit;  // lanes whose terms this wave adds
     const uint64_t own_mask = kSplit == 1 ? ~0ull : ((1ull << kOwn) - 1ull) << (part * kOwn);
     const bool own = kSplit == 1 || __lane_id() / kOwn == part;
@@ -275,14 +275,20 @@ __global__ void k_zero_u64(unsigned long long *p) { *p = 0ull; }
 
 // Hardware waves per target wave of the coherent walk: grids of target waves
 // that fill only part of the GPU's wave slots (256 CUs x 4 SIMDs x 8 waves)
-// share each target wave's terms among 2 or 4 hardware waves (walk_coherent,
-// kSplit), so that more SIMDs work on the same walks.
+// share each target wave's terms among 2 to 16 hardware waves (walk_coherent,
+// kSplit), so that more SIMDs work on the same walks. Measured (walk medians,
+// Plummer): 16 waves beat 8 up to 128 target waves (8,192 particles: 0.297
+// against 0.324 ms) but not at 256 (16,384: 0.385 against 0.388, and uniform
+// 16,384 0.216 against 0.196); 8 beat 4 up to 512 (16,384: 0.397 against
+// 0.463, 32,768: 0.475 against 0.495).
 #ifndef ORR_WALK_SPLIT_FORCE
 #define ORR_WALK_SPLIT_FORCE 0
 #endif
 uint32_t walk_split(int64_t target_waves) {
     if (ORR_WALK_SPLIT_FORCE) return ORR_WALK_SPLIT_FORCE;
     constexpr int64_t kSlots = 256 * 4 * 8;
+    if (16 * target_waves <= kSlots / 4) return 16;
+    if (8 * target_waves <= kSlots / 2) return 8;
     if (4 * target_waves <= kSlots / 2) return 4;
     if (2 * target_waves <= kSlots / 2) return 2;
     return 1;
@@ -300,7 +306,7 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
         // 8 XCD lists of up to L target waves each (scheduled_target)
         const int64_t L = (int64_t)(kScheduleRegions / 8) * ceil_div(nw, (int64_t)kScheduleRegions);
         const uint32_t split = mode == kWalkCoherentMin ? 1u : walk_split(nw);
-        const unsigned cblocks = 8u * (unsigned)ceil_div(L, (int64_t)(kWalkBlock / 64 / split));
+        const unsigned cblocks = 8u * (unsigned)ceil_div(L * split, (int64_t)(kWalkBlock / 64));
         const uint32_t wave0 = (uint32_t)(rg.first / 64);
         const uint32_t e2 = theta2_pow2_exp(theta2);
 #define ORR_COHERENT(OFF32, MIN, SPLIT)                                                                          \
@@ -314,6 +320,10 @@ hipError_t launch_walk_t(const Workspace &ws, int mode, const WalkRange &rg, flo
                 ORR_COHERENT(false, true, 1);
         } else if (!off32) {
             ORR_COHERENT(false, false, 1);
+        } else if (split == 16) {
+            ORR_COHERENT(true, false, 16);
+        } else if (split == 8) {
+            ORR_COHERENT(true, false, 8);
         } else if (split == 4) {
             ORR_COHERENT(true, false, 4);
         } else if (split == 2) {
