@@ -1,4 +1,7 @@
-"""Build liborr.so (HIP, gfx950) in-tree: barnes_hut_gravitational_amd/liborr.so.
+"""Build liborr.so (HIP, gfx950) in-tree: barnes_hut_gravitational_amd/liborr.so,
+and its checked build liborr_checked.so (ORR_CHECKED=1: every index a kernel
+takes from device data is tested against its array's length, and a failure is
+reported instead of read or written; csrc/checked.h).
 
 Every translation unit is compiled by hipcc for gfx950 with
   -ffp-contract=off   no fused multiply-add contraction: every float step is
@@ -20,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liborr.so")
+CHECKED_LIB = os.path.join(PKG, "liborr_checked.so")
 SOURCES = ["cube_keys.hip", "sort.hip", "tree.hip", "walk.hip", "walk_grouped.hip", "walk_width.hip", "direct.hip", "orr_api.hip"]
 ARCH = "gfx950"
 
@@ -45,10 +49,11 @@ def _compile(src: str, extra=(), build_dir=BUILD) -> str:
     return obj
 
 
-def build(jobs: int = 8, extra_flags=(), out: str = LIB) -> str:
+def build(jobs: int = 8, extra_flags=(), out: str = LIB, build_dir: str | None = None) -> str:
     """Compile and link; extra_flags (e.g. -D definitions) and out allow
     variant builds elsewhere."""
-    build_dir = BUILD if out == LIB else out + ".objs"
+    if build_dir is None:
+        build_dir = BUILD if out == LIB else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
         objs = list(ex.map(lambda src: _compile(src, extra_flags, build_dir), SOURCES))
@@ -59,6 +64,11 @@ def build(jobs: int = 8, extra_flags=(), out: str = LIB) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, out)
     return out
+
+
+def build_checked(jobs: int = 8) -> str:
+    """The checked build, liborr_checked.so (same ABI)."""
+    return build(jobs, ["-DORR_CHECKED=1"], CHECKED_LIB, os.path.join(BUILD, "checked"))
 
 
 def resources(src: str = "walk.hip") -> list:
@@ -93,3 +103,4 @@ if __name__ == "__main__":
                 print(f"{src}\t{name}\tvgpr {v}\tsgpr {sg}\tlds {lds}\tscratch {scratch}\tvgpr_spill {spill}")
     else:
         print(build())
+        print(build_checked())

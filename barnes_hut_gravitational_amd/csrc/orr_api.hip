@@ -247,6 +247,8 @@ orr_status read_params(const orr_tree *t, DevParams *out) {
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
     if ((e = hipStreamSynchronize(t->stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     if (out->bad_input & 2u) return fail(ORR_ERR_HIP, "a device look-back wait gave up; results are invalid");
+    if (out->bad_input & kBadIndex)
+        return fail(ORR_ERR_HIP, "a device index check failed (index out of its array's range); results are invalid");
     return ORR_OK;
 }
 

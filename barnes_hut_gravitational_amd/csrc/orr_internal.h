@@ -56,7 +56,8 @@ struct DevParams {
     float side;
     float scale;          // 2^21 / side
     uint32_t bad_input;   // bit 0: non-finite position/mass, negative mass or overflowing extent;
-                          // bit 1: a look-back or phase wait of the sort gave up (never expected)
+                          // bit 1: a look-back or phase wait of the sort gave up (never expected);
+                          // bit 2 (kBadIndex): an index check of the checked build failed
     uint32_t n_nodes;
     uint32_t n_leaves;    // filled by the info kernels only
     uint32_t depth;
@@ -70,8 +71,10 @@ struct DevParams {
     uint32_t fb_hist_done;               // finished tiles of the fallback's histogram phase
     uint32_t fb_plan;                    // bit q: the fallback's digit q is not the same for all keys
     uint32_t fb_done[1 + kFullPasses];   // phase 0 (nt once the plan is set) and finished tiles per pass
-    uint32_t pad[2];
+    uint32_t n_particles;                // particles of the build
+    uint32_t pad;
 };
+constexpr uint32_t kBadIndex = 4u;       // bit of DevParams::bad_input
 static_assert(sizeof(DevParams) == 128, "DevParams layout");
 
 // One tree node, 32 bytes: g = (com.x, com.y, com.z, M),

@@ -48,6 +48,7 @@
 //     the full key: equal keys have equal H, so they are in index order
 //     there, and a stable sort of it by the full key is the sort by
 //     (key, index).
+#include "checked.h"
 #include "orr_internal.h"
 
 namespace orr {
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(256) void k_morton_hist(const float *__restrict__ p
                 prm->side = side;
                 prm->scale = scale;
                 prm->bad_input = bad;
+                prm->n_particles = n;
                 prm->n_nodes = 0;
                 for (int q = 0; q < kRadixPasses; q++) prm->sort_ticket[q] = 0;
                 prm->n_cut = 0;
@@ -428,7 +430,7 @@ __device__ __forceinline__ void sweep_tile(const IO &io, uint32_t n, int shift, 
             if (j < tile_n) {
                 const uint64_t k = s_keys[j];
                 const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
-                if (o < n) io.store_with(o, k, s_vals[j], g[r]);
+                if (guarded_lt(o, n, err)) io.store_with(o, k, s_vals[j], g[r]);
             }
         }
         return;
@@ -437,7 +439,7 @@ __device__ __forceinline__ void sweep_tile(const IO &io, uint32_t n, int shift, 
         const uint64_t k = s_keys[j];
         const uint32_t v = s_vals[j];
         const uint32_t o = s_delta[(uint32_t)(k >> shift) & (kRadixBins - 1)] + j;
-        if (o < n) io.store(o, k, v);  // always, unless a look-back wait gave up (flagged)
+        if (guarded_lt(o, n, err)) io.store(o, k, v);  // always, unless a look-back wait gave up (flagged)
     }
 }
 
@@ -521,9 +523,11 @@ __global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__rest
                 rank += (o < key) | ((o == key) & (i < q));
             }
             const int64_t out = t0 - kFixHalo + s + rank;
-            keys_out[out] = key;
-            vals_out[out] = v;
-            xs[out] = xs0[v];
+            if (checked_lt((uint64_t)out, n, &prm->bad_input)) {
+                keys_out[out] = key;
+                vals_out[out] = v;
+                if (checked_lt(v, n, &prm->bad_input)) xs[out] = xs0[v];
+            }
         } else if (s == q) {
             s_long[atomicAdd(&s_nlong, 1u)] = (uint32_t)p;
         }
@@ -601,10 +605,11 @@ __global__ __launch_bounds__(kFixThreads) void k_sort_fix(const uint64_t *__rest
         }
         for (uint32_t i = t; i < len; i += kFixThreads) {
             const uint32_t src = S + (uint32_t)(s_buf[i] & 0xfffu);
+            if (!checked_lt(src, n, &prm->bad_input)) continue;
             const uint32_t w = vals_in[src];
             keys_out[S + i] = keys_in[src];
             vals_out[S + i] = w;
-            xs[S + i] = xs0[w];
+            if (checked_lt(w, n, &prm->bad_input)) xs[S + i] = xs0[w];
         }
         __syncthreads();  // s_buf and s_end are reused by the next run
     }
@@ -645,6 +650,7 @@ struct FallbackIO {
     const float4 *xs0;
     float4 *xs;
     uint32_t n;  // particles: gathered indices are checked against it
+    uint32_t *err;  // the build's status word (checked build)
     __device__ __forceinline__ uint32_t run_of(uint64_t e) const {  // last r with vb[r] <= e
         uint32_t lo = 0, hi = tb->nr - 1;
         while (lo < hi) {
@@ -664,6 +670,11 @@ struct FallbackIO {
         } else {
             const uint32_t r = run_of(e);
             const uint64_t ph = tb->s[r] + (e - tb->vb[r]);
+            ORR_IF_CHECKED(if (!checked_lt(ph, n, err)) {
+                k = 0ull;
+                v = 0u;
+                return;
+            })
             k = ((uint64_t)r << kSortLowBits) | (ki[ph] & 0x7fffffffull);
             v = vi[ph];
         }
@@ -677,15 +688,17 @@ struct FallbackIO {
         uint64_t ph = o;
         if (!tb->full) {
             const uint32_t r = (uint32_t)(k >> kSortLowBits);
+            ORR_IF_CHECKED(if (!checked_lt(r, tb->nr, err)) return;)
             ph = tb->s[r] + (o - tb->vb[r]);
             k = ((uint64_t)tb->h[r] << kSortLowBits) | (k & 0x7fffffffull);
         }
+        ORR_IF_CHECKED(if (!checked_lt(ph, n, err)) return;)
         ko[ph] = k;
         vo[ph] = v;
-        if (v < n) xs[ph] = xs0[v];
+        if (guarded_lt(v, n, err)) xs[ph] = xs0[v];
     }
     __device__ __forceinline__ bool gathers() const { return dst_out; }
-    __device__ __forceinline__ float4 fetch(uint32_t v) const { return v < n ? xs0[v] : float4{}; }
+    __device__ __forceinline__ float4 fetch(uint32_t v) const { return guarded_lt(v, n, err) ? xs0[v] : float4{}; }
     __device__ __forceinline__ void store_with(uint64_t o, uint64_t k, uint32_t v, float4 g) const {
         if (!dst_out) {
             ko[o] = k;
@@ -695,9 +708,11 @@ struct FallbackIO {
         uint64_t ph = o;
         if (!tb->full) {
             const uint32_t r = (uint32_t)(k >> kSortLowBits);
+            ORR_IF_CHECKED(if (!checked_lt(r, tb->nr, err)) return;)
             ph = tb->s[r] + (o - tb->vb[r]);
             k = ((uint64_t)tb->h[r] << kSortLowBits) | (k & 0x7fffffffull);
         }
+        ORR_IF_CHECKED(if (!checked_lt(ph, n, err)) return;)
         ko[ph] = k;
         vo[ph] = v;
         xs[ph] = g;
@@ -784,7 +799,7 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(const uint64_t *
             // serialise 64 adds).
             for (int k = threadIdx.x; k < kFullPasses * kRadixBins; k += kTileThreads) s_h[k] = 0;
             __syncthreads();
-            const FallbackIO io{&tb, true, false, keys_a, vals_a, nullptr, nullptr, nullptr, nullptr, n};
+            const FallbackIO io{&tb, true, false, keys_a, vals_a, nullptr, nullptr, nullptr, nullptr, n, &prm->bad_input};
             const uint64_t t0 = (uint64_t)tile * kTile;
             const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
             for (uint32_t r = 0; r < kItems; r++) {
@@ -859,7 +874,7 @@ __global__ __launch_bounds__(kTileThreads) void k_sort_fallback(const uint64_t *
                 const uint32_t *vi = slot == 1 ? vals_a : (slot & 1) ? vals_y : vals_x;
                 uint64_t *ko = last ? keys_out : (slot & 1) ? keys_x : keys_y;
                 uint32_t *vo = last ? vals_out : (slot & 1) ? vals_x : vals_y;
-                const FallbackIO io{&tb, slot == 1, last, ki, vi, ko, vo, xs0, xs, n};
+                const FallbackIO io{&tb, slot == 1, last, ki, vi, ko, vo, xs0, xs, n, &prm->bad_input};
                 if (slots == 0) {
                     // Every digit is the same: the input order is the sorted order.
                     const uint64_t t0 = (uint64_t)tile * kTile;

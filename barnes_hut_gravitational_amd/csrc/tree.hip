@@ -29,6 +29,7 @@
 // above the cut. Every node sums in the fixed order (leaf: its particles in
 // sorted order; internal: its children in octant order), so every bit depends
 // only on the tree.
+#include "checked.h"
 #include "orr_internal.h"
 #include "schedule.h"
 
@@ -213,13 +214,15 @@ __device__ uint32_t cell_end(const uint64_t *__restrict__ keys, uint32_t n, uint
 __global__ __launch_bounds__(256) void k_tree_stub(const uint32_t *__restrict__ info,
                                                    const uint32_t *__restrict__ tile_pre,
                                                    const uint32_t *__restrict__ loc, uint32_t n,
-                                                   NodeRec *__restrict__ nodes, uint8_t *__restrict__ level) {
+                                                   NodeRec *__restrict__ nodes, uint8_t *__restrict__ level,
+                                                   uint32_t max_nodes, DevParams *__restrict__ prm) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n) return;
     const uint32_t inf = info[i];
     const int first = (int)(inf & 0xffu), D = (int)(inf >> 8);
     uint32_t node = base_at(tile_pre, loc, i);
     for (int l = first; l <= D; l++, node++) {
+        ORR_IF_CHECKED(if (!checked_lt(node, max_nodes, &prm->bad_input)) break;)
         nodes[node].t.y = i;
         level[node] = (uint8_t)l;
     }
@@ -227,13 +230,14 @@ __global__ __launch_bounds__(256) void k_tree_stub(const uint32_t *__restrict__ 
 
 // Sums of one node, stored for the parent (S, M) and for the walk (com, M).
 __device__ __forceinline__ void store_sums(uint32_t k, float M, float sx, float sy, float sz, uint32_t first,
-                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum) {
+                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum,
+                                           const Check &ck) {
     msum[k] = make_float4(sx, sy, sz, M);
     float4 g;
     if (M > 0.0f) {
         g = make_float4(sx / M, sy / M, sz / M, M);  // correctly rounded divisions
     } else {
-        const float4 p = xs[first];
+        const float4 p = checked_lt(first, ck.n_particles, ck.word) ? xs[first] : float4{};
         g = make_float4(p.x, p.y, p.z, M);
     }
     nodes[k].g = g;
@@ -242,7 +246,7 @@ __device__ __forceinline__ void store_sums(uint32_t k, float M, float sx, float 
 // Leaf: its particles in sorted order (loads issued four at a time, the sums
 // still one particle after the other).
 __device__ __forceinline__ void finish_leaf(uint32_t k, uint32_t first, uint32_t count, const float4 *__restrict__ xs,
-                                            NodeRec *nodes, float4 *msum) {
+                                            NodeRec *nodes, float4 *msum, const Check &ck) {
     float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
     const uint32_t end = first + count;
     for (uint32_t j0 = first; j0 < end; j0 += 4) {
@@ -259,7 +263,7 @@ __device__ __forceinline__ void finish_leaf(uint32_t k, uint32_t first, uint32_t
             }
         }
     }
-    store_sums(k, M, sx, sy, sz, first, xs, nodes, msum);
+    store_sums(k, M, sx, sy, sz, first, xs, nodes, msum, ck);
 }
 
 // One thread per node: its cell end (searched from its first particle), count,
@@ -270,12 +274,15 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
                                                    const uint32_t *__restrict__ loc, DevParams *__restrict__ prm,
                                                    uint32_t max_nodes, NodeRec *nodes,
                                                    const uint8_t *__restrict__ level, uint32_t *__restrict__ top_list,
-                                                   const float4 *__restrict__ xs, float4 *msum) {
+                                                   uint32_t max_top, const float4 *__restrict__ xs, float4 *msum) {
     const uint32_t k = blockIdx.x * 256u + threadIdx.x;
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     if (k >= nn) return;
+    const Check ck{&prm->bad_input, n};
+    ORR_IF_CHECKED(if (!checked_lt(prm->n_nodes, (uint64_t)max_nodes + 1u, ck.word)) return;)
     const int l = level[k];
     const uint32_t i = nodes[k].t.y;
+    ORR_IF_CHECKED(if (!checked_lt(i, n, ck.word)) return;)
     // In preorder a node is a leaf iff the next node is not its first child
     // (level not above its own); a leaf's particles end where the next node's
     // begin, and its escape is the next index. Internal nodes search for the
@@ -290,6 +297,10 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
         end = l == 0 ? n : cell_end(keys, n, i, sh, keys[i] >> sh);
         esc = base_at(tile_pre, loc, end);
     }
+    // a node's particles [i, end) are not empty and lie among the n; its
+    // escape is a node index or the end of the tree
+    ORR_IF_CHECKED(if (!(checked_lt(i, end, ck.word) && checked_lt(end, (uint64_t)n + 1u, ck.word) &&
+                         checked_lt(esc, (uint64_t)nn + 1u, ck.word))) return;)
     const uint32_t count = end - i;
     const float s = ldexpf(prm->side, -l);  // exact
     const float s2 = s * s;
@@ -300,8 +311,11 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
     // a check of its own and still always ends
     nodes[k].t.x = max(esc, k + 1);
     *reinterpret_cast<uint2 *>(&nodes[k].t.z) = make_uint2(count, __float_as_uint(s2));
-    if (count > kCutParticles) top_list[atomicAdd(&prm->n_top, 1u)] = k;
-    if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum);
+    if (count > kCutParticles) {
+        const uint32_t e = atomicAdd(&prm->n_top, 1u);
+        if (checked_lt(e, max_top, ck.word)) top_list[e] = k;
+    }
+    if (esc == k + 1) finish_leaf(k, i, count, xs, nodes, msum, ck);
 }
 
 // Cut nodes (count <= kCutParticles, parent larger or none): the root if no
@@ -310,7 +324,8 @@ __global__ __launch_bounds__(256) void k_tree_ends(const uint64_t *__restrict__ 
 // kids[9e + 1 ..] = their indices in octant order.
 __global__ __launch_bounds__(256) void k_tree_cut(const NodeRec *__restrict__ nodes, DevParams *__restrict__ prm,
                                                   uint32_t max_nodes, const uint32_t *__restrict__ top_list,
-                                                  uint32_t *__restrict__ kids, uint32_t *__restrict__ cut_list) {
+                                                  uint32_t max_top, uint32_t *__restrict__ kids,
+                                                  uint32_t *__restrict__ cut_list) {
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     const uint32_t n_top = prm->n_top;
     if (n_top == 0) {
@@ -321,13 +336,18 @@ __global__ __launch_bounds__(256) void k_tree_cut(const NodeRec *__restrict__ no
         return;
     }
     for (uint32_t e = blockIdx.x * 256u + threadIdx.x; e < n_top; e += gridDim.x * 256u) {
+        ORR_IF_CHECKED(if (!checked_lt(e, max_top, &prm->bad_input)) break;)
         const uint32_t k = top_list[e];
+        ORR_IF_CHECKED(if (!checked_lt(k, nn, &prm->bad_input)) continue;)
         const uint32_t end = min(nodes[k].t.x, nn);
         uint32_t nk = 0;
         for (uint32_t q = k + 1; q < end && nk < 8;) {
             const uint4 tq = nodes[q].t;
             kids[9 * e + 1 + nk++] = q;
-            if (tq.z <= kCutParticles) cut_list[atomicAdd(&prm->n_cut, 1u)] = q;
+            if (tq.z <= kCutParticles) {
+                const uint32_t c = atomicAdd(&prm->n_cut, 1u);
+                if (checked_lt(c, max_nodes, &prm->bad_input)) cut_list[c] = q;
+            }
             q = max(tq.x, q + 1);
         }
         kids[9 * e] = nk;
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(256) void k_tree_cut(const NodeRec *__restrict__ no
 
 // Internal node: its children in octant order, by the escape chain.
 __device__ __forceinline__ void finish_internal(uint32_t k, const uint4 &t, const float4 *__restrict__ xs,
-                                                NodeRec *nodes, float4 *msum) {
+                                                NodeRec *nodes, float4 *msum, const Check &ck) {
     float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
     for (uint32_t q = k + 1; q < t.x; q = max(nodes[q].t.x, q + 1)) {
         const float4 cs = msum[q];
@@ -345,7 +365,7 @@ __device__ __forceinline__ void finish_internal(uint32_t k, const uint4 &t, cons
         sy += cs.y;
         sz += cs.z;
     }
-    store_sums(k, M, sx, sy, sz, t.y, xs, nodes, msum);
+    store_sums(k, M, sx, sy, sz, t.y, xs, nodes, msum, ck);
 }
 
 // Sums of internal node k from its children's, in octant order (escape
@@ -373,6 +393,7 @@ __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ 
                                                      const uint32_t *__restrict__ cut_list,
                                                      const DevParams *__restrict__ prm, uint32_t max_nodes,
                                                      float4 *msum) {
+    const Check ck = make_check(prm);
     __shared__ float4 s_sum[kCutLdsNodes];
     __shared__ uint32_t s_esc[kCutLdsNodes];
     __shared__ uint8_t s_lvl[kCutLdsNodes];
@@ -380,7 +401,11 @@ __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ 
     const uint32_t n_cut = prm->n_cut;
     const uint32_t nn = min(prm->n_nodes, max_nodes);
     for (uint32_t e = blockIdx.x; e < n_cut; e += gridDim.x) {
-        const uint32_t r = cut_list[e];
+        // e and r are the same in the whole work-group: the checks below
+        // leave its barriers in uniform control flow
+        ORR_IF_CHECKED(if (!checked_lt(e, max_nodes, ck.word)) break;)
+        const uint32_t r = __builtin_amdgcn_readfirstlane(cut_list[e]);
+        ORR_IF_CHECKED(if (!checked_lt(r, nn, ck.word)) continue;)
         const uint32_t end = min(max(nodes[r].t.x, r + 1), nn);
         const uint32_t m = end - r;
         const int lmin = level[r];
@@ -411,14 +436,14 @@ __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ 
             for (uint32_t k = threadIdx.x; k < m; k += 256) {
                 if (s_esc[k] == k + 1) continue;
                 const float4 c = s_sum[k];
-                store_sums(r + k, c.w, c.x, c.y, c.z, nodes[r + k].t.y, xs, nodes, msum);
+                store_sums(r + k, c.w, c.x, c.y, c.z, nodes[r + k].t.y, xs, nodes, msum, ck);
             }
         } else {
             for (int l = lmax; l >= lmin; l--) {
                 for (uint32_t k = r + threadIdx.x; k < end; k += 256) {
                     if (level[k] != l) continue;
                     const uint4 t = nodes[k].t;
-                    if (t.x != k + 1) finish_internal(k, t, xs, nodes, msum);
+                    if (t.x != k + 1 && checked_lt(t.x, (uint64_t)nn + 1u, ck.word)) finish_internal(k, t, xs, nodes, msum, ck);
                 }
                 __syncthreads();
             }
@@ -433,11 +458,12 @@ __global__ __launch_bounds__(256) void k_moments_cut(const float4 *__restrict__ 
 constexpr int kTopCached = 4;
 
 __device__ __forceinline__ void finish_top(uint32_t k, uint32_t nk, const uint32_t *kid,
-                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum) {
+                                           const float4 *__restrict__ xs, NodeRec *nodes, float4 *msum,
+                                           uint32_t nn, const Check &ck) {
     float4 cs[8];
 #pragma unroll
     for (uint32_t j = 0; j < 8; j++)
-        if (j < nk) cs[j] = msum[kid[j]];
+        if (j < nk) cs[j] = checked_lt(kid[j], nn, ck.word) ? msum[kid[j]] : float4{};
     float M = 0.0f, sx = 0.0f, sy = 0.0f, sz = 0.0f;
 #pragma unroll
     for (uint32_t j = 0; j < 8; j++) {
@@ -447,7 +473,7 @@ __device__ __forceinline__ void finish_top(uint32_t k, uint32_t nk, const uint32
         sy += cs[j].y;
         sz += cs[j].z;
     }
-    store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum);
+    store_sums(k, M, sx, sy, sz, nodes[k].t.y, xs, nodes, msum, ck);
 }
 
 // k_moments_top: block 0 finishes the moments above the cut; blocks 1..8
@@ -459,7 +485,8 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
                                                       const uint8_t *__restrict__ level,
                                                       const uint32_t *__restrict__ top_list,
                                                       const uint32_t *__restrict__ kids,
-                                                      const DevParams *__restrict__ prm, float4 *msum,
+                                                      const DevParams *__restrict__ prm, uint32_t max_nodes,
+                                                      uint32_t max_top, float4 *msum,
                                                       const uint32_t *__restrict__ wave_cost, uint32_t n_waves,
                                                       uint32_t *__restrict__ wave_order) {
     if (blockIdx.x >= 1) {
@@ -467,7 +494,11 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
         return;
     }
     __shared__ int s_lmin, s_lmax;
-    const uint32_t n_top = prm->n_top;
+    const Check chk = make_check(prm);
+    const uint32_t nn = min(prm->n_nodes, max_nodes);
+    // entries of the list (more than it holds only in a corrupt build, which
+    // the checked build reports and clamps)
+    const uint32_t n_top = checked_lt(prm->n_top, (uint64_t)max_top + 1u, chk.word) ? prm->n_top : max_top;
     if (threadIdx.x == 0) {
         s_lmin = kMaxLevel + 1;
         s_lmax = -1;
@@ -483,7 +514,8 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
         for (int q = 0; q < 8; q++) ckid[j][q] = e < n_top ? kids[9 * e + 1 + q] : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kTopCached; j++) cl[j] = threadIdx.x + 1024u * j < n_top ? (int)level[ck[j]] : -1;
+    for (int j = 0; j < kTopCached; j++)
+        cl[j] = threadIdx.x + 1024u * j < n_top && checked_lt(ck[j], nn, chk.word) ? (int)level[ck[j]] : -1;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kTopCached; j++)
@@ -492,7 +524,9 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
             atomicMax(&s_lmax, cl[j]);
         }
     for (uint32_t e = threadIdx.x + 1024u * kTopCached; e < n_top; e += 1024) {
-        const int l = level[top_list[e]];
+        const uint32_t k = top_list[e];
+        ORR_IF_CHECKED(if (!checked_lt(k, nn, chk.word)) continue;)
+        const int l = level[k];
         atomicMin(&s_lmin, l);
         atomicMax(&s_lmax, l);
     }
@@ -500,14 +534,14 @@ __global__ __launch_bounds__(1024) void k_moments_top(const float4 *__restrict__
     for (int l = s_lmax; l >= s_lmin; l--) {
 #pragma unroll
         for (int j = 0; j < kTopCached; j++)
-            if (cl[j] == l && cnk[j] != 0) finish_top(ck[j], cnk[j], ckid[j], xs, nodes, msum);
+            if (cl[j] == l && cnk[j] != 0) finish_top(ck[j], cnk[j], ckid[j], xs, nodes, msum, nn, chk);
         for (uint32_t e = threadIdx.x + 1024u * kTopCached; e < n_top; e += 1024) {
             const uint32_t k = top_list[e];
             const uint32_t nk = kids[9 * e];
-            if (level[k] != l || nk == 0) continue;  // other level, or a leaf (done)
+            if (!checked_lt(k, nn, chk.word) || level[k] != l || nk == 0) continue;  // other level, or a leaf (done)
             uint32_t kid[8];
             for (uint32_t q = 0; q < 8; q++) kid[q] = q < nk ? kids[9 * e + 1 + q] : 0u;
-            finish_top(k, nk, kid, xs, nodes, msum);
+            finish_top(k, nk, kid, xs, nodes, msum, nn, chk);
         }
         __syncthreads();
     }
@@ -555,10 +589,12 @@ hipError_t launch_build(const Workspace &ws, hipStream_t s) {
     k_tree_count<<<scan_tiles, 256, 0, s>>>(ws.keys[0], n, (uint32_t)ws.leaf_cap, ws.info, ws.base, ws.tile_sum,
                                             ws.wave_cost);
     k_tile_scan<<<1, 1024, 0, s>>>(ws.tile_sum, scan_tiles, ws.prm);
-    k_tree_stub<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.tile_sum, ws.base, n, ws.nodes, ws.level);
+    k_tree_stub<<<(unsigned)ceil_div(ws.n, 256), 256, 0, s>>>(ws.info, ws.tile_sum, ws.base, n, ws.nodes, ws.level,
+                                                              (uint32_t)ws.max_nodes, ws.prm);
     k_tree_ends<<<node_blocks, 256, 0, s>>>(ws.keys[0], n, ws.tile_sum, ws.base, ws.prm, (uint32_t)ws.max_nodes,
-                                            ws.nodes, ws.level, ws.top_list, ws.xs, ws.msum);
-    k_tree_cut<<<64, 256, 0, s>>>(ws.nodes, ws.prm, (uint32_t)ws.max_nodes, ws.top_list, ws.kids, ws.cut_list);
+                                            ws.nodes, ws.level, ws.top_list, (uint32_t)ws.max_top, ws.xs, ws.msum);
+    k_tree_cut<<<64, 256, 0, s>>>(ws.nodes, ws.prm, (uint32_t)ws.max_nodes, ws.top_list, (uint32_t)ws.max_top,
+                                  ws.kids, ws.cut_list);
     return hipGetLastError();
 }
 
@@ -570,8 +606,9 @@ hipError_t launch_moments(const Workspace &ws, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<int64_t>(4096, std::max<int64_t>(1, ceil_div(ws.n, kCutParticles) * 64));
     k_moments_cut<<<blocks, 256, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.cut_list, ws.prm, (uint32_t)ws.max_nodes,
                                          ws.msum);
-    k_moments_top<<<9, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm, ws.msum,
-                                     ws.wave_cost, (uint32_t)ws.n_waves, ws.wave_order);
+    k_moments_top<<<9, 1024, 0, s>>>(ws.xs, ws.nodes, ws.level, ws.top_list, ws.kids, ws.prm,
+                                     (uint32_t)ws.max_nodes, (uint32_t)ws.max_top, ws.msum, ws.wave_cost,
+                                     (uint32_t)ws.n_waves, ws.wave_order);
     return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "checked.h"
 #include "orr_internal.h"
 #include "term.h"
 #include "schedule.h"
@@ -87,7 +88,8 @@ template <int kInv, bool kOff32, bool kMin, bool kPow2, uint32_t kSplit>
 __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                               const uint32_t *__restrict__ perm, uint32_t i, uint32_t part,
                                               uint32_t n, uint32_t n_nodes, float eps2, float theta2,
-                                              uint32_t s2_shift, const WalkOut &out, WalkLds &lds) {
+                                              uint32_t s2_shift, const WalkOut &out, WalkLds &lds,
+                                              const Check &ck) {
     static_assert(kSplit == 1 || kSplit == 2 || kSplit == 4 || kSplit == 8 || kSplit == 16, "split");
     constexpr uint32_t kOwn = 64u / kSplit;  // lanes whose terms this wave adds
     const uint64_t own_mask = kSplit == 1 ? ~0ull : ((1ull << kOwn) - 1ull) << (part * kOwn);
@@ -110,6 +112,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         const NodeRec nd = kOff32 ? *reinterpret_cast<const NodeRec *>(node_bytes + (c << 5)) : nodes[c];
         const uint32_t esc = nd.t.x;  // > c: the build stores escape = max(escape, index + 1)
         const uint32_t c1 = c + 1;
+        ORR_IF_CHECKED(if (!escape_ok(c, esc, n_nodes, ck.word)) break;)  // wave-uniform
         // A lane that did not accept at the wave's previous node wants exactly
         // the node the wave visits next (it opened that node, so it wants the
         // node after it, which is the smallest index any lane can want), so
@@ -145,7 +148,7 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
         if (m_open) {
             nopen = add_lane_bit(nopen, m_open);
             const uint64_t m_mine = m_open & own_mask;  // the opening lanes whose terms this wave adds
-            if (esc == c1 && m_mine) {  // a leaf that some own lane opens
+            if (esc == c1 && m_mine && leaf_ok(nd.t.y, nd.t.z, ck)) {  // a leaf that some own lane opens
                 const uint32_t b = nd.t.y, cnt = nd.t.z;
                 leaf_terms<kInv>(xs, b, cnt, m_mine, opening, xi, eps2, ax, ay, az, lds, wv);
                 if (opening) pp += cnt - ((i - b) < cnt ? 1u : 0u);
@@ -162,7 +165,10 @@ __device__ __forceinline__ void walk_coherent(const float4 *__restrict__ xs, con
             c = m_open ? c1 : esc;
         }
     }
-    if (valid && own) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
+    if (valid && own) {
+        const uint32_t dst = perm[i];
+        if (checked_lt(dst, ck.n_particles, ck.word)) write_out(out, dst, ax, ay, az, pc + nopen, steps, pp, pc);
+    }
 }
 
 // The walk schedule (which waves each XCD runs, longest first) is computed
@@ -190,8 +196,9 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(kSpl
     // the scaled comparison only in the production variant (uniform branches)
     constexpr bool kScaled = kOff32 && !kMin;
     const bool pow2 = kScaled && pow2_scale_ok(prm, theta2_exp);
+    const Check ck = make_check(prm);
 #define ORR_WALK(INV, POW2) \
-    walk_coherent<INV, kOff32, kMin, POW2, kSplit>(xs, nodes, perm, i, part, n, n_nodes, eps2, theta2, sh, out, lds)
+    walk_coherent<INV, kOff32, kMin, POW2, kSplit>(xs, nodes, perm, i, part, n, n_nodes, eps2, theta2, sh, out, lds, ck)
     if (r2_cannot_overflow(prm, eps2)) {
         if (pow2)
             ORR_WALK(kInvFastNoClamp, kScaled);
@@ -209,13 +216,14 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(kSpl
 template <int kInv>
 __device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                                  const uint32_t *__restrict__ perm, uint32_t i, uint32_t n_nodes,
-                                                 float eps2, float theta2, const WalkOut &out) {
+                                                 float eps2, float theta2, const WalkOut &out, const Check &ck) {
     const float4 xi = xs[i];
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
     uint32_t vown = 0, pp = 0, pc = 0;
     uint32_t c = 0;
     while (c < n_nodes) {
         const NodeRec nd = nodes[c];
+        ORR_IF_CHECKED(if (!escape_ok(c, nd.t.x, n_nodes, ck.word)) break;)
         const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
         const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
         const float d2 = (dx * dx + dy * dy) + dz * dz;
@@ -226,17 +234,20 @@ __device__ __forceinline__ void walk_independent(const float4 *__restrict__ xs, 
             c = esc;
         } else if (esc == c + 1) {
             const uint32_t b = nd.t.y, cnt = nd.t.z;
-            for (uint32_t j = b; j < b + cnt; j++) {
-                const float4 p = xs[j];
-                add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+            if (leaf_ok(b, cnt, ck)) {
+                for (uint32_t j = b; j < b + cnt; j++) {
+                    const float4 p = xs[j];
+                    add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                }
+                pp += cnt - ((i - b) < cnt ? 1u : 0u);
             }
-            pp += cnt - ((i - b) < cnt ? 1u : 0u);
             c = esc;
         } else {
             c = c + 1;
         }
     }
-    write_out(out, perm[i], ax, ay, az, vown, vown, pp, pc);
+    const uint32_t dst = perm[i];
+    if (checked_lt(dst, ck.n_particles, ck.word)) write_out(out, dst, ax, ay, az, vown, vown, pp, pc);
 }
 
 __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *__restrict__ xs,
@@ -248,10 +259,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_independent(const float4 *_
     const uint32_t i = first + xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     if (i >= n) return;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
+    const Check ck = make_check(prm);
     if (r2_cannot_overflow(prm, eps2))
-        walk_independent<kInvFastNoClamp>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
+        walk_independent<kInvFastNoClamp>(xs, nodes, perm, i, n_nodes, eps2, theta2, out, ck);
     else
-        walk_independent<kInvFast>(xs, nodes, perm, i, n_nodes, eps2, theta2, out);
+        walk_independent<kInvFast>(xs, nodes, perm, i, n_nodes, eps2, theta2, out, ck);
 }
 
 // Self-check over the float bit patterns [first, first + count): the cube of

@@ -3,6 +3,7 @@
 // sub-group width" of the performance page), and the descend-together walk
 // that ADR-0029 rejects ("Alternatives considered"). Both use per-lane vector
 // loads; the production walks are in walk.hip.
+#include "checked.h"
 #include "orr_internal.h"
 #include "term.h"
 #include "walk_common.h"
@@ -28,7 +29,8 @@ namespace {
 template <uint32_t kW, bool kDescend, int kInv>
 __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                              const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
-                                             uint32_t n_nodes, float eps2, float theta2, const WalkOut &out) {
+                                             uint32_t n_nodes, float eps2, float theta2, const WalkOut &out,
+                                             const Check &ck) {
     static_assert(kW >= 1 && kW <= 64 && (kW & (kW - 1)) == 0, "group width");
     const bool valid = i < n;
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -42,6 +44,10 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
         if (c < n_nodes) {
             steps += 1;
             const NodeRec nd = nodes[c];
+            ORR_IF_CHECKED(if (!escape_ok(c, nd.t.x, n_nodes, ck.word)) {  // the same in the whole group
+                c = n_nodes;
+                continue;
+            })
             const uint32_t esc = max(nd.t.x, c + 1);  // a well-formed tree has escape > c; never step back
             const float dx = nd.g.x - xi.x, dy = nd.g.y - xi.y, dz = nd.g.z - xi.z;
             const float d2 = (dx * dx + dy * dy) + dz * dz;
@@ -54,7 +60,7 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
                 if ((opening >> first) & gmask) {
                     if (valid) {
                         nopen += 1;
-                        if (esc == c + 1) {
+                        if (esc == c + 1 && leaf_ok(nd.t.y, nd.t.z, ck)) {
                             const uint32_t b = nd.t.y, cnt = nd.t.z;
                             for (uint32_t j = b; j < b + cnt; j++) {
                                 const float4 p = xs[j];
@@ -83,11 +89,13 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
                 nopen += 1;
                 if (esc == c + 1) {  // an opened leaf: its particles in sorted order
                     const uint32_t b = nd.t.y, cnt = nd.t.z;
-                    for (uint32_t j = b; j < b + cnt; j++) {
-                        const float4 p = xs[j];
-                        add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                    if (leaf_ok(b, cnt, ck)) {
+                        for (uint32_t j = b; j < b + cnt; j++) {
+                            const float4 p = xs[j];
+                            add_term<kInv>(p.w, p.x - xi.x, p.y - xi.y, p.z - xi.z, eps2, ax, ay, az);
+                        }
+                        pp += cnt - ((i - b) < cnt ? 1u : 0u);
                     }
-                    pp += cnt - ((i - b) < cnt ? 1u : 0u);
                     next = esc;
                 } else {
                     next = c + 1;
@@ -100,7 +108,10 @@ __device__ __forceinline__ void walk_grouped(const float4 *__restrict__ xs, cons
             c = ((down >> first) & gmask) ? c + 1 : esc;
         }
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
+    if (valid) {
+        const uint32_t dst = perm[i];
+        if (checked_lt(dst, ck.n_particles, ck.word)) write_out(out, dst, ax, ay, az, pc + nopen, steps, pp, pc);
+    }
 }
 
 template <uint32_t kW, bool kDescend>
@@ -112,10 +123,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk_grouped(const float4 *__res
                                                              WalkOut out) {
     const uint32_t i = xcd_block(blockIdx.x, gridDim.x) * kWalkBlock + threadIdx.x;
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
+    const Check ck = make_check(prm);
     if (r2_cannot_overflow(prm, eps2))
-        walk_grouped<kW, kDescend, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_grouped<kW, kDescend, kInvFastNoClamp>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, ck);
     else
-        walk_grouped<kW, kDescend, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out);
+        walk_grouped<kW, kDescend, kInvFast>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, out, ck);
 }
 
 }  // namespace

@@ -23,6 +23,7 @@
 // order with the operations of term.h, so acc, visits_own, n_pp and n_pc are
 // those of the 64-lane walk bit for bit; visits_stepped is the size of the
 // union over the target's group of the given width.
+#include "checked.h"
 #include "orr_internal.h"
 #include "term.h"
 #include "schedule.h"
@@ -52,7 +53,7 @@ template <int kInv, bool kPow2>
 __device__ __forceinline__ void walk_halves(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                             const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
                                             uint32_t n_nodes, float eps2, float theta2, uint32_t s2_shift,
-                                            const WalkOut &out, WalkLds &lds) {
+                                            const WalkOut &out, WalkLds &lds, const Check &ck) {
     constexpr uint64_t kLo = 0x00000000ffffffffull, kHi = ~kLo;
     const bool valid = i < n;
     const bool hi = __lane_id() >= 32u;
@@ -95,7 +96,7 @@ __device__ __forceinline__ void walk_halves(const float4 *__restrict__ xs, const
             for (uint32_t h = 0; h < 2u; h++) {
                 const uint64_t m_h = m_open & (h ? kHi : kLo);
                 const uint32_t esc_h = h ? b.t.x : a.t.x, c_h = h ? c_hi : c_lo;
-                if (m_h && esc_h == c_h + 1u) {
+                if (m_h && esc_h == c_h + 1u && leaf_ok(h ? b.t.y : a.t.y, h ? b.t.z : a.t.z, ck)) {
                     const uint32_t lb = h ? b.t.y : a.t.y, lc = h ? b.t.z : a.t.z;
                     const bool mine = opening && (hi == (h == 1u));
                     leaf_terms<kInv>(xs, lb, lc, m_h, mine, xi, eps2, ax, ay, az, lds, wv);
@@ -103,11 +104,19 @@ __device__ __forceinline__ void walk_halves(const float4 *__restrict__ xs, const
                 }
             }
         }
-        // per half: c + 1 if a lane of the half opened c, else the escape
+        // per half: c + 1 if a lane of the half opened c, else the escape (a
+        // half ends at a bad escape in the checked build)
+        ORR_IF_CHECKED(const bool bad_lo = run_lo && !escape_ok(c_lo, a.t.x, n_nodes, ck.word);
+                       const bool bad_hi = run_hi && !escape_ok(c_hi, b.t.x, n_nodes, ck.word);)
         if (run_lo) c_lo = (m_open & kLo) ? c_lo + 1u : a.t.x;
         if (run_hi) c_hi = (m_open & kHi) ? c_hi + 1u : b.t.x;
+        ORR_IF_CHECKED(if (bad_lo) c_lo = n_nodes; if (bad_hi) c_hi = n_nodes;)
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, hi ? steps_hi : steps_lo, pp, pc);
+    if (valid) {
+        const uint32_t dst = perm[i];
+        if (checked_lt(dst, ck.n_particles, ck.word))
+            write_out(out, dst, ax, ay, az, pc + nopen, hi ? steps_hi : steps_lo, pp, pc);
+    }
 }
 
 // Waves in the production walk's schedule (each wave 64 consecutive sorted
@@ -129,13 +138,14 @@ __global__ __launch_bounds__(kWalkBlock) __attribute__((amdgpu_waves_per_eu(6, 6
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const uint32_t sh = theta2_exp << 23;
     const bool pow2 = pow2_scale_ok(prm, theta2_exp);
+    const Check ck = make_check(prm);
     if (r2_cannot_overflow(prm, eps2)) {
         if (pow2)
-            walk_halves<kInvFastNoClamp, true>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds);
+            walk_halves<kInvFastNoClamp, true>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds, ck);
         else
-            walk_halves<kInvFastNoClamp, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds);
+            walk_halves<kInvFastNoClamp, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds, ck);
     } else {
-        walk_halves<kInvFast, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds);
+        walk_halves<kInvFast, false>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds, ck);
     }
 }
 
@@ -149,7 +159,8 @@ template <int kInv, bool kPow2, uint32_t kTeam>
 __device__ __forceinline__ void walk_team(const float4 *__restrict__ xs, const NodeRec *__restrict__ nodes,
                                           const uint32_t *__restrict__ perm, uint32_t i, uint32_t n,
                                           uint32_t n_nodes, float eps2, float theta2, uint32_t s2_shift,
-                                          const WalkOut &out, WalkLdsT<kTeam> &lds, volatile uint32_t *flags) {
+                                          const WalkOut &out, WalkLdsT<kTeam> &lds, volatile uint32_t *flags,
+                                          const Check &ck) {
     const bool valid = i < n;
     const float4 xi = valid ? xs[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     uint32_t next = valid ? 0u : n_nodes;
@@ -178,7 +189,7 @@ __device__ __forceinline__ void walk_team(const float4 *__restrict__ xs, const N
         const bool opening = active && !far;
         if (m_open) {
             nopen = add_lane_bit(nopen, m_open);
-            if (esc == c1) {
+            if (esc == c1 && leaf_ok(nd.t.y, nd.t.z, ck)) {
                 leaf_terms<kInv>(xs, nd.t.y, nd.t.z, m_open, opening, xi, eps2, ax, ay, az, lds, wv);
                 if (opening) pp += nd.t.z - ((i - nd.t.y) < nd.t.z ? 1u : 0u);
             }
@@ -189,11 +200,19 @@ __device__ __forceinline__ void walk_team(const float4 *__restrict__ xs, const N
             if (wv == 0u) flags[slot1] = 0u;
         }
         __syncthreads();
-        const uint32_t any = flags[slot];
-        c = any ? c1 : esc;
+        // the same word for every lane: readfirstlane makes the loop's exit
+        // uniform for the compiler too, so its barrier stays in uniform
+        // control flow
+        const uint32_t any = __builtin_amdgcn_readfirstlane(flags[slot]);
+        // every wave reads the same record, so all end together at a bad
+        // escape (checked build)
+        c = !escape_ok(c, esc, n_nodes, ck.word) ? n_nodes : any ? c1 : esc;
         slot = slot1;
     }
-    if (valid) write_out(out, perm[i], ax, ay, az, pc + nopen, steps, pp, pc);
+    if (valid) {
+        const uint32_t dst = perm[i];
+        if (checked_lt(dst, ck.n_particles, ck.word)) write_out(out, dst, ax, ay, az, pc + nopen, steps, pp, pc);
+    }
 }
 
 template <uint32_t kTeam>
@@ -209,17 +228,18 @@ __global__ __launch_bounds__(64 * kTeam) __attribute__((amdgpu_waves_per_eu(8, 8
     const uint32_t n_nodes = min(prm->n_nodes, max_nodes);
     const uint32_t sh = theta2_exp << 23;
     const bool pow2 = pow2_scale_ok(prm, theta2_exp);
+    const Check ck = make_check(prm);
     if (threadIdx.x < 3u) flags[threadIdx.x] = 0u;
     __syncthreads();
     if (r2_cannot_overflow(prm, eps2)) {
         if (pow2)
             walk_team<kInvFastNoClamp, true, kTeam>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds,
-                                                   flags);
+                                                   flags, ck);
         else
             walk_team<kInvFastNoClamp, false, kTeam>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds,
-                                                    flags);
+                                                    flags, ck);
     } else {
-        walk_team<kInvFast, false, kTeam>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds, flags);
+        walk_team<kInvFast, false, kTeam>(xs, nodes, perm, i, n, n_nodes, eps2, theta2, sh, out, lds, flags, ck);
     }
 }
 

@@ -14,7 +14,10 @@ from dataclasses import dataclass
 import torch  # loaded before liborr so both share one HIP runtime
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liborr.so")
+# ORR_CHECKED=1 loads the checked build (the same ABI, with every index a
+# kernel takes from device data tested; a failed test makes the next
+# synchronising call return ORR_ERR_HIP).
+LIB_PATH = os.path.join(_HERE, "liborr_checked.so" if os.environ.get("ORR_CHECKED") == "1" else "liborr.so")
 
 (ORR_OK, ORR_ERR_INVALID_ARG, ORR_ERR_RANGE, ORR_ERR_NONFINITE, ORR_ERR_HIP, ORR_ERR_WORKSPACE,
  ORR_ERR_HOST_MEMORY) = range(7)

@@ -36,6 +36,20 @@ def test_library_exports_every_declared_symbol():
     assert set(declared()) <= syms
 
 
+def test_checked_build_exports_the_same_symbols():
+    """The checked build (device index checks) is the same ABI: every
+    declared entry point, loaded without a GPU call."""
+    from barnes_hut_gravitational_amd import build_lib
+
+    assert os.path.exists(build_lib.CHECKED_LIB), "run __graft_entry__.build()"
+    out = subprocess.run(["nm", "-D", "--defined-only", build_lib.CHECKED_LIB], capture_output=True, text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    assert set(declared()) <= syms
+    L = ctypes.CDLL(build_lib.CHECKED_LIB)
+    L.orr_abi_version.restype = ctypes.c_int
+    assert L.orr_abi_version() == orr.abi_version()
+
+
 def test_static_strings_and_version():
     L = orr.lib()
     assert orr.abi_version() == 2
