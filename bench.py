@@ -111,7 +111,7 @@ def walk_traffic_bytes():
     try:
         fields = dict(l.split(": ", 1) for l in open(prof).read().splitlines()[:5] if ": " in l)
         h = hashlib.sha256()
-        for name in ("walk.hip", "walk_common.h", "walk_leaf.h", "term.h", "schedule.h"):  # the walk and what it inlines
+        for name in ("walk.hip", "walk_common.h", "walk_leaf.h", "term.h", "schedule.h", "checked.h"):  # the walk and what it inlines
             h.update(open(os.path.join(csrc, name), "rb").read())
         digest = h.hexdigest()[:16]
         if fields.get("walk-source-sha256-16", "").strip() == digest:
