@@ -120,14 +120,23 @@ struct orr_tree {
 
 namespace {
 
+// Node indices, escapes and node counts are 32-bit on the device, so the
+// workspace's node bound must stay below 2^32 (it does for every n <=
+// ORR_MAX_N at leaf capacities of 20 and more; at capacity 1 up to about 373
+// million particles).
+bool node_bound_fits(int64_t n, int32_t leaf_cap) { return max_nodes_for(n, leaf_cap) <= (int64_t)0xffffffffll; }
+
 bool valid_sizes(int64_t n, int32_t leaf_cap) {
-    return n >= 1 && n <= ORR_MAX_N && leaf_cap >= 1 && leaf_cap <= ORR_MAX_LEAF_CAP;
+    return n >= 1 && n <= ORR_MAX_N && leaf_cap >= 1 && leaf_cap <= ORR_MAX_LEAF_CAP && node_bound_fits(n, leaf_cap);
 }
 
 orr_status check_sizes(int64_t n, int32_t leaf_cap) {
     if (n < 1 || n > ORR_MAX_N) return fail(ORR_ERR_RANGE, "n = %lld is outside [1, %lld]", (long long)n, ORR_MAX_N);
     if (leaf_cap < 1 || leaf_cap > ORR_MAX_LEAF_CAP)
         return fail(ORR_ERR_RANGE, "leaf_cap = %d is outside [1, %d]", leaf_cap, ORR_MAX_LEAF_CAP);
+    if (!node_bound_fits(n, leaf_cap))
+        return fail(ORR_ERR_RANGE, "n = %lld at leaf_cap = %d allows more than 2^32 - 1 nodes (32-bit node indices)",
+                    (long long)n, leaf_cap);
     return ORR_OK;
 }
 

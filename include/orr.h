@@ -147,7 +147,12 @@ const char *orr_last_error(void);
 
 /* Workspace bytes needed for n particles at this leaf capacity; 0 if the
  * arguments are out of range. Needs no GPU. The bound allows n leaves plus,
- * on each of the 21 split levels, n / (leaf_cap + 1) internal nodes. */
+ * on each of the 21 split levels, n / (leaf_cap + 1) internal nodes. Node
+ * indices are 32-bit, so that bound, n + 21 floor(n / (leaf_cap + 1)) + 1,
+ * must not exceed 2^32 - 1: no limit below ORR_MAX_N at leaf capacities of
+ * 20 and more, about 373 million particles at leaf capacity 1. Sizes beyond
+ * it are out of range here and ORR_ERR_RANGE for every entry point that
+ * takes n and leaf_cap. */
 size_t orr_workspace_bytes(int64_t n, int32_t leaf_cap);
 
 /* Enqueue the tree build: root cube, keys, sort, gather, topology, escape
@@ -155,7 +160,8 @@ size_t orr_workspace_bytes(int64_t n, int32_t leaf_cap);
  * handle (free with orr_tree_free) that refers to the workspace and stream.
  * Errors: ORR_ERR_INVALID_ARG (null pos/mass/workspace/out, workspace not
  * 256-byte aligned), ORR_ERR_RANGE (n < 1 or n > ORR_MAX_N, leaf_cap < 1 or
- * > ORR_MAX_LEAF_CAP), ORR_ERR_WORKSPACE, ORR_ERR_HIP. */
+ * > ORR_MAX_LEAF_CAP, or a node bound beyond 32-bit indices: see
+ * orr_workspace_bytes), ORR_ERR_WORKSPACE, ORR_ERR_HIP. */
 orr_status orr_build_tree(const float *pos, const float *mass, int64_t n, int32_t leaf_cap,
                           void *workspace, size_t workspace_bytes, void *hip_stream, orr_tree **out);
 

@@ -71,6 +71,37 @@ def test_workspace_bytes():
     assert orr.workspace_bytes(1000, 32) < orr.workspace_bytes(2000, 32)
 
 
+def node_bound(n, cap):
+    return n + 21 * (n // (cap + 1)) + 1
+
+
+@pytest.mark.parametrize("cap", [1, 2, 8, 19])
+def test_node_bound_limited_to_32_bit_indices(cap):
+    """Node indices are 32-bit on the device: the largest n whose node bound
+    n + 21 floor(n / (cap + 1)) + 1 is at most 2^32 - 1 is accepted and the
+    next one refused, by the size query and by the entry points, before any
+    device work. From leaf capacity 20 on, every n up to ORR_MAX_N fits."""
+    lo, hi = 1, 2**31 - 1
+    while lo < hi:  # the largest n whose bound fits
+        m = (lo + hi + 1) // 2
+        lo, hi = (m, hi) if node_bound(m, cap) <= 2**32 - 1 else (lo, m - 1)
+    assert node_bound(lo, cap) <= 2**32 - 1 < node_bound(lo + 1, cap)
+    assert orr.workspace_bytes(lo, cap) > 0
+    assert orr.workspace_bytes(lo + 1, cap) == 0
+    st, msg = _eval(n=lo + 1, cap=cap)
+    assert st == orr.ORR_ERR_RANGE and "32-bit node indices" in msg
+    h = ctypes.c_void_p()
+    assert orr.lib().orr_build_tree(1, 1, lo + 1, cap, 256, 1 << 30, None, ctypes.byref(h)) == orr.ORR_ERR_RANGE
+    assert h.value is None
+    if cap == 1:
+        assert lo == 373_475_417
+
+
+def test_no_node_bound_limit_from_leaf_capacity_20():
+    assert node_bound(2**31 - 1, 20) <= 2**32 - 1
+    assert orr.workspace_bytes(2**31 - 1, 20) > 0
+
+
 def _eval(**kw):
     L = orr.lib()
     args = dict(pos=1, mass=1, n=100, eps=0.05, theta=0.5, cap=32, tr=1, ws=256, ws_bytes=1 << 30)
