@@ -50,6 +50,8 @@ int main(void) {
         for (size_t b = 0; b < sizeof caps / sizeof caps[0]; b++) {
             size_t w = orr_workspace_bytes(ns[a], caps[b]);
             int ok = ns[a] >= 1 && ns[a] <= ORR_MAX_N && caps[b] >= 1 && caps[b] <= ORR_MAX_LEAF_CAP;
+            /* node indices are 32-bit: n + 21 floor(n / (cap + 1)) + 1 < 2^32 */
+            if (ok && ns[a] + 21 * (ns[a] / (caps[b] + 1)) + 1 > 4294967295LL) ok = 0;
             if ((w != 0) != ok) {
                 fprintf(stderr, "workspace_bytes(%lld, %d) = %zu\n", (long long)ns[a], caps[b], w);
                 failures++;
