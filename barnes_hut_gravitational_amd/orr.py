@@ -136,6 +136,33 @@ def _as_inputs(pos, mass):
     return pos.contiguous(), mass.contiguous()
 
 
+def _device_tensor(t, name, dtype, shape, device):
+    """t as the kernels will write it: a contiguous tensor of this dtype and
+    shape in the memory of `device`. The C ABI takes bare device pointers and
+    cannot check them; a host tensor or a short one here would be a bad
+    device address."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise OrrError(ORR_ERR_INVALID_ARG, f"{name} must be a tensor on {device}")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise OrrError(ORR_ERR_INVALID_ARG, f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} "
+                                            f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise OrrError(ORR_ERR_INVALID_ARG, f"{name} must be contiguous")
+    return t
+
+
+def _workspace(workspace, n, leaf_cap, device):
+    """(tensor, bytes): a caller's workspace, checked to lie contiguous on
+    `device`, or a new one."""
+    if workspace is None:
+        workspace = new_workspace(n, leaf_cap, device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.device != device:
+        raise OrrError(ORR_ERR_INVALID_ARG, f"workspace must be a tensor on {device}")
+    if not workspace.is_contiguous():
+        raise OrrError(ORR_ERR_INVALID_ARG, "workspace must be contiguous")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def new_workspace(n: int, leaf_cap: int, device) -> torch.Tensor:
     nbytes = workspace_bytes(n, leaf_cap)
     if nbytes == 0:
@@ -153,9 +180,20 @@ class Result:
     timings: dict | None
 
 
-def _outputs(n, device):
-    acc = torch.empty((n, 3), dtype=torch.float32, device=device)
-    cnt = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(4)]
+def _outputs(n, device, out=None):
+    """(acc, [visits_own, visits_stepped, n_pp, n_pc]): new tensors, or the
+    caller's `out` in that layout, checked (any entry may be None: that
+    output is not written)."""
+    if out is None:
+        acc = torch.empty((n, 3), dtype=torch.float32, device=device)
+        cnt = [torch.empty(n, dtype=torch.int32, device=device) for _ in range(4)]
+        return acc, cnt
+    acc, cnt = out
+    if len(cnt) != 4:
+        raise OrrError(ORR_ERR_INVALID_ARG, "out must be (acc, [visits_own, visits_stepped, n_pp, n_pc])")
+    acc = None if acc is None else _device_tensor(acc, "acc", torch.float32, (n, 3), device)
+    cnt = [None if c is None else _device_tensor(c, f"counter {k}", torch.int32, (n,), device)
+           for k, c in enumerate(cnt)]
     return acc, cnt
 
 
@@ -165,12 +203,11 @@ def orr_eval_forces(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, traversal="c
     int32 tensors holding the uint32 values."""
     pos, mass = _as_inputs(pos, mass)
     n = pos.shape[0]
-    if workspace is None:
-        workspace = new_workspace(n, leaf_cap, pos.device)
-    acc, cnt = out if out is not None else _outputs(n, pos.device)
+    workspace, ws_bytes = _workspace(workspace, n, leaf_cap, pos.device)
+    acc, cnt = _outputs(n, pos.device, out)
     tm = Timings() if timings else None
     st = lib().orr_eval_forces(_ptr(pos), _ptr(mass), n, eps, theta, leaf_cap, TRAVERSALS[traversal],
-                               _ptr(acc), *[_ptr(c) for c in cnt], _ptr(workspace), workspace.numel(),
+                               _ptr(acc), *[_ptr(c) for c in cnt], _ptr(workspace), ws_bytes,
                                _stream(pos.device), ctypes.byref(tm) if tm is not None else None)
     _check(st)
     return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], tm.as_dict() if tm is not None else None)
@@ -183,7 +220,7 @@ def orr_eval_forces_noalloc(pos, mass, *, eps=0.05, theta=0.5, leaf_cap=32, trav
     allocated here only when `out` is not given."""
     pos, mass = _as_inputs(pos, mass)
     n = pos.shape[0]
-    acc, cnt = out if out is not None else _outputs(n, pos.device)
+    acc, cnt = _outputs(n, pos.device, out)
     _check(lib().orr_eval_forces_noalloc(_ptr(pos), _ptr(mass), n, eps, theta, leaf_cap, TRAVERSALS[traversal],
                                          _ptr(acc), *[_ptr(c) for c in cnt], _stream(pos.device)))
     return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
@@ -193,7 +230,10 @@ def orr_workspace_check(workspace: torch.Tensor) -> None:
     """Raise if the most recent evaluation in this workspace had non-finite
     input or an invalid sort (orr_workspace_check); synchronises the current
     stream."""
-    _check(lib().orr_workspace_check(_ptr(workspace), workspace.numel(), _stream(workspace.device)))
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise OrrError(ORR_ERR_INVALID_ARG, "workspace must be a contiguous GPU tensor")
+    _check(lib().orr_workspace_check(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(workspace.device)))
 
 
 def orr_direct_forces(pos, mass, *, eps=0.05, out=None) -> torch.Tensor:
@@ -201,7 +241,8 @@ def orr_direct_forces(pos, mass, *, eps=0.05, out=None) -> torch.Tensor:
     returns acc [n, 3] in caller order."""
     pos, mass = _as_inputs(pos, mass)
     n = pos.shape[0]
-    acc = out if out is not None else torch.empty((n, 3), dtype=torch.float32, device=pos.device)
+    acc = (torch.empty((n, 3), dtype=torch.float32, device=pos.device) if out is None
+           else _device_tensor(out, "out", torch.float32, (n, 3), pos.device))
     _check(lib().orr_direct_forces(_ptr(pos), _ptr(mass), n, eps, _ptr(acc), _stream(pos.device)))
     return acc
 
@@ -214,7 +255,8 @@ def orr_direct_forces_targets(pos, mass, targets, *, eps=0.05, out=None) -> torc
         raise OrrError(ORR_ERR_INVALID_ARG, "targets must be a 1-d int64 GPU tensor")
     targets = targets.contiguous()
     m = targets.shape[0]
-    acc = out if out is not None else torch.empty((m, 3), dtype=torch.float32, device=pos.device)
+    acc = (torch.empty((m, 3), dtype=torch.float32, device=pos.device) if out is None
+           else _device_tensor(out, "out", torch.float32, (m, 3), pos.device))
     if m == 0:
         return acc
     _check(lib().orr_direct_forces_targets(_ptr(pos), _ptr(mass), pos.shape[0], eps, _ptr(targets), m, _ptr(acc),
@@ -231,7 +273,8 @@ def orr_direct_forces_fp64_targets(pos, mass, targets, *, eps=0.05, out=None) ->
         raise OrrError(ORR_ERR_INVALID_ARG, "targets must be a 1-d int64 GPU tensor")
     targets = targets.contiguous()
     m = targets.shape[0]
-    acc = out if out is not None else torch.empty((m, 3), dtype=torch.float64, device=pos.device)
+    acc = (torch.empty((m, 3), dtype=torch.float64, device=pos.device) if out is None
+           else _device_tensor(out, "out", torch.float64, (m, 3), pos.device))
     if m == 0:
         return acc
     _check(lib().orr_direct_forces_fp64_targets(_ptr(pos), _ptr(mass), pos.shape[0], float(eps), _ptr(targets), m,
@@ -257,17 +300,17 @@ class Tree:
         pos, mass = _as_inputs(pos, mass)
         self.n = pos.shape[0]
         self.device = pos.device
-        self.workspace = workspace if workspace is not None else new_workspace(self.n, leaf_cap, pos.device)
+        self.workspace, ws_bytes = _workspace(workspace, self.n, leaf_cap, pos.device)
         self._inputs = (pos, mass)
         h = _vp()
         _check(lib().orr_build_tree(_ptr(pos), _ptr(mass), self.n, leaf_cap, _ptr(self.workspace),
-                                    self.workspace.numel(), _stream(pos.device), ctypes.byref(h)))
+                                    ws_bytes, _stream(pos.device), ctypes.byref(h)))
         self._h = h
 
     def walk(self, eps=0.05, theta=0.5, traversal="coherent", out=None, timings=False) -> Result:
         """The walk of the built tree (orr_tree_walk); timings=True times it
         with HIP events and synchronises."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         tm = Timings() if timings else None
         _check(lib().orr_tree_walk(self._h, eps, theta, TRAVERSALS[traversal], _ptr(acc),
                                    *[_ptr(c) for c in cnt], ctypes.byref(tm) if tm is not None else None))
@@ -276,13 +319,13 @@ class Tree:
     def walk_grouped(self, eps=0.05, theta=0.5, group_width=32, out=None) -> Result:
         """The walk with groups of group_width targets sharing a node index
         (orr_tree_walk_grouped)."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         _check(lib().orr_tree_walk_grouped(self._h, eps, theta, group_width, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
     def walk_descend(self, eps=0.05, theta=0.5, group_width=64, out=None) -> Result:
         """The descend-together group walk (orr_tree_walk_descend)."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         _check(lib().orr_tree_walk_descend(self._h, eps, theta, group_width, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
@@ -290,21 +333,21 @@ class Tree:
         """The coherent walk advancing by an explicit wave minimum of the
         lanes' next nodes (orr_tree_walk_min_advance); same outputs as the
         coherent walk."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         _check(lib().orr_tree_walk_min_advance(self._h, eps, theta, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
     def walk_width(self, eps=0.05, theta=0.5, width=64, out=None) -> Result:
         """The coherent walk at coherence width 32, 64, 128 or 256 with the
         production machinery (orr_tree_walk_width)."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         _check(lib().orr_tree_walk_width(self._h, eps, theta, width, _ptr(acc), *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)
 
     def walk_range(self, first, count, eps=0.05, theta=0.5, traversal="coherent", out=None) -> Result:
         """The walk of the sorted targets [first, first + count), whole waves
         (orr_tree_walk_range); writes only those targets' outputs."""
-        acc, cnt = out if out is not None else _outputs(self.n, self.device)
+        acc, cnt = _outputs(self.n, self.device, out)
         _check(lib().orr_tree_walk_range(self._h, eps, theta, TRAVERSALS[traversal], first, count, _ptr(acc),
                                          *[_ptr(c) for c in cnt]))
         return Result(acc, cnt[0], cnt[1], cnt[2], cnt[3], None)

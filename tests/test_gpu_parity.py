@@ -304,6 +304,37 @@ def test_argument_errors_on_device_tensors():
     with pytest.raises(orr.OrrError) as e:
         orr.orr_eval_forces(P, M, workspace=torch.empty(1024, dtype=torch.uint8, device="cuda"))
     assert e.value.status == orr.ORR_ERR_WORKSPACE
+    # Tensors the kernels would write are checked before the call: host
+    # memory, wrong shape or dtype, or a strided view would be bad device
+    # addresses for the C ABI.
+    n = 100
+    ws_host = torch.empty(orr.workspace_bytes(n, 32), dtype=torch.uint8)
+    acc = torch.empty((n, 3), device="cuda")
+    cnt = [torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(4)]
+    bad = [dict(workspace=ws_host),
+           dict(workspace=torch.empty(2 * orr.workspace_bytes(n, 32), dtype=torch.uint8, device="cuda")[::2]),
+           dict(out=(torch.empty((n, 3)), cnt)), dict(out=(torch.empty((n - 1, 3), device="cuda"), cnt)),
+           dict(out=(torch.empty((n, 3), dtype=torch.float64, device="cuda"), cnt)),
+           dict(out=(torch.empty((3, n), device="cuda").t(), cnt)),
+           dict(out=(acc, cnt[:3])), dict(out=(acc, cnt[:3] + [torch.empty(n, dtype=torch.int64, device="cuda")]))]
+    for kw in bad:
+        with pytest.raises(orr.OrrError) as e:
+            orr.orr_eval_forces(P, M, **kw)
+        assert e.value.status == orr.ORR_ERR_INVALID_ARG, kw
+    tree = orr.Tree(P, M, 32)
+    with pytest.raises(orr.OrrError) as e:
+        tree.walk(out=(torch.empty((n, 3)), cnt))
+    assert e.value.status == orr.ORR_ERR_INVALID_ARG
+    with pytest.raises(orr.OrrError) as e:
+        orr.orr_direct_forces(P, M, out=torch.empty((n, 3)))
+    assert e.value.status == orr.ORR_ERR_INVALID_ARG
+    with pytest.raises(orr.OrrError) as e:
+        orr.Tree(P, M, 32, workspace=ws_host)
+    assert e.value.status == orr.ORR_ERR_INVALID_ARG
+    # NULL outputs stay allowed: the library writes only what it is given
+    r = orr.orr_eval_forces(P, M, out=(acc, [None, None, cnt[2], None]))
+    torch.cuda.synchronize()
+    assert r.visits_own is None and torch.isfinite(r.acc).all()
 
 
 def test_native_library_loaded_once():
