@@ -18,7 +18,7 @@ import oracle
 from barnes_hut_gravitational_amd import inputs, orr
 
 from eps_bound import smallest_eps
-from parity import check_acc_bitwise, check_tree, check_walk, to_dev
+from parity import check_acc_bitwise, check_tree, check_walk, to_dev, u32
 
 pytestmark = pytest.mark.gpu
 EPS, THETA = inputs.EPS, inputs.THETA
@@ -117,6 +117,46 @@ def test_64bit_node_offsets(kind, n, cap, theta, monkeypatch):
     monkeypatch.setenv("ORR_WALK_NODE_OFFSETS", "64")
     pos, mass = inputs.make(kind, n)
     run_full_case(pos, mass, cap, EPS, theta)
+
+
+def test_64bit_node_offsets_natural_size():
+    """The coherent walk's large-tree path taken on its own, not forced. It
+    is chosen when the workspace's node bound times 32 bytes passes 4 GiB, and
+    at leaf capacity 1 that bound, n + 21 floor(n / 2) + 1, does so above
+    11.7 million particles. A ragged uniform cube of 12,000,017 particles:
+    the tree bit for bit against the oracle; through the benchmark's entry
+    point (orr_eval_forces, coherent), 3,000 sampled targets' accelerations
+    and counts against the oracle's walk, and their waves' visits_stepped
+    against the oracle's unions; the independent walk equal on every
+    target."""
+    n, cap = 12_000_017, 1
+    assert oracle.max_nodes(n, cap) * 32 > 2**32
+    pos, mass = inputs.make("uniform", n)
+    print(f"[case] natural 64-bit node offsets n={n} cap={cap}", flush=True)
+    ot = oracle.build_tree(pos, mass, cap)
+    print(f"[case] oracle tree: {ot.n_nodes} nodes", flush=True)
+    P, M = to_dev(pos, mass)
+    ws = orr.new_workspace(n, cap, P.device)
+    r = orr.orr_eval_forces(P, M, eps=EPS, theta=THETA, leaf_cap=cap, traversal="coherent", workspace=ws,
+                            timings=True)
+    tg = np.sort(np.random.default_rng(12).choice(n, 3000, replace=False))  # sorted positions
+    acc, pp, pc, vis = oracle.walk(ot, EPS, THETA, tg)
+    rows = ot.perm[tg].astype(np.int64)  # their caller-order indices
+    assert np.array_equal(r.acc.cpu().numpy()[rows].view(np.uint32), acc.view(np.uint32))
+    assert np.array_equal(u32(r.n_pp)[rows], pp)
+    assert np.array_equal(u32(r.n_pc)[rows], pc)
+    assert np.array_equal(u32(r.visits_own)[rows], vis)
+    waves, inv = np.unique(tg // 64, return_inverse=True)
+    union = oracle.union_visits(ot, EPS, THETA, 64, waves)
+    assert np.array_equal(u32(r.visits_stepped)[rows], union[inv])
+    tree = orr.Tree(P, M, cap, workspace=ws)
+    check_tree(tree, ot)
+    ri = tree.walk(EPS, THETA, "independent")
+    torch.cuda.synchronize()
+    assert torch.equal(r.acc.view(torch.int32), ri.acc.view(torch.int32))
+    for f in ("visits_own", "n_pp", "n_pc"):
+        assert torch.equal(getattr(r, f), getattr(ri, f))
+    print(f"[case] natural 64-bit node offsets ok, timings {r.timings}", flush=True)
 
 
 @pytest.mark.parametrize("n", [16384, 16385, 32768, 32769, 262144, 262145])
