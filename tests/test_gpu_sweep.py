@@ -13,6 +13,8 @@ and their counts exactly, and the benchmark's entry point (orr_eval_forces,
 coherent) equal to the tree walk.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,7 +30,8 @@ KINDS = ("plummer", "uniform", "merger", "clusters", "lattice")
 CAPS = (1, 2, 3, 8, 16, 32, 64, 100, 256)
 THETAS = (0.0, 0.2, 0.5, 0.7, 1.0, 1.5)
 EPSES = (1e-3, 0.01, 0.05, 0.2)
-N_CASES = 80
+# ORR_SWEEP_CASES draws more cases (the case i is the same for every count).
+N_CASES = int(os.environ.get("ORR_SWEEP_CASES", "80"))
 N_MAX = 600000
 
 
