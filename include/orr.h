@@ -69,6 +69,13 @@
  *     particles at leaf capacity 32, and by 64-bit indices above. Setting the
  *     environment variable ORR_WALK_NODE_OFFSETS to "64" makes every launch of
  *     it take the 64-bit path; results are the same bit for bit.
+ *   - Checked build: liborr_checked.so exports this same ABI from the same
+ *     sources compiled with ORR_CHECKED=1. Its kernels test every index they
+ *     take from device data (node escapes, leaf ranges, the permutation, the
+ *     sort's gather and run positions, the build's node slots and lists)
+ *     against the array it addresses, skip an access that fails, and record
+ *     the failure; the next call that synchronises (as for non-finite input,
+ *     below) then returns ORR_ERR_HIP. It is about a quarter slower.
  *   - Inputs whose positions or masses are non-finite, whose masses are
  *     negative, or whose extent overflows float32 are detected on the device
  *     while the tree is built; the evaluation still runs to completion on a
@@ -309,7 +316,8 @@ orr_status orr_eval_forces_noalloc(const float *pos, const float *mass, int64_t 
  * evaluation used) and reads the workspace's parameter block. ORR_OK;
  * ORR_ERR_NONFINITE if that input was non-finite or had a negative mass;
  * ORR_ERR_HIP if a bounded wait of its radix sort gave up (never expected;
- * its outputs are then invalid). Every build resets the status, so a caller
+ * its outputs are then invalid), or, in the checked build, if a device
+ * index check failed. Every build resets the status, so a caller
  * that evaluates several times checks after each evaluation it relies on.
  * Errors: ORR_ERR_INVALID_ARG (null or unaligned workspace),
  * ORR_ERR_WORKSPACE (smaller than its parameter block), ORR_ERR_HIP. */
