@@ -42,6 +42,10 @@ struct Check {
     uint32_t n_particles;
 };
 
+// Kernels that only read the parameter block take it as const (their loads
+// of it may go through the scalar cache); the checked build still reports
+// through it. That is sound because none of them reads the status word, and
+// the atomic goes to memory, past the caches the const loads may use.
 __device__ __forceinline__ Check make_check(const DevParams *prm) {
     if constexpr (kChecked)
         return Check{const_cast<uint32_t *>(&prm->bad_input), prm->n_particles};
