@@ -102,6 +102,13 @@ def test_degenerate_inputs():
     # collinear, and a flat (zero-extent) axis
     t = np.linspace(-1, 1, 1500, dtype=np.float32)
     run_full_case(np.stack([t, 2 * t, np.zeros_like(t)], 1), np.full(1500, 1 / 1500, np.float32), 32, EPS, 0.5)
+    # every mass zero (each node's centre is its first particle), and all the
+    # mass on one particle
+    pos, mass = inputs.make("plummer", 3000)
+    run_full_case(pos, np.zeros(3000, np.float32), 32, EPS, 0.5)
+    one = np.zeros(3000, np.float32)
+    one[1234] = 1.0
+    run_full_case(pos, one, 16, EPS, 0.5)
     # tiny and huge coordinate scales
     pos, mass = inputs.make("plummer", 2000)
     run_full_case(pos * np.float32(1e-30), mass, 32, EPS, 0.5)
