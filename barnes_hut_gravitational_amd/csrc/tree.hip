@@ -183,28 +183,59 @@ __global__ __launch_bounds__(1024) void k_tile_scan(uint32_t *__restrict__ tile_
 }
 
 // First j > start whose key differs from pre in its top bits (key >> sh), or
-// n; key[start] >> sh == pre.
+// n; key[start] >> sh == pre. The probes of each round are loaded together,
+// eight at a time (offsets 1, 2, 4, ... from start to bracket the end, then
+// seven evenly spaced points of the bracket), so the chain of dependent loads
+// is a few rounds long instead of two per halving.
 __device__ uint32_t cell_end(const uint64_t *__restrict__ keys, uint32_t n, uint32_t start, int sh, uint64_t pre) {
-    uint64_t lo = start, hi, step = 1;
-    for (;;) {
-        const uint64_t probe = lo + step;
-        if (probe >= n) {
-            hi = n;
-            break;
+    uint64_t lo = start, hi = n;  // key[lo] in the cell; hi = n or a key outside it
+    for (uint32_t q0 = 0; q0 < 64; q0 += 8) {
+        uint64_t k[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; u++) {
+            const uint64_t p = (uint64_t)start + (1ull << (q0 + u));
+            k[u] = p < n ? keys[p] : 0ull;
         }
-        if ((keys[probe] >> sh) != pre) {
-            hi = probe;
-            break;
+        bool bracketed = false;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; u++) {
+            const uint64_t p = (uint64_t)start + (1ull << (q0 + u));
+            if (bracketed) continue;
+            if (p >= n) {
+                hi = n;
+                bracketed = true;
+            } else if ((k[u] >> sh) != pre) {
+                hi = p;
+                bracketed = true;
+            } else {
+                lo = p;
+            }
         }
-        lo = probe;
-        step <<= 1;
+        if (bracketed) break;
     }
     while (hi - lo > 1) {
-        const uint64_t mid = lo + (hi - lo) / 2;
-        if ((keys[mid] >> sh) == pre)
-            lo = mid;
-        else
-            hi = mid;
+        const uint64_t step = (hi - lo + 7) / 8;  // probes lo + step, lo + 2 step, ... below hi
+        uint64_t k[7];
+#pragma unroll
+        for (uint32_t t = 0; t < 7; t++) {
+            const uint64_t p = lo + step * (t + 1);
+            k[t] = p < hi ? keys[p] : 0ull;
+        }
+        uint64_t nlo = lo, nhi = hi;
+        bool done = false;
+#pragma unroll
+        for (uint32_t t = 0; t < 7; t++) {
+            const uint64_t p = lo + step * (t + 1);
+            if (done || p >= hi) continue;
+            if ((k[t] >> sh) != pre) {
+                nhi = p;
+                done = true;
+            } else {
+                nlo = p;
+            }
+        }
+        lo = nlo;
+        hi = nhi;
     }
     return (uint32_t)hi;
 }
