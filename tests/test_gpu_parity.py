@@ -342,6 +342,32 @@ def test_workspace_reuse_and_side_stream():
             check_walk(r, ref, "coherent")
 
 
+def test_concurrent_streams_separate_workspaces():
+    """Evaluations enqueued on four streams at once, each with its own
+    workspace and input (sizes that take different team sizes and sort tile
+    sizes), several times over without waiting in between: every result is
+    bit for bit the oracle's. The library keeps no device state outside the
+    caller's workspace."""
+    cases = [inputs.make("plummer", 20000), inputs.make("uniform", 70000), inputs.make("merger", 300007),
+             clustered(3, 9000, 1e-5, 21)]
+    refs = [oracle.evaluate(p, m, EPS, THETA, 32) for p, m in cases]
+    dev = [to_dev(p, m) for p, m in cases]
+    streams = [torch.cuda.Stream() for _ in cases]
+    wss = [orr.new_workspace(len(m), 32, "cuda") for _, m in cases]
+    outs = [[None] * 3 for _ in cases]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k, (P, M) in enumerate(dev):
+            with torch.cuda.stream(streams[k]):
+                outs[k][rep] = orr.orr_eval_forces(P, M, workspace=wss[k] if rep != 1 else None)
+    torch.cuda.synchronize()
+    for k, ref in enumerate(refs):
+        for rep in range(3):
+            check_walk(outs[k][rep], ref, "coherent")
+            check_acc_bitwise(outs[k][rep], ref.acc)
+        orr.orr_workspace_check(wss[k])
+
+
 def test_argument_errors_on_device_tensors():
     P, M = to_dev(*inputs.make("plummer", 100))
     for kw in ({"eps": 0.0}, {"eps": float("nan")}, {"theta": -1.0}, {"leaf_cap": 0}, {"leaf_cap": 257}):
