@@ -368,6 +368,24 @@ def test_concurrent_streams_separate_workspaces():
         orr.orr_workspace_check(wss[k])
 
 
+def test_one_tree_many_walks():
+    """A tree built once and walked with different softenings and opening
+    angles (including a power-of-two theta^2, which takes the scaled
+    comparison, and theta = 0), each walk bit for bit the oracle's for the
+    same parameters; the tree itself is unchanged by the walks."""
+    pos, mass = inputs.make("merger", 30000)
+    ot = oracle.build_tree(pos, mass, 16)
+    P, M = to_dev(pos, mass)
+    tree = orr.Tree(P, M, 16)
+    for eps, theta in ((0.05, 0.5), (0.01, 0.7), (0.2, 0.25), (1e-3, 1.2), (0.05, 0.0)):
+        ref, r = oracle.evaluate(pos, mass, eps, theta, 16), tree.walk(eps, theta, "coherent")
+        torch.cuda.synchronize()
+        print(f"[case] one tree eps={eps} theta={theta}", flush=True)
+        check_walk(r, ref, "coherent")
+        check_acc_bitwise(r, ref.acc)
+    check_tree(tree, ot)
+
+
 def test_argument_errors_on_device_tensors():
     P, M = to_dev(*inputs.make("plummer", 100))
     for kw in ({"eps": 0.0}, {"eps": float("nan")}, {"theta": -1.0}, {"leaf_cap": 0}, {"leaf_cap": 257}):
