@@ -109,6 +109,10 @@ def test_degenerate_inputs():
     one = np.zeros(3000, np.float32)
     one[1234] = 1.0
     run_full_case(pos, one, 16, EPS, 0.5)
+    # far from the origin: a large corner, few position bits inside the cube
+    pos, mass = inputs.make("plummer", 3000)
+    run_full_case((pos + np.float32(1e4)).astype(np.float32), mass, 32, EPS, 0.5)
+    run_full_case((pos * np.float32(1e-3) - np.float32(7e3)).astype(np.float32), mass, 8, EPS, 0.5)
     # tiny and huge coordinate scales
     pos, mass = inputs.make("plummer", 2000)
     run_full_case(pos * np.float32(1e-30), mass, 32, EPS, 0.5)
